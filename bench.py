@@ -1,0 +1,338 @@
+"""Benchmark: the synthetic decode sweep of the W4 g64 hot path on one MI355X.
+
+One step = 16 layer-equivalents of (o_proj 5120x5120, fused gate-up
+5120 -> 34816, down_proj 17408 -> 5120) W4 g64 products back to back on one
+stream, then the 248,320-row lm_head product and the greedy argmax over the
+full vocabulary.  Every product takes its own pre-generated bf16 input (no
+norm or activation between them; the inputs are seeded synthetic data of the
+model's shapes, the weights seeded synthetic codes, scales and biases).  The
+step is captured once in a HIP graph and replayed.
+
+Printed: one JSON line.  `value` is the algorithmic bytes of a step
+(0.5625*N*K + 2*B*K + 4*B*N per product, 4*B*V for the argmax) over the
+measured step time, in GB/s.  The line also carries the roofline of the
+dominant kernel (the gate-up product), the oracle timed on the host cores, and
+secondary figures: lm_head+argmax microseconds per token, the 512-row prompt
+products in TFLOP/s, and the batch-8 sweep.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--batch 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, vendor figure
+METRIC = "W4 g64 GEMV GB/s (% HBM peak); lm_head+argmax µs/token; prompt GEMM TFLOPS"
+
+HIDDEN, INTER, VOCAB, LAYERS = 5120, 17408, 248320, 16
+
+
+def gemv_bytes(N, K, B):
+    return int(0.5625 * N * K) + 2 * B * K + 4 * B * N
+
+
+def step_bytes(B):
+    per_layer = (gemv_bytes(HIDDEN, HIDDEN, B) + gemv_bytes(2 * INTER, HIDDEN, B)
+                 + gemv_bytes(HIDDEN, INTER, B))
+    return LAYERS * per_layer + gemv_bytes(VOCAB, HIDDEN, B) + 4 * B * VOCAB
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--batch", type=int, default=1)
+    p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    p.add_argument("--skip-extras", action="store_true",
+                   help="only the headline sweep (used for profiler runs)")
+    p.add_argument("--skip-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return p.parse_args()
+
+
+class Mat:
+    """One quantized matrix resident on the GPU."""
+
+    def __init__(self, N, K, workload, matrix, layer, dev):
+        from w4_gemv_greedy_amd import synth
+        import torch
+        wq, sc, bi = synth.weights(N, K, workload=workload, matrix=matrix, layer=layer)
+        self.N, self.K = N, K
+        self.wq = torch.from_numpy(wq.view(np.int32)).to(dev)
+        self.sc = torch.from_numpy(sc.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.bi = torch.from_numpy(bi.view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def make_x(M, K, workload, matrix, layer, dev):
+    from w4_gemv_greedy_amd import synth
+    import torch
+    x = synth.activations(M, K, workload=workload, matrix=matrix, layer=layer)
+    return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (plain C, OpenMP over output rows) on the host cores, bounded sample."""
+    import oracle
+    from w4_gemv_greedy_amd import synth
+    oracle.load()
+    threads = oracle.threads()
+    shapes = [("o_proj", HIDDEN, HIDDEN, synth.O_PROJ), ("gate_up", 2 * INTER, HIDDEN, synth.GATE_UP),
+              ("down", HIDDEN, INTER, synth.DOWN)]
+    done_bytes, spent, pieces = 0, 0.0, []
+    for name, N, K, mid in shapes:
+        if spent > budget_s:
+            break
+        rows = N if name == "o_proj" else N // 4
+        wq, sc, bi = synth.weights(N, K, workload=5, matrix=mid, layer=0)
+        x = synth.activations(1, K, workload=5, matrix=mid, layer=0)
+        sel = np.arange(0, N, N // rows, dtype=np.int64)[:rows]
+        t0 = time.perf_counter()
+        oracle.qmm_rows(wq, sc, bi, x, sel)
+        dt = time.perf_counter() - t0
+        spent += dt
+        done_bytes += int(0.5625 * rows * K) + 2 * K + 4 * rows
+        pieces.append(f"{name} {rows} of {N} rows")
+    logits = synth.logits(1, VOCAB)
+    t0 = time.perf_counter()
+    oracle.argmax(logits)
+    dt = time.perf_counter() - t0
+    spent += dt
+    done_bytes += 4 * VOCAB
+    pieces.append("argmax over 248320 logits")
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "batch-1 decode products of layer 0 (" + ", ".join(pieces) + f"), {spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import w4_gemv_greedy_amd as w4g
+    from w4_gemv_greedy_amd import synth
+    from w4_gemv_greedy_amd import _lib
+
+    _lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B = args.batch
+    if not 1 <= B <= 8:
+        sys.exit("--batch must be 1..8")
+
+    t0 = time.perf_counter()
+    layers = []
+    for l in range(LAYERS):
+        layers.append((Mat(HIDDEN, HIDDEN, 5, synth.O_PROJ, l, dev),
+                       Mat(2 * INTER, HIDDEN, 5, synth.GATE_UP, l, dev),
+                       Mat(HIDDEN, INTER, 5, synth.DOWN, l, dev)))
+    head = Mat(VOCAB, HIDDEN, 5, synth.LM_HEAD, 0, dev)
+    log(f"weights resident ({step_bytes(1) / 1e9:.2f} GB algorithmic per step), "
+        f"{time.perf_counter() - t0:.1f} s")
+
+    def inputs(Bn):
+        xs = []
+        for l in range(LAYERS):
+            xs.append((make_x(Bn, HIDDEN, 5, synth.O_PROJ, l, dev), make_x(Bn, HIDDEN, 5, synth.GATE_UP, l, dev),
+                       make_x(Bn, INTER, 5, synth.DOWN, l, dev)))
+        return xs, make_x(Bn, HIDDEN, 5, synth.LM_HEAD, 0, dev)
+
+    def outputs(Bn):
+        return (torch.empty((Bn, HIDDEN), dtype=torch.float32, device=dev),
+                torch.empty((Bn, 2 * INTER), dtype=torch.float32, device=dev),
+                torch.empty((Bn, HIDDEN), dtype=torch.float32, device=dev),
+                torch.empty((Bn, VOCAB), dtype=torch.float32, device=dev),
+                torch.empty(Bn, dtype=torch.int32, device=dev),
+                torch.empty(w4g.workspace_bytes(w4g.OP_ARGMAX, Bn, VOCAB, 0), dtype=torch.uint8, device=dev))
+
+    def make_step(Bn, events=None):
+        xs, xh = inputs(Bn)
+        yo, yg, yd, logits, ids, ws = outputs(Bn)
+
+        def step():
+            for l in range(LAYERS):
+                o, g, d = layers[l]
+                xo, xg, xd = xs[l]
+                w4g.qmm_gemv(o.wq, o.sc, o.bi, xo, yo)
+                if events is not None:
+                    events[l][0].record()
+                w4g.qmm_gemv(g.wq, g.sc, g.bi, xg, yg)
+                if events is not None:
+                    events[l][1].record()
+                w4g.qmm_gemv(d.wq, d.sc, d.bi, xd, yd)
+            w4g.qmm_gemv(head.wq, head.sc, head.bi, xh, logits)
+            w4g.vocab_argmax(logits, ids, ws)
+        return step, ids, logits
+
+    def timed(fn, steps, warmup, graph):
+        if graph:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for _ in range(2):
+                    fn()
+            torch.cuda.current_stream().wait_stream(s)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            run = g.replay
+        else:
+            run = fn
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        return e0.elapsed_time(e1) / steps, wall
+
+    graph = not args.no_graph
+    step, ids, logits = make_step(B)
+    ms, wall = timed(step, args.steps, args.warmup, graph)
+    nbytes = step_bytes(B)
+    value = nbytes / (ms * 1e-3) / 1e9
+    log(f"sweep B={B}: {ms * 1e3:.1f} us/step, {value:.0f} GB/s ({graph=}), wall {wall:.2f} s")
+
+    # dominant kernel: the gate-up product, timed launch by launch with events on its stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(LAYERS)]
+    istep, _, _ = make_step(B, events=ev)
+    durs = []
+    for _ in range(max(3, args.steps // 4)):
+        istep()
+        torch.cuda.synchronize()
+        durs += [a.elapsed_time(b) for a, b in ev]
+    gu_us = float(np.mean(durs)) * 1e3
+    gu_bytes = gemv_bytes(2 * INTER, HIDDEN, B)
+    gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemv_valu_kernel (gate_up 5120 -> 34816)", "avg_launch_us": round(gu_us, 2),
+                "bytes_per_launch": gu_bytes}
+    log(f"gate_up launch avg {gu_us:.2f} us -> {gu_gbs:.0f} GB/s")
+
+    extras = {}
+    if not args.skip_extras:
+        extras = secondary(torch, w4g, synth, layers, head, dev, timed, args)
+
+    cpu = None
+    if not args.skip_cpu:
+        cpu = cpu_baseline()
+        log(f"cpu baseline {cpu}")
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": "decode sweep: 16 x (o_proj 5120x5120, gate_up 5120->34816, "
+                                  "down 17408->5120) + lm_head 5120->248320 + greedy argmax",
+                      "batch": B, "bytes_per_step": nbytes, "hip_graph": graph,
+                      "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+           "roofline": roofline, "cpu_baseline": cpu, "secondary": extras}
+    print(json.dumps(out), flush=True)
+
+
+def secondary(torch, w4g, synth, layers, head, dev, timed, args):
+    ex = {}
+    # lm_head + argmax per token (batch 1)
+    xh = make_x(1, HIDDEN, 5, synth.LM_HEAD, 1, dev)
+    logits = torch.empty((1, VOCAB), dtype=torch.float32, device=dev)
+    ids = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(w4g.workspace_bytes(w4g.OP_ARGMAX, 1, VOCAB, 0), dtype=torch.uint8, device=dev)
+
+    def head_step():
+        w4g.qmm_gemv(head.wq, head.sc, head.bi, xh, logits)
+        w4g.vocab_argmax(logits, ids, ws)
+    ms, _ = timed(head_step, 20, 3, True)
+    ex["lm_head_argmax_us_per_token"] = round(ms * 1e3, 2)
+    ex["lm_head_argmax_GBps"] = round((gemv_bytes(VOCAB, HIDDEN, 1) + 4 * VOCAB) / (ms * 1e-3) / 1e9, 1)
+
+    def argmax_only():
+        w4g.vocab_argmax(logits, ids, ws)
+    ms, _ = timed(argmax_only, 50, 5, True)
+    ex["argmax_us"] = round(ms * 1e3, 2)
+    log(f"lm_head+argmax {ex['lm_head_argmax_us_per_token']} us/token, argmax alone {ex['argmax_us']} us")
+
+    # per-product averages at batch 1, 4, 8, each cycling through the 16 layers' weights
+    for Bn in (1, 4, 8):
+        for name, idx, N, K, mid in (("o_proj", 0, HIDDEN, HIDDEN, synth.O_PROJ),
+                                     ("gate_up", 1, 2 * INTER, HIDDEN, synth.GATE_UP),
+                                     ("down", 2, HIDDEN, INTER, synth.DOWN)):
+            x = make_x(Bn, K, 5, mid, 99, dev)
+            y = torch.empty((Bn, N), dtype=torch.float32, device=dev)
+
+            def run(idx=idx, x=x, y=y):
+                for l in range(LAYERS):
+                    m = layers[l][idx]
+                    w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y)
+            ms, _ = timed(run, 5, 2, True)
+            us = ms * 1e3 / LAYERS
+            gbs = gemv_bytes(N, K, Bn) / (us * 1e-6) / 1e9
+            ex[f"gemv_{name}_b{Bn}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
+                                       "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+    log("per-product: " + ", ".join(f"{k} {v['us']}us {v['GBps']}GB/s" for k, v in ex.items()
+                                    if k.startswith("gemv_")))
+
+    # prompt products, M = 512
+    pr = {}
+    for name, idx, N, K, mid in (("o_proj", 0, HIDDEN, HIDDEN, synth.O_PROJ),
+                                 ("gate_up", 1, 2 * INTER, HIDDEN, synth.GATE_UP),
+                                 ("down", 2, HIDDEN, INTER, synth.DOWN)):
+        M = 512
+        x = make_x(M, K, 4, mid, 0, dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, w4g.workspace_bytes(w4g.OP_GEMM, M, N, K)), dtype=torch.uint8, device=dev)
+        m = layers[0][idx]
+
+        def run(m=m, x=x, y=y, ws=ws):
+            w4g.qmm_gemm(m.wq, m.sc, m.bi, x, y, ws)
+        ms, _ = timed(run, 10, 2, True)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        pr[name] = {"us": round(ms * 1e3, 1), "TFLOPS": round(tf, 1),
+                    "pct_mfma_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1)}
+    ex["prompt_gemm_m512"] = pr
+    log("prompt: " + ", ".join(f"{k} {v['us']}us {v['TFLOPS']}TF" for k, v in pr.items()))
+
+    # the batch-8 sweep
+    if args.batch != 8:
+        xs8 = [(make_x(8, HIDDEN, 6, synth.O_PROJ, l, dev), make_x(8, HIDDEN, 6, synth.GATE_UP, l, dev),
+                make_x(8, INTER, 6, synth.DOWN, l, dev)) for l in range(LAYERS)]
+        xh8 = make_x(8, HIDDEN, 6, synth.LM_HEAD, 0, dev)
+        yo = torch.empty((8, HIDDEN), dtype=torch.float32, device=dev)
+        yg = torch.empty((8, 2 * INTER), dtype=torch.float32, device=dev)
+        lg = torch.empty((8, VOCAB), dtype=torch.float32, device=dev)
+        ids8 = torch.empty(8, dtype=torch.int32, device=dev)
+        ws8 = torch.empty(w4g.workspace_bytes(w4g.OP_ARGMAX, 8, VOCAB, 0), dtype=torch.uint8, device=dev)
+
+        def step8():
+            for l in range(LAYERS):
+                o, g, d = layers[l]
+                w4g.qmm_gemv(o.wq, o.sc, o.bi, xs8[l][0], yo)
+                w4g.qmm_gemv(g.wq, g.sc, g.bi, xs8[l][1], yg)
+                w4g.qmm_gemv(d.wq, d.sc, d.bi, xs8[l][2], yo)
+            w4g.qmm_gemv(head.wq, head.sc, head.bi, xh8, lg)
+            w4g.vocab_argmax(lg, ids8, ws8)
+        ms, _ = timed(step8, 10, 2, True)
+        ex["sweep_b8"] = {"us_per_step": round(ms * 1e3, 1), "us_per_token": round(ms * 1e3 / 8, 2),
+                          "GBps": round(step_bytes(8) / (ms * 1e-3) / 1e9, 1)}
+        log(f"sweep B=8: {ex['sweep_b8']}")
+    return ex
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * w4g.h -- C ABI of the MI355X (gfx950) library for 4-bit affine group-64
+ * quantized matrix products and the greedy vocabulary argmax.
+ *
+ * Operations (what each computes, and where the sources define it):
+ *
+ *   qmm_gemv / qmm_gemm:  y[m][n] = sum_k x[m][k] * w[n][k], fp32 result,
+ *     with w[n][k] = q[n][k] * s[n][k/64] + b[n][k/64].
+ *     - 4-bit affine quantization with group size 64: TensorFold PR #1437
+ *       ("qwen27: document two-Mac 27B serving and the seam's known tie"),
+ *       Receipt.
+ *     - fp32 accumulation and an fp32 store: the same PR, commit "Add the
+ *       pair seam and register its kernels with the kernel contract".
+ *     - The K reduction order is a function of the matrix width K alone,
+ *       never of N, the batch, the grid or timing: TensorFold PR #1433,
+ *       step-2 description (a rank's K tree is its own full matrix's; the
+ *       split is keyed on the whole matrix, not on a slice).
+ *     qmm_gemv is the decode path (1 <= B <= 8 activation rows); qmm_gemm is
+ *     the prompt path (any M >= 1, matrix cores).
+ *
+ *   vocab_argmax:  ids[r] = the greedy token of logit row r.  A row holding any
+ *     NaN, +Inf or -Inf yields W4G_SENTINEL (0xFFFFFFFF); otherwise the largest
+ *     value wins and exact ties go to the lowest id (-0.0 ties +0.0).
+ *     TensorFold PR #1433, step-1 description (pair_argmax flags a non-finite
+ *     row with bit 31 of its id word, pair_pick turns the flag into the
+ *     maxInt(u32) sentinel, and a pick that ties to the higher id is a planted
+ *     failure) and step-2 description (the session reads the sentinel as a
+ *     failure, never as a logit).
+ *
+ * Data layout (all row-major, all device memory):
+ *   wq      [N][K/8]  uint32: element k = 8i+j of row n is bits [4j, 4j+4) of
+ *                     word wq[n][i] (low nibble first), an unsigned code 0..15.
+ *   scales  [N][K/64] bf16 (passed as uint16 bit patterns).
+ *   biases  [N][K/64] bf16.
+ *   x       [B][K] or [M][K] bf16.
+ *   y       [B][N] or [M][N] fp32.
+ *   logits  [rows][ld] fp32 or bf16; row r occupies elements [r*ld, r*ld+vocab).
+ *   ids     [rows] uint32.
+ *
+ * Ownership and behaviour common to every entry point:
+ *   - Every pointer is a device pointer owned by the caller.  No call
+ *     allocates, frees or synchronizes; the library keeps no state between
+ *     calls.  Work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream) and completes asynchronously.
+ *   - All arguments are validated on the host before any HIP call; a call that
+ *     fails validation enqueues nothing and returns a nonzero W4G_E* status.
+ *   - Outputs must not overlap inputs or the workspace.
+ *   - Non-finite logits are data, not an error: the row's id is the sentinel.
+ *   - Device faults surface at the caller's next synchronization.
+ *   - Calls that share one workspace buffer must be ordered on one stream.
+ */
+#ifndef W4G_H
+#define W4G_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4G_ABI_VERSION 1
+#define W4G_SENTINEL 0xFFFFFFFFu
+#define W4G_MAX_GEMV_BATCH 8
+
+/* status codes */
+#define W4G_OK 0
+#define W4G_EINVAL_PTR 1  /* a required pointer is NULL */
+#define W4G_ESHAPE 2      /* a size is out of range (K % 64, B, N, M, vocab, ld) */
+#define W4G_EALIGN 3      /* wq, x, y or logits not 16-byte aligned */
+#define W4G_EWORKSPACE 4  /* workspace missing or smaller than qmm_workspace_bytes */
+#define W4G_EDTYPE 5      /* unknown logits dtype or op code */
+#define W4G_ELAUNCH 6     /* the HIP runtime refused a launch */
+#define W4G_EALIAS 7      /* an output overlaps an input or the workspace */
+
+/* logits dtypes */
+#define W4G_F32 0
+#define W4G_BF16 1
+
+/* op codes for qmm_workspace_bytes */
+#define W4G_OP_GEMV 0
+#define W4G_OP_GEMM 1
+#define W4G_OP_ARGMAX 2
+
+/*
+ * Decode product, 1 <= B <= 8 activation rows.
+ *   wq, scales, biases: the quantized matrix (N rows, K columns), see layout.
+ *   x [B][K] bf16, y [B][N] fp32.  N >= 1; K >= 64 and K % 64 == 0.
+ *   wq, x and y must be 16-byte aligned.
+ *   workspace: at least qmm_workspace_bytes(W4G_OP_GEMV, B, N, K) bytes
+ *   (may be NULL when that is 0).
+ * Reduction order (a function of K only): K is cut into chunks of 1024
+ * elements (the last may be shorter); within a chunk, lane j of a 32-lane
+ * group owns elements [32j, 32j+32), half of one 64-group, and forms
+ * s*D + (b - 128*s)*X, where D is the dot of x with (128 + q) taken over
+ * bf16 pairs in ascending pair order and X the fp32 sum of those 32 x; each
+ * lane adds its chunk terms in ascending chunk order, and the 32 lane sums
+ * meet in a fixed xor butterfly (16, 8, 4, 2, 1).  Row m of a B-row call is
+ * bitwise equal to the same row computed alone.
+ */
+int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+             const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Prompt product on the matrix cores, any M >= 1 rows.
+ *   Same layout and constraints as qmm_gemv with M in place of B.
+ *   workspace: at least qmm_workspace_bytes(W4G_OP_GEMM, M, N, K) bytes.
+ * Each code enters the bf16 matrix cores as the exact value 2 + q/8; a
+ * 64-group's partial P_g is scaled by 8s in fp32 and added to the running sum
+ * in ascending group order; the remaining affine term sum_g (b - 16 s) X_g
+ * (X_g the fp32 group sum of x, split exactly into three bf16 parts) is
+ * accumulated on the matrix cores after the last group.  Row m of the result
+ * does not depend on M or on the other rows.
+ */
+int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+             const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy argmax of `rows` logit rows of `vocab` entries (row pitch `ld`).
+ *   dtype: W4G_F32 or W4G_BF16 (bf16 is widened to fp32 exactly).
+ *   1 <= vocab < 2^31 (bit 31 of an id word is the non-finite flag),
+ *   ld >= vocab, rows >= 1.  logits must be 16-byte aligned.
+ *   ids [rows] uint32: the winning id, or W4G_SENTINEL for a row holding NaN
+ *   or +-Inf.
+ *   workspace: at least qmm_workspace_bytes(W4G_OP_ARGMAX, rows, vocab, 0).
+ * Two passes: pass 1 reduces blocks of 1024 ids to (value, id | flag) records,
+ * pass 2 combines a row's records; both keep the lowest id among equal
+ * values and propagate the flag.
+ */
+int vocab_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                 uint32_t* ids, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace an operation needs for the given sizes; 0 when none.
+ *   op W4G_OP_GEMV: rows = B, n = N, k = K.
+ *   op W4G_OP_GEMM: rows = M, n = N, k = K.
+ *   op W4G_OP_ARGMAX: rows = rows, n = vocab, k ignored.
+ * Returns (size_t)-1 for an unknown op or sizes out of range.
+ */
+size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* w4g_status_string(int status);
+
+/* W4G_ABI_VERSION of the loaded library. */
+int w4g_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4G_H */

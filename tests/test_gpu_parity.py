@@ -1,0 +1,127 @@
+"""GPU parity of the HIP library against the CPU oracle at sizes the oracle
+finishes quickly, spanning several tiles and ragged tails.  Calls go through
+the C ABI (ctypes) with device pointers and the current stream."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (assert_close, down, ids_down, up_bf16, up_f32, up_u32)
+from w4_gemv_greedy_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+w4g = pytest.importorskip("w4_gemv_greedy_amd")
+
+
+def _case(N, K, rows, seed):
+    wq, sc, bi = synth.weights(N, K, workload=50 + seed)
+    x = synth.activations(rows, K, workload=50 + seed)
+    return wq, sc, bi, x
+
+
+GEMV_SHAPES = [(37, 64), (64, 1088), (129, 2048), (200, 5120), (40, 17408), (9, 3072)]
+
+
+@pytest.mark.parametrize("N,K", GEMV_SHAPES)
+@pytest.mark.parametrize("B", [1, 2, 4, 8])
+def test_gemv_matches_oracle(N, K, B):
+    wq, sc, bi, x = _case(N, K, B, N + K)
+    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x)))
+    ref = oracle.qmm(wq, sc, bi, x)
+    e = assert_close(y, ref, f"gemv B={B} N={N} K={K}")
+    print(f"gemv B={B} N={N} K={K} normwise {e:.2e}")
+
+
+@pytest.mark.parametrize("B", [3, 5, 6, 7])
+def test_gemv_odd_batches(B):
+    wq, sc, bi, x = _case(70, 1024, B, 7)
+    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x)))
+    assert_close(y, oracle.qmm(wq, sc, bi, x), f"gemv B={B}")
+
+
+def test_gemv_batch_invariance_and_determinism():
+    wq, sc, bi, x = _case(300, 5120, 8, 3)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y8 = down(w4g.qmm_gemv(*W, up_bf16(x)))
+    y8b = down(w4g.qmm_gemv(*W, up_bf16(x)))
+    assert np.array_equal(y8.view(np.uint32), y8b.view(np.uint32)), "not run-to-run deterministic"
+    for m in (0, 3, 7):
+        y1 = down(w4g.qmm_gemv(*W, up_bf16(x[m:m + 1])))
+        assert np.array_equal(y1[0].view(np.uint32), y8[m].view(np.uint32)), f"row {m} differs at B=1"
+
+
+def test_gemv_row_permutation_bitwise():
+    wq, sc, bi, x = _case(96, 2048, 1, 4)
+    p = np.random.default_rng(0).permutation(96)
+    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x)))
+    yp = down(w4g.qmm_gemv(up_u32(wq[p]), up_bf16(sc[p]), up_bf16(bi[p]), up_bf16(x)))
+    assert np.array_equal(yp.view(np.uint32), y[:, p].view(np.uint32))
+
+
+GEMM_SHAPES = [(1, 37, 64), (7, 130, 1088), (130, 256, 1024), (64, 128, 5120), (33, 70, 17408)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_matches_oracle(M, N, K):
+    wq, sc, bi, x = _case(N, K, M, M + N + K)
+    y = down(w4g.qmm_gemm(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x)))
+    ref = oracle.qmm(wq, sc, bi, x)
+    e = assert_close(y, ref, f"gemm M={M} N={N} K={K}")
+    print(f"gemm M={M} N={N} K={K} normwise {e:.2e}")
+
+
+def test_gemm_deterministic_and_row_independent():
+    wq, sc, bi, x = _case(256, 2048, 160, 9)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y = down(w4g.qmm_gemm(*W, up_bf16(x)))
+    y2 = down(w4g.qmm_gemm(*W, up_bf16(x)))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    ys = down(w4g.qmm_gemm(*W, up_bf16(x[:5])))
+    assert np.array_equal(ys.view(np.uint32), y[:5].view(np.uint32)), "prompt rows depend on M"
+
+
+def _argmax_gpu(logits_np, bf16=False):
+    t = up_bf16(logits_np) if bf16 else up_f32(logits_np)
+    return ids_down(w4g.vocab_argmax(t))
+
+
+def test_argmax_planted_full_vocab():
+    x, notes = synth.planted_logits(synth.VOCAB)
+    got = _argmax_gpu(x)
+    want = oracle.argmax(x)
+    assert np.array_equal(got, want), list(zip(notes, got, want))
+    assert want[2] == want[3] == want[4] == 0xFFFFFFFF
+    xb = synth.f32_to_bf16_bits(x)
+    xb[7] = synth.f32_to_bf16_bits(-np.abs(x[7]) - 1.0)
+    xb[7, 100], xb[7, 101] = 0x0001, 0x0002  # bf16 denormals
+    gotb = _argmax_gpu(xb, bf16=True)
+    assert np.array_equal(gotb, oracle.argmax(xb))
+
+
+@pytest.mark.parametrize("V", [1, 5, 1023, 1024, 1025, 3000, 4096])
+def test_argmax_small_vocab(V):
+    r = np.random.default_rng(V)
+    x = np.round(r.standard_normal((6, V)) * 2).astype(np.float32)  # many exact ties
+    x[1, V // 2] = np.nan
+    x[2, :] = 0.0
+    x[2, V - 1] = -0.0
+    assert np.array_equal(_argmax_gpu(x), oracle.argmax(x))
+
+
+def test_argmax_pitched_rows():
+    torch = pytest.importorskip("torch")
+    r = np.random.default_rng(1)
+    full = r.standard_normal((3, 2100)).astype(np.float32)
+    V = 2049
+    full[:, V:] = 1e30  # padding beyond vocab must be ignored
+    t = up_f32(full)
+    got = ids_down(w4g.vocab_argmax(t, vocab=V))
+    assert np.array_equal(got, oracle.argmax(np.ascontiguousarray(full[:, :V])))
+    del torch
+
+
+def test_argmax_random_rows_bitexact():
+    r = np.random.default_rng(123)
+    x = (r.standard_normal((64, 50000)) * 3).astype(np.float32)
+    x[32:] = np.round(x[32:] * 2) / 2
+    assert np.array_equal(_argmax_gpu(x), oracle.argmax(x))

@@ -1,0 +1,129 @@
+"""W4 g64 quantized GEMV/GEMM and greedy vocabulary argmax for MI355X (gfx950).
+
+A thin binding over the C ABI of ``libw4g.so`` (include/w4g.h): it checks
+tensor dtypes, devices and shapes, then passes raw device pointers and the
+current HIP stream.  Every step of the computation runs in the library's HIP
+kernels; there is no Python or CPU fallback, and a missing library raises.
+
+Tensors (all on one GPU, contiguous):
+  wq      [N][K/8]  int32/uint32  packed 4-bit codes, element 8i+j in bits [4j, 4j+4)
+  scales  [N][K/64] bfloat16
+  biases  [N][K/64] bfloat16
+  x       [B or M][K] bfloat16
+  returns y [B or M][N] float32
+"""
+import ctypes
+
+from . import _lib
+from ._lib import (BF16, F32, MAX_GEMV_BATCH, OP_ARGMAX, OP_GEMM, OP_GEMV, SENTINEL,  # noqa: F401
+                   W4GError)
+
+__all__ = ["qmm_gemv", "qmm_gemm", "vocab_argmax", "workspace_bytes", "SENTINEL", "W4GError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtypes, ndim, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on the same GPU as the weights")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_qmm(wq, scales, biases, x):
+    torch = _torch()
+    _need(wq, "wq", (torch.int32, torch.uint32), 2, None)
+    dev = wq.device
+    _need(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), 2, dev)
+    _need(biases, "biases", (torch.bfloat16, torch.int16, torch.uint16), 2, dev)
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2, dev)
+    N, K = wq.shape[0], wq.shape[1] * 8
+    if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
+        raise ValueError("scales and biases must be [N][K/64]")
+    if x.shape[1] != K:
+        raise ValueError(f"x must be [rows][{K}]")
+    return N, K
+
+
+def workspace_bytes(op, rows, n, k):
+    v = _lib.load().qmm_workspace_bytes(op, rows, n, k)
+    if v == ctypes.c_size_t(-1).value:
+        raise ValueError("sizes out of range for this op")
+    return v
+
+
+def _workspace(op, rows, n, k, device, workspace):
+    need = workspace_bytes(op, rows, n, k)
+    if need == 0:
+        return None, 0
+    torch = _torch()
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    return workspace, need
+
+
+def _call_qmm(fn, op, wq, scales, biases, x, y, workspace):
+    torch = _torch()
+    N, K = _check_qmm(wq, scales, biases, x)
+    rows = x.shape[0]
+    if y is None:
+        y = torch.empty((rows, N), dtype=torch.float32, device=wq.device)
+    _need(y, "y", (torch.float32,), 2, wq.device)
+    if tuple(y.shape) != (rows, N):
+        raise ValueError(f"y must be [{rows}][{N}]")
+    ws, nbytes = _workspace(op, rows, N, K, wq.device, workspace)
+    lib = _lib.load()
+    status = getattr(lib, fn)(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
+                              y.data_ptr(), rows, N, K, ws.data_ptr() if ws is not None else None,
+                              nbytes if ws is not None else 0, _stream(wq))
+    _lib.check(fn, status)
+    return y
+
+
+def qmm_gemv(wq, scales, biases, x, y=None, workspace=None):
+    """Decode product for 1 <= B <= 8 rows of x; returns y [B][N] fp32."""
+    if x.dim() == 2 and not 1 <= x.shape[0] <= MAX_GEMV_BATCH:
+        raise ValueError(f"qmm_gemv takes 1..{MAX_GEMV_BATCH} rows")
+    return _call_qmm("qmm_gemv", OP_GEMV, wq, scales, biases, x, y, workspace)
+
+
+def qmm_gemm(wq, scales, biases, x, y=None, workspace=None):
+    """Prompt product for any M >= 1 rows of x (matrix cores); returns y [M][N] fp32."""
+    return _call_qmm("qmm_gemm", OP_GEMM, wq, scales, biases, x, y, workspace)
+
+
+def vocab_argmax(logits, ids=None, workspace=None, vocab=None):
+    """Greedy ids [rows] (int32 tensor holding uint32 bits; 0xFFFFFFFF = non-finite row)."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32, torch.bfloat16), 2, None)
+    rows, ld = logits.shape
+    vocab = ld if vocab is None else vocab
+    dtype = F32 if logits.dtype == torch.float32 else BF16
+    if ids is None:
+        ids = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    _need(ids, "ids", (torch.int32, torch.uint32), 1, logits.device)
+    if ids.shape[0] != rows:
+        raise ValueError("ids must have one entry per row")
+    ws, nbytes = _workspace(OP_ARGMAX, rows, vocab, 0, logits.device, workspace)
+    lib = _lib.load()
+    status = lib.vocab_argmax(logits.data_ptr(), dtype, rows, vocab, ld, ids.data_ptr(),
+                              ws.data_ptr(), nbytes, _stream(logits))
+    _lib.check("vocab_argmax", status)
+    return ids

@@ -1,0 +1,59 @@
+"""ctypes view of libw4g.so (the C ABI declared in include/w4g.h)."""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4g.so")
+
+# status codes and constants, as in include/w4g.h
+OK, EINVAL_PTR, ESHAPE, EALIGN, EWORKSPACE, EDTYPE, ELAUNCH, EALIAS = range(8)
+F32, BF16 = 0, 1
+OP_GEMV, OP_GEMM, OP_ARGMAX = 0, 1, 2
+SENTINEL = 0xFFFFFFFF
+MAX_GEMV_BATCH = 8
+ABI_VERSION = 1
+
+EXPORTS = ["qmm_gemv", "qmm_gemm", "vocab_argmax", "qmm_workspace_bytes", "w4g_status_string",
+           "w4g_abi_version"]
+
+_lib = None
+
+
+class W4GError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+def load(path=None):
+    """Load the library (once).  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m w4_gemv_greedy_amd.build`")
+    lib = ctypes.CDLL(p)
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.qmm_gemv.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
+    lib.qmm_gemv.restype = I
+    lib.qmm_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
+    lib.qmm_gemm.restype = I
+    lib.vocab_argmax.argtypes = [P, I, I64, I64, I64, P, P, SZ, P]
+    lib.vocab_argmax.restype = I
+    lib.qmm_workspace_bytes.argtypes = [I, I64, I64, I64]
+    lib.qmm_workspace_bytes.restype = SZ
+    lib.w4g_status_string.argtypes = [I]
+    lib.w4g_status_string.restype = ctypes.c_char_p
+    lib.w4g_abi_version.argtypes = []
+    lib.w4g_abi_version.restype = I
+    if lib.w4g_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{p}: ABI version {lib.w4g_abi_version()}, expected {ABI_VERSION}")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def check(fn, status):
+    if status != OK:
+        raise W4GError(fn, status, load().w4g_status_string(status).decode())

@@ -1,0 +1,39 @@
+"""Compile the HIP library libw4g.so for gfx950, in-tree, next to this file.
+
+Usage: python -m w4_gemv_greedy_amd.build
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libw4g.so")
+SOURCES = ["gemv.hip", "gemm.hip", "argmax.hip", "abi.hip"]
+ARCH = "gfx950"
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    # no packed fp32 instructions anywhere in the library
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result",
+]
+
+
+def build(quiet=False):
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc] + FLAGS + srcs + ["-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
+    os.replace(tmp, LIB)
+    if msgs.strip() and not quiet:
+        print(msgs, file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,129 @@
+// C ABI of the library (declared in include/w4g.h): argument validation on the
+// host, then dispatch to the kernels on the caller's stream.  Validation never
+// touches the HIP runtime, so every rejection path runs without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/w4g.h"
+#include "w4g_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+// [p, p + bytes) and [q, q + qbytes) overlap (empty ranges never do)
+bool overlap(const void* p, size_t bytes, const void* q, size_t qbytes) {
+  if (!p || !q || bytes == 0 || qbytes == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + qbytes && b < a + bytes;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // rows, columns and batch below 2^31
+
+int check_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+              const uint16_t* x, const float* y, int64_t rows, int64_t N, int64_t K,
+              const void* workspace, size_t workspace_bytes, size_t need) {
+  if (!wq || !scales || !biases || !x || !y) return W4G_EINVAL_PTR;
+  if (rows < 1 || rows >= kMaxDim || N < 1 || N >= kMaxDim || K < 64 || K >= kMaxDim || K % 64)
+    return W4G_ESHAPE;
+  if (!aligned16(wq) || !aligned16(x) || !aligned16(y) || !aligned2(scales) || !aligned2(biases))
+    return W4G_EALIGN;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return W4G_EWORKSPACE;
+  const size_t ybytes = (size_t)rows * (size_t)N * sizeof(float);
+  const size_t wbytes = (size_t)N * (size_t)(K / 8) * sizeof(uint32_t);
+  const size_t gbytes = (size_t)N * (size_t)(K / 64) * sizeof(uint16_t);
+  const size_t xbytes = (size_t)rows * (size_t)K * sizeof(uint16_t);
+  if (overlap(y, ybytes, wq, wbytes) || overlap(y, ybytes, scales, gbytes) ||
+      overlap(y, ybytes, biases, gbytes) || overlap(y, ybytes, x, xbytes) ||
+      overlap(y, ybytes, workspace, need))
+    return W4G_EALIAS;
+  if (need > 0 && (overlap(workspace, need, wq, wbytes) || overlap(workspace, need, x, xbytes) ||
+                   overlap(workspace, need, scales, gbytes) ||
+                   overlap(workspace, need, biases, gbytes)))
+    return W4G_EALIAS;
+  return W4G_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? W4G_OK : W4G_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int w4g_abi_version(void) { return W4G_ABI_VERSION; }
+
+const char* w4g_status_string(int status) {
+  switch (status) {
+    case W4G_OK: return "ok";
+    case W4G_EINVAL_PTR: return "a required pointer is NULL";
+    case W4G_ESHAPE: return "a size is out of range";
+    case W4G_EALIGN: return "a buffer is not aligned (16 bytes for codes, x, y, logits)";
+    case W4G_EWORKSPACE: return "workspace missing or too small";
+    case W4G_EDTYPE: return "unknown dtype or op";
+    case W4G_ELAUNCH: return "the HIP runtime refused a launch";
+    case W4G_EALIAS: return "an output overlaps an input or the workspace";
+    default: return "unknown status";
+  }
+}
+
+size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k) {
+  switch (op) {
+    case W4G_OP_GEMV:
+      if (rows < 1 || rows > W4G_MAX_GEMV_BATCH || n < 1 || n >= kMaxDim || k < 64 ||
+          k >= kMaxDim || k % 64)
+        return (size_t)-1;
+      return 0;
+    case W4G_OP_GEMM:
+      if (rows < 1 || rows >= kMaxDim || n < 1 || n >= kMaxDim || k < 64 || k >= kMaxDim || k % 64)
+        return (size_t)-1;
+      return w4g::gemm_workspace_bytes(rows, n, k);
+    case W4G_OP_ARGMAX:
+      if (rows < 1 || rows > 65535 || n < 1 || n >= kMaxDim) return (size_t)-1;
+      return w4g::argmax_workspace_bytes(rows, n);
+    default:
+      return (size_t)-1;
+  }
+}
+
+int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+             const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  if (B < 1 || B > W4G_MAX_GEMV_BATCH) return (!wq || !scales || !biases || !x || !y) ? W4G_EINVAL_PTR : W4G_ESHAPE;
+  const int rc = check_qmm(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, 0);
+  if (rc) return rc;
+  return from_hip(w4g::launch_gemv(wq, scales, biases, x, y, (int)B, N, K,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+             const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  if (M < 1 || M >= kMaxDim || N < 1 || N >= kMaxDim || K < 64 || K >= kMaxDim || K % 64)
+    return (!wq || !scales || !biases || !x || !y) ? W4G_EINVAL_PTR : W4G_ESHAPE;
+  const size_t need = w4g::gemm_workspace_bytes(M, N, K);
+  const int rc = check_qmm(wq, scales, biases, x, y, M, N, K, workspace, workspace_bytes, need);
+  if (rc) return rc;
+  return from_hip(w4g::launch_gemm(wq, scales, biases, x, y, M, N, K, workspace,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+int vocab_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                 uint32_t* ids, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !ids) return W4G_EINVAL_PTR;
+  if (dtype != W4G_F32 && dtype != W4G_BF16) return W4G_EDTYPE;
+  if (rows < 1 || rows > 65535 || vocab < 1 || vocab >= kMaxDim || ld < vocab || ld >= ((int64_t)1 << 40))
+    return W4G_ESHAPE;
+  if (!aligned16(logits) || (reinterpret_cast<uintptr_t>(ids) & 3u)) return W4G_EALIGN;
+  const size_t need = w4g::argmax_workspace_bytes(rows, vocab);
+  if (!workspace || workspace_bytes < need) return W4G_EWORKSPACE;
+  const size_t esz = dtype == W4G_F32 ? 4 : 2;
+  const size_t lbytes = ((size_t)(rows - 1) * (size_t)ld + (size_t)vocab) * esz;
+  if (overlap(ids, (size_t)rows * 4, logits, lbytes) || overlap(ids, (size_t)rows * 4, workspace, need) ||
+      overlap(workspace, need, logits, lbytes))
+    return W4G_EALIAS;
+  return from_hip(w4g::launch_argmax(logits, dtype, rows, vocab, ld, ids, workspace,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

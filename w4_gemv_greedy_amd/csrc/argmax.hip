@@ -1,0 +1,158 @@
+// Greedy vocabulary argmax in two passes.
+//
+// Rules (TensorFold PR #1433, step-1 description): a row holding any NaN,
+// +Inf or -Inf fails; pass 1 reports such a block with bit 31 set in its id
+// word (and NaN in its value word), and pass 2 turns any flag in the row into
+// the sentinel 0xFFFFFFFF.  Otherwise the largest value wins and equal values
+// go to the lowest id (a pick that ties to the higher id is one of the planted
+// failures there).  The session reads the sentinel as a failure, never as a
+// logit (step-2 description).
+//
+// Comparison: each finite fp32 value maps to an unsigned key that orders
+// exactly as IEEE comparison does, with -0.0 and +0.0 given the same key, so
+// denormals compare exactly whatever the float denormal mode.  A candidate is
+// the 64-bit word (key << 32) | (0xFFFFFFFF - id); the maximum word is the
+// largest value with the lowest id, so every reduction step is an unsigned max
+// and the result does not depend on the reduction tree.
+#include "w4g_internal.h"
+
+namespace w4g {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr uint32_t kFlag = 0x80000000u;
+
+__device__ __forceinline__ uint32_t order_key(uint32_t u) {
+  if ((u & 0x7FFFFFFFu) == 0) return 0x80000000u;  // +0 and -0 tie
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t key_bits(uint32_t k) {
+  return (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+}
+__device__ __forceinline__ bool finite_bits(uint32_t u) {
+  return (u & 0x7F800000u) != 0x7F800000u;
+}
+__device__ __forceinline__ uint64_t cand(uint32_t bits, uint32_t id) {
+  return ((uint64_t)order_key(bits) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Block-wide reduction of (best, bad); returns the result in every thread.
+__device__ __forceinline__ void block_reduce(uint64_t& best, bool& bad) {
+  __shared__ uint64_t s_best[kThreads / 64];
+  __shared__ int s_bad[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = (uint32_t)best, hi = (uint32_t)(best >> 32);
+    lo = __shfl_xor(lo, off);
+    hi = __shfl_xor(hi, off);
+    best = umax64(best, ((uint64_t)hi << 32) | lo);
+  }
+  const bool any_bad = __any(bad);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_best[wave] = best;
+    s_bad[wave] = any_bad ? 1 : 0;
+  }
+  __syncthreads();
+  best = s_best[0];
+  int b = s_bad[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) {
+    best = umax64(best, s_best[w]);
+    b |= s_bad[w];
+  }
+  bad = b != 0;
+}
+
+// Widened element bits: fp32 as is, bf16 shifted into the top half (exact).
+template <int DT>
+__device__ __forceinline__ uint32_t elem_bits(const void* p, int64_t i) {
+  if (DT == 0) return reinterpret_cast<const uint32_t*>(p)[i];
+  return ((uint32_t)reinterpret_cast<const uint16_t*>(p)[i]) << 16;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void argmax_pass1(const void* __restrict__ logits,
+                                                         int64_t ld, int64_t vocab, int nblk,
+                                                         uint2* __restrict__ rec) {
+  const int64_t row = blockIdx.y;
+  const int64_t blk = blockIdx.x;
+  const int64_t i0 = blk * kArgmaxBlock + (int64_t)threadIdx.x * 4;
+  const int64_t base = row * ld;
+  uint32_t u[4];
+  const bool vec = ((ld & 3) == 0) && (i0 + 3 < vocab);
+  if (vec) {
+    if (DT == 0) {
+      const uint4 v = *reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint32_t*>(logits) + base + i0);
+      u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(
+          reinterpret_cast<const uint16_t*>(logits) + base + i0);
+      u[0] = v.x << 16; u[1] = v.x & 0xFFFF0000u; u[2] = v.y << 16; u[3] = v.y & 0xFFFF0000u;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[j] = (i0 + j < vocab) ? elem_bits<DT>(logits, base + i0 + j) : 0u;
+  }
+  uint64_t best = 0;  // below every finite candidate
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (i0 + j < vocab) {
+      if (!finite_bits(u[j])) bad = true;
+      else best = umax64(best, cand(u[j], (uint32_t)(i0 + j)));
+    }
+  }
+  block_reduce(best, bad);
+  if (threadIdx.x == 0) {
+    uint2 r;
+    if (bad) {
+      r.x = 0x7FC00000u;
+      r.y = kFlag | (uint32_t)(blk * kArgmaxBlock);
+    } else {
+      r.x = key_bits((uint32_t)(best >> 32));
+      r.y = 0xFFFFFFFFu - (uint32_t)best;
+    }
+    rec[row * nblk + blk] = r;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void argmax_pass2(const uint2* __restrict__ rec, int nblk,
+                                                         uint32_t* __restrict__ ids) {
+  const int64_t row = blockIdx.x;
+  uint64_t best = 0;
+  bool bad = false;
+  for (int i = threadIdx.x; i < nblk; i += kThreads) {
+    const uint2 r = rec[row * nblk + i];
+    if (r.y & kFlag) bad = true;
+    else best = umax64(best, cand(r.x, r.y));
+  }
+  block_reduce(best, bad);
+  if (threadIdx.x == 0) ids[row] = bad ? 0xFFFFFFFFu : 0xFFFFFFFFu - (uint32_t)best;
+}
+
+}  // namespace
+
+size_t argmax_workspace_bytes(int64_t rows, int64_t vocab) {
+  const int64_t nblk = (vocab + kArgmaxBlock - 1) / kArgmaxBlock;
+  return (size_t)(rows * nblk) * sizeof(uint2);
+}
+
+hipError_t launch_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                         uint32_t* ids, void* workspace, hipStream_t stream) {
+  const int nblk = (int)((vocab + kArgmaxBlock - 1) / kArgmaxBlock);
+  uint2* rec = reinterpret_cast<uint2*>(workspace);
+  const dim3 g1((unsigned)nblk, (unsigned)rows);
+  if (dtype == 0)
+    hipLaunchKernelGGL(argmax_pass1<0>, g1, dim3(kThreads), 0, stream, logits, ld, vocab, nblk, rec);
+  else
+    hipLaunchKernelGGL(argmax_pass1<1>, g1, dim3(kThreads), 0, stream, logits, ld, vocab, nblk, rec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(argmax_pass2, dim3((unsigned)rows), dim3(kThreads), 0, stream, rec, nblk, ids);
+  return hipGetLastError();
+}
+
+}  // namespace w4g

@@ -1,0 +1,28 @@
+// Internal declarations shared by the library's own translation units only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4g {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Kernel launchers.  Arguments are already validated; each returns the
+// hipError_t of its launch(es).
+hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                       const uint16_t* x, float* y, int B, int64_t N, int64_t K,
+                       hipStream_t stream);
+hipError_t launch_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                       const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
+                       void* workspace, hipStream_t stream);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                         uint32_t* ids, void* workspace, hipStream_t stream);
+size_t argmax_workspace_bytes(int64_t rows, int64_t vocab);
+
+constexpr int kArgmaxBlock = 1024;  // ids per pass-1 record
+
+}  // namespace w4g
