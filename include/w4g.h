@@ -95,12 +95,38 @@ extern "C" {
  * s*D + (b - 128*s)*X, where D is the dot of x with (128 + q) taken over
  * bf16 pairs in ascending pair order and X the fp32 sum of those 32 x; each
  * lane adds its chunk terms in ascending chunk order, and the 32 lane sums
- * meet in a fixed xor butterfly (16, 8, 4, 2, 1).  Row m of a B-row call is
- * bitwise equal to the same row computed alone.
+ * meet in a fixed xor butterfly (16, 8, 4, 2, 1).  That is the order of the
+ * vector-ALU family; qmm_gemv may pick the matrix-core family instead (see
+ * qmm_gemv_ex), by B and shape only, so a given (B, N, K) always runs the
+ * same kernel and its bits never change from call to call.
  */
 int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
              const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* kernel families for qmm_gemv_ex */
+#define W4G_GEMV_AUTO 0   /* the library's choice by B and shape (what qmm_gemv uses) */
+#define W4G_GEMV_VALU 1   /* vector-ALU dot2 kernel (the order documented for qmm_gemv) */
+#define W4G_GEMV_MFMA 2   /* matrix-core kernel (order documented below) */
+#define W4G_GEMV_VALU_REGS 3  /* vector-ALU family, register-staged variant (same bits as 1) */
+
+/*
+ * qmm_gemv with an explicit kernel family.  Same arguments and results as
+ * qmm_gemv; `kernel` is one of W4G_GEMV_*, else W4G_EDTYPE.  The vector-ALU
+ * family stages x in LDS when B * 2.125 * K bytes fit in 64 KiB and in
+ * registers otherwise; W4G_GEMV_VALU_REGS forces the register variant (for
+ * checking that both variants give the same bits).
+ * The matrix-core family (W4G_GEMV_MFMA) feeds the codes to
+ * v_mfma_f32_32x32x16_bf16 as exact bf16 values 128 + q; per 64-group it adds
+ * s*P_g and (b - 128 s)*X_g in fp32 (P_g the matrix-core group product, X_g
+ * the fp32 group sum of x), wave w of four taking the groups g = w (mod 4) in
+ * ascending order, and the four wave sums are added in ascending order.
+ * Within one family, row m of a B-row call is bitwise equal to the same row
+ * computed alone; the two families agree within fp32 rounding, not bitwise.
+ */
+int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K,
+                void* workspace, size_t workspace_bytes, void* stream, int kernel);
 
 /*
  * Prompt product on the matrix cores, any M >= 1 rows.

@@ -1,0 +1,85 @@
+"""Parity at the full model shapes, in the configurations the benchmark runs.
+
+The GPU computes every output; the oracle checks a sample of output rows it
+can afford one by one (the first and last 64 rows and 256 seeded random ones),
+against the same seeded inputs.  The argmax is bit-exact on the GPU's own
+logits, and end to end the greedy id must match the oracle's unless the
+oracle's top-two gap is within the products' error bound."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close, down, ids_down, up_bf16, up_u32
+from w4_gemv_greedy_amd import synth
+
+pytestmark = pytest.mark.gpu
+w4g = pytest.importorskip("w4_gemv_greedy_amd")
+
+SHAPES = {"o_proj": (5120, 5120, synth.O_PROJ), "gate_up": (34816, 5120, synth.GATE_UP),
+          "down": (5120, 17408, synth.DOWN), "lm_head": (248320, 5120, synth.LM_HEAD)}
+_cache = {}
+
+
+def _weights(name):
+    if name not in _cache:
+        N, K, mid = SHAPES[name]
+        wq, sc, bi = synth.weights(N, K, workload=5, matrix=mid, layer=0)
+        _cache.clear()  # keep one full matrix on the host and the GPU at a time
+        _cache[name] = (wq, sc, bi, (up_u32(wq), up_bf16(sc), up_bf16(bi)))
+    return _cache[name]
+
+
+def _sample_rows(N, seed):
+    r = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(64), np.arange(N - 64, N), r.choice(N, 256, replace=False)])
+    return np.unique(rows)
+
+
+@pytest.mark.parametrize("family", ["valu", "mfma", "auto"])
+@pytest.mark.parametrize("B", [1, 4, 8])
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_gemv_full_shape(name, B, family):
+    wq, sc, bi, W = _weights(name)
+    N, K, mid = SHAPES[name]
+    x = synth.activations(B, K, workload=5, matrix=mid, layer=B)
+    kernel = {"valu": 1, "mfma": 2, "auto": 0}[family]
+    y = down(w4g.qmm_gemv(*W, up_bf16(x), kernel=kernel))
+    rows = _sample_rows(N, B)
+    ref = oracle.qmm_rows(wq, sc, bi, x, rows)
+    e = assert_close(y[:, rows], ref, f"{name} B={B} {family}")
+    print(f"{name} B={B} {family}: normwise {e:.2e} over {rows.size} sampled rows")
+
+
+@pytest.mark.parametrize("name", ["o_proj", "gate_up", "down"])
+def test_gemm_prompt_full_shape(name):
+    wq, sc, bi, W = _weights(name)
+    N, K, mid = SHAPES[name]
+    M = 512
+    x = synth.activations(M, K, workload=4, matrix=mid, layer=0)
+    y = down(w4g.qmm_gemm(*W, up_bf16(x)))
+    cols = np.unique(np.concatenate([np.arange(32), np.arange(N - 32, N),
+                                     np.random.default_rng(1).choice(N, 64, replace=False)]))
+    ref = oracle.qmm_rows(wq, sc, bi, x, cols)
+    e = assert_close(y[:, cols], ref, f"prompt {name}")
+    print(f"prompt {name} M=512: normwise {e:.2e} over {cols.size} sampled columns x 512 rows")
+
+
+def test_lm_head_argmax_end_to_end():
+    wq, sc, bi, W = _weights("lm_head")
+    N, K, mid = SHAPES["lm_head"]
+    B = 4
+    x = synth.activations(B, K, workload=3, matrix=mid, layer=0)
+    logits = w4g.qmm_gemv(*W, up_bf16(x))
+    ids = ids_down(w4g.vocab_argmax(logits))
+    lg = down(logits)
+    # bit-exact on identical logits
+    assert np.array_equal(ids, oracle.argmax(lg))
+    # end to end against the oracle's own logits
+    ref = oracle.qmm(wq, sc, bi, x)
+    assert_close(lg, ref, "lm_head logits")
+    want = oracle.argmax(ref)
+    for m in range(B):
+        if ids[m] != want[m]:
+            top2 = np.sort(ref[m])[-2:]
+            bound = 2e-5 * np.max(np.abs(ref[m]))
+            assert top2[1] - top2[0] <= 2 * bound, f"row {m}: id {ids[m]} vs {want[m]} beyond a tie"

@@ -20,42 +20,74 @@ def _case(N, K, rows, seed):
 
 
 GEMV_SHAPES = [(37, 64), (64, 1088), (129, 2048), (200, 5120), (40, 17408), (9, 3072)]
+FAMILIES = {"valu": 1, "mfma": 2, "auto": 0, "valu_regs": 3}
 
 
+@pytest.mark.parametrize("family", ["valu", "mfma"])
 @pytest.mark.parametrize("N,K", GEMV_SHAPES)
 @pytest.mark.parametrize("B", [1, 2, 4, 8])
-def test_gemv_matches_oracle(N, K, B):
+def test_gemv_matches_oracle(N, K, B, family):
     wq, sc, bi, x = _case(N, K, B, N + K)
-    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x)))
+    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x), kernel=FAMILIES[family]))
     ref = oracle.qmm(wq, sc, bi, x)
-    e = assert_close(y, ref, f"gemv B={B} N={N} K={K}")
-    print(f"gemv B={B} N={N} K={K} normwise {e:.2e}")
+    e = assert_close(y, ref, f"gemv[{family}] B={B} N={N} K={K}")
+    print(f"gemv[{family}] B={B} N={N} K={K} normwise {e:.2e}")
 
 
+@pytest.mark.parametrize("family", ["valu", "mfma", "auto"])
 @pytest.mark.parametrize("B", [3, 5, 6, 7])
-def test_gemv_odd_batches(B):
+def test_gemv_odd_batches(B, family):
     wq, sc, bi, x = _case(70, 1024, B, 7)
-    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x)))
-    assert_close(y, oracle.qmm(wq, sc, bi, x), f"gemv B={B}")
+    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x), kernel=FAMILIES[family]))
+    assert_close(y, oracle.qmm(wq, sc, bi, x), f"gemv[{family}] B={B}")
 
 
-def test_gemv_batch_invariance_and_determinism():
-    wq, sc, bi, x = _case(300, 5120, 8, 3)
+@pytest.mark.parametrize("K", [5120, 17408])
+@pytest.mark.parametrize("family", ["valu", "mfma"])
+def test_gemv_batch_invariance_and_determinism(family, K):
+    # at K = 17408 the vector-ALU family stages x in registers for B >= 2 and in
+    # LDS for B = 1: the two variants must give the same bits
+    wq, sc, bi, x = _case(300, K, 8, 3)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
-    y8 = down(w4g.qmm_gemv(*W, up_bf16(x)))
-    y8b = down(w4g.qmm_gemv(*W, up_bf16(x)))
+    k = FAMILIES[family]
+    y8 = down(w4g.qmm_gemv(*W, up_bf16(x), kernel=k))
+    y8b = down(w4g.qmm_gemv(*W, up_bf16(x), kernel=k))
     assert np.array_equal(y8.view(np.uint32), y8b.view(np.uint32)), "not run-to-run deterministic"
     for m in (0, 3, 7):
-        y1 = down(w4g.qmm_gemv(*W, up_bf16(x[m:m + 1])))
+        y1 = down(w4g.qmm_gemv(*W, up_bf16(x[m:m + 1]), kernel=k))
         assert np.array_equal(y1[0].view(np.uint32), y8[m].view(np.uint32)), f"row {m} differs at B=1"
+    for Bn in (2, 5):
+        yb = down(w4g.qmm_gemv(*W, up_bf16(x[:Bn]), kernel=k))
+        assert np.array_equal(yb.view(np.uint32), y8[:Bn].view(np.uint32)), f"B={Bn} differs"
 
 
-def test_gemv_row_permutation_bitwise():
-    wq, sc, bi, x = _case(96, 2048, 1, 4)
+@pytest.mark.parametrize("family", ["valu", "mfma"])
+def test_gemv_row_permutation_bitwise(family):
+    wq, sc, bi, x = _case(96, 2048, 2, 4)
     p = np.random.default_rng(0).permutation(96)
-    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x)))
-    yp = down(w4g.qmm_gemv(up_u32(wq[p]), up_bf16(sc[p]), up_bf16(bi[p]), up_bf16(x)))
+    k = FAMILIES[family]
+    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x), kernel=k))
+    yp = down(w4g.qmm_gemv(up_u32(wq[p]), up_bf16(sc[p]), up_bf16(bi[p]), up_bf16(x), kernel=k))
     assert np.array_equal(yp.view(np.uint32), y[:, p].view(np.uint32))
+
+
+@pytest.mark.parametrize("B", [1, 2, 4])
+@pytest.mark.parametrize("N,K", [(70, 1088), (300, 5120), (64, 17408)])
+def test_gemv_valu_variants_bitwise(N, K, B):
+    """The LDS-staged and register-staged vector-ALU variants give the same bits."""
+    wq, sc, bi, x = _case(N, K, B, 31)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x))
+    a = down(w4g.qmm_gemv(*W, kernel=1))
+    b = down(w4g.qmm_gemv(*W, kernel=3))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_gemv_families_agree():
+    wq, sc, bi, x = _case(256, 5120, 4, 12)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x))
+    a = down(w4g.qmm_gemv(*W, kernel=1))
+    b = down(w4g.qmm_gemv(*W, kernel=2))
+    assert_close(a, b, "valu vs mfma")
 
 
 GEMM_SHAPES = [(1, 37, 64), (7, 130, 1088), (130, 256, 1024), (64, 128, 5120), (33, 70, 17408)]

@@ -15,8 +15,9 @@ Tensors (all on one GPU, contiguous):
 import ctypes
 
 from . import _lib
-from ._lib import (BF16, F32, MAX_GEMV_BATCH, OP_ARGMAX, OP_GEMM, OP_GEMV, SENTINEL,  # noqa: F401
-                   W4GError)
+from ._lib import (BF16, F32, GEMV_AUTO, GEMV_MFMA, GEMV_VALU, GEMV_VALU_REGS,  # noqa: F401
+                   MAX_GEMV_BATCH,
+                   OP_ARGMAX, OP_GEMM, OP_GEMV, SENTINEL, W4GError)
 
 __all__ = ["qmm_gemv", "qmm_gemm", "vocab_argmax", "workspace_bytes", "SENTINEL", "W4GError"]
 
@@ -79,7 +80,7 @@ def _workspace(op, rows, n, k, device, workspace):
     return workspace, need
 
 
-def _call_qmm(fn, op, wq, scales, biases, x, y, workspace):
+def _call_qmm(fn, op, wq, scales, biases, x, y, workspace, extra=()):
     torch = _torch()
     N, K = _check_qmm(wq, scales, biases, x)
     rows = x.shape[0]
@@ -92,16 +93,22 @@ def _call_qmm(fn, op, wq, scales, biases, x, y, workspace):
     lib = _lib.load()
     status = getattr(lib, fn)(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
                               y.data_ptr(), rows, N, K, ws.data_ptr() if ws is not None else None,
-                              nbytes if ws is not None else 0, _stream(wq))
+                              nbytes if ws is not None else 0, _stream(wq), *extra)
     _lib.check(fn, status)
     return y
 
 
-def qmm_gemv(wq, scales, biases, x, y=None, workspace=None):
-    """Decode product for 1 <= B <= 8 rows of x; returns y [B][N] fp32."""
+def qmm_gemv(wq, scales, biases, x, y=None, workspace=None, kernel=GEMV_AUTO):
+    """Decode product for 1 <= B <= 8 rows of x; returns y [B][N] fp32.
+
+    kernel: GEMV_AUTO (the library's choice), GEMV_VALU, GEMV_MFMA, or
+    GEMV_VALU_REGS (the register-staged variant of the vector-ALU family).
+    """
     if x.dim() == 2 and not 1 <= x.shape[0] <= MAX_GEMV_BATCH:
         raise ValueError(f"qmm_gemv takes 1..{MAX_GEMV_BATCH} rows")
-    return _call_qmm("qmm_gemv", OP_GEMV, wq, scales, biases, x, y, workspace)
+    if kernel == GEMV_AUTO:
+        return _call_qmm("qmm_gemv", OP_GEMV, wq, scales, biases, x, y, workspace)
+    return _call_qmm("qmm_gemv_ex", OP_GEMV, wq, scales, biases, x, y, workspace, (int(kernel),))
 
 
 def qmm_gemm(wq, scales, biases, x, y=None, workspace=None):

@@ -13,7 +13,9 @@ SENTINEL = 0xFFFFFFFF
 MAX_GEMV_BATCH = 8
 ABI_VERSION = 1
 
-EXPORTS = ["qmm_gemv", "qmm_gemm", "vocab_argmax", "qmm_workspace_bytes", "w4g_status_string",
+GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_VALU_REGS = 0, 1, 2, 3
+
+EXPORTS = ["qmm_gemv", "qmm_gemv_ex", "qmm_gemm", "vocab_argmax", "qmm_workspace_bytes", "w4g_status_string",
            "w4g_abi_version"]
 
 _lib = None
@@ -37,6 +39,8 @@ def load(path=None):
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.qmm_gemv.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.qmm_gemv.restype = I
+    lib.qmm_gemv_ex.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P, I]
+    lib.qmm_gemv_ex.restype = I
     lib.qmm_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.qmm_gemm.restype = I
     lib.vocab_argmax.argtypes = [P, I, I64, I64, I64, P, P, SZ, P]

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4g.so")
-SOURCES = ["gemv.hip", "gemm.hip", "argmax.hip", "abi.hip"]
+SOURCES = ["gemv.hip", "gemv_mfma.hip", "gemm.hip", "argmax.hip", "abi.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",

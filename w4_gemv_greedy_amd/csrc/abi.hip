@@ -86,14 +86,29 @@ size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k) {
   }
 }
 
+int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
+                size_t workspace_bytes, void* stream, int kernel) {
+  if (kernel != W4G_GEMV_AUTO && kernel != W4G_GEMV_VALU && kernel != W4G_GEMV_MFMA &&
+      kernel != W4G_GEMV_VALU_REGS)
+    return W4G_EDTYPE;
+  if (B < 1 || B > W4G_MAX_GEMV_BATCH)
+    return (!wq || !scales || !biases || !x || !y) ? W4G_EINVAL_PTR : W4G_ESHAPE;
+  const int rc = check_qmm(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, 0);
+  if (rc) return rc;
+  if (kernel == W4G_GEMV_AUTO) kernel = w4g::gemv_auto_family((int)B, N, K);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (kernel == W4G_GEMV_MFMA)
+    return from_hip(w4g::launch_gemv_mfma(wq, scales, biases, x, y, (int)B, N, K, s));
+  return from_hip(w4g::launch_gemv(wq, scales, biases, x, y, (int)B, N, K,
+                                   kernel == W4G_GEMV_VALU_REGS, s));
+}
+
 int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
              const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
              size_t workspace_bytes, void* stream) {
-  if (B < 1 || B > W4G_MAX_GEMV_BATCH) return (!wq || !scales || !biases || !x || !y) ? W4G_EINVAL_PTR : W4G_ESHAPE;
-  const int rc = check_qmm(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, 0);
-  if (rc) return rc;
-  return from_hip(w4g::launch_gemv(wq, scales, biases, x, y, (int)B, N, K,
-                                   reinterpret_cast<hipStream_t>(stream)));
+  return qmm_gemv_ex(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, stream,
+                     W4G_GEMV_AUTO);
 }
 
 int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,

@@ -1,73 +1,302 @@
-// Decode product y[b][n] = sum_k x[b][k] * (q*s + b)[n][k] for 1 <= B <= 8,
+// Decode product y[b][n] = sum_k x[b][k] * (q*s + b)[n][k] on the vector ALUs,
 // 4-bit affine codes with one bf16 scale and bias per 64-group (TensorFold
 // PR #1437, Receipt: "4-bit affine with group 64"; fp32 result: same PR,
 // commit "Add the pair seam and register its kernels with the kernel
 // contract").
 //
-// Work split: a 32-lane half wave owns R output rows.  It walks K in chunks of
-// 1024 elements; in each chunk lane j owns elements [32j, 32j+32), i.e. half
-// of one 64-group, and reads them as one 128-bit load per row (the half wave
-// reads 512 contiguous bytes of each row).  The four code words are expanded
-// in registers to bf16 pairs (128 + q) by OR-ing the nibble into the exponent
-// pattern of 128.0, and v_dot2 against bf16 pairs of x accumulates
-// D = sum x*(128 + q) in fp32.  The lane then adds s*D + (b - 128 s)*X, X the
-// fp32 sum of its 32 x values, so the group's affine map is applied once per
-// half group instead of once per weight.  After the last chunk the 32 lane
-// sums meet in an xor butterfly.  The order of every floating-point step
-// depends on K alone, so a row's bits do not change with N, B or the grid
-// (TensorFold PR #1433, step-2 description: the K reduction tree is the full
-// matrix's).
+// Arithmetic, per output row and batch row (the order depends on K alone, so a
+// row's bits do not change with N, B or the grid: TensorFold PR #1433, step-2
+// description, the K reduction tree is the full matrix's):
+//   K is cut into chunks of 1024 elements; in chunk c, lane l of a 32-lane
+//   half wave owns elements [32l, 32l + 32), half of one 64-group.  The lane
+//   expands its four code words to bf16 pairs (128 + q[i], 128 + q[i+4]) by
+//   OR-ing each nibble into the bit pattern of 128.0, and v_dot2 against the
+//   matching pairs (x[i], x[i+4]) accumulates D = sum x*(128 + q) in fp32,
+//   word by word and pair by pair.  X is the fp32 sum of the same 32 x, taken
+//   over the same pairs in the same order against (1, 1).  The lane then adds
+//   s*D and (b - 128 s)*X to its running sum with fused multiply-adds
+//   (b - 128 s itself one fused multiply-add), chunk after chunk in ascending
+//   order.  After the last chunk the 32 lane sums meet in a fixed tree: the
+//   two 16-lane rows add lane by lane, then each row folds by mirror
+//   (i, 15 - i), half mirror (i, 7 - i), and quad swaps (i, i ^ 2), (i, i ^ 1).
+//
+// Memory: a half wave owns whole rows; in each chunk lane l reads one 16-byte
+// code vector at byte 16l, so a wave-wide load covers 512 contiguous bytes of
+// each of two rows.  A work item is one chunk of R consecutive rows; items are
+// double buffered (one in flight while the other is consumed).  The
+// activations are paired and summed once per workgroup into LDS, laid out so
+// that a half wave's reads are contiguous, and each item's R rows share them.
 #include "w4g_internal.h"
+#ifdef W4G_TUNING
+#include <stdlib.h>
+#endif
 
 namespace w4g {
 namespace {
 
 constexpr int kChunk = 1024;
+constexpr int kThreads = 256;
+constexpr int kHalfWaves = kThreads / 32;
+constexpr size_t kMaxLds = 64 * 1024;  // LDS one workgroup may take here
 constexpr uint32_t kMagic128 = 0x43004300u;  // bf16 pair (128.0, 128.0)
 constexpr uint32_t kOnes = 0x3F803F80u;      // bf16 pair (1.0, 1.0)
+constexpr uint32_t kNibbles = 0x000F000Fu;
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// (x[j], x[j+4]) pairs of an 8-element block held as natural pairs
-// n0 = (x0,x1), n1 = (x2,x3), n2 = (x4,x5), n3 = (x6,x7).
-__device__ __forceinline__ void pair_x(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t n3,
-                                       uint32_t* p) {
-  p[0] = __builtin_amdgcn_perm(n2, n0, 0x05040100u);  // (x0, x4)
-  p[1] = __builtin_amdgcn_perm(n2, n0, 0x07060302u);  // (x1, x5)
-  p[2] = __builtin_amdgcn_perm(n3, n1, 0x05040100u);  // (x2, x6)
-  p[3] = __builtin_amdgcn_perm(n3, n1, 0x07060302u);  // (x3, x7)
+// (a & m) | g in one instruction (the compiler would emit two with literals)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t g) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(g));
+  return d;
 }
 
-// (128 + q[j], 128 + q[j+4]) bf16 pairs of one code word, j = 0..3.
-__device__ __forceinline__ void pair_q(uint32_t w, uint32_t* p) {
-  p[0] = (w & 0x000F000Fu) | kMagic128;
-  p[1] = ((w >> 4) & 0x000F000Fu) | kMagic128;
-  p[2] = ((w >> 8) & 0x000F000Fu) | kMagic128;
-  p[3] = ((w >> 12) & 0x000F000Fu) | kMagic128;
+// (x[i], x[i+4]) pairs of an 8-element block held as natural pairs
+// (x0,x1), (x2,x3), (x4,x5), (x6,x7).
+__device__ __forceinline__ uint4 pair_x(uint4 v) {
+  uint4 p;
+  p.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // (x0, x4)
+  p.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // (x1, x5)
+  p.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // (x2, x6)
+  p.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // (x3, x7)
+  return p;
+}
+
+// D += the 8 codes of one word against 4 x pairs
+__device__ __forceinline__ float dot_word(uint32_t w, uint4 xp, float d, uint32_t m, uint32_t g) {
+  d = dot2(and_or(w, m, g), xp.x, d);
+  d = dot2(and_or(w >> 4, m, g), xp.y, d);
+  d = dot2(and_or(w >> 8, m, g), xp.z, d);
+  d = dot2(and_or(w >> 12, m, g), xp.w, d);
+  return d;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-template <int B, int R>
-__global__ __launch_bounds__(64) void gemv_valu_kernel(const uint32_t* __restrict__ wq,
-                                                       const uint16_t* __restrict__ scales,
-                                                       const uint16_t* __restrict__ biases,
-                                                       const uint16_t* __restrict__ x,
-                                                       float* __restrict__ y, int64_t N,
-                                                       int64_t K) {
-  const int lane = threadIdx.x & 31;
-  const int64_t row0 = ((int64_t)blockIdx.x * 2 + (threadIdx.x >> 5)) * R;
-  const int64_t G = K >> 6;
-  const int64_t K8 = K >> 3;
+// Sum over the 32 lanes of each half wave, the same bits in every lane:
+// the two 16-lane rows add lane by lane (v_permlane16_swap), then each row
+// folds onto itself by mirror (lane i with 15 - i), half mirror (i with
+// 7 - i within 8) and the two quad swaps (i with i ^ 2, then i ^ 1).  Every
+// step adds a pair of equal-order partners, so all lanes end equal.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int o = __builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false);
+  return v + __int_as_float(o);
+}
+__device__ __forceinline__ float half_wave_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  v = dpp_add<0x140>(v);  // row_mirror
+  v = dpp_add<0x141>(v);  // row_half_mirror
+  v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+  return v;
+}
+
+template <int R>
+struct Item {
+  uint4 w[R];
+  uint16_t s[R], b[R];  // kept 16-bit so no widening copy waits on the loads
+};
+
+// LDS: paired activations [B][C][4][32] uint4 (chunk, vector, lane), then lane
+// sums [B][C][32] float.  P items are in flight per half wave (a ring of P
+// buffers).  A half wave owns `ng` groups of R consecutive rows
+// (rows past N repeat row N-1 and store nothing; both half waves of a wave run
+// the same number of items, so every branch in the stream is wave-uniform).
+// A lane past the end of a short last chunk reads lane 0 of chunk 0 (always
+// staged, so finite) and adds exact zeros.
+template <int B, int R, int P, bool RAGGED>
+__global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __restrict__ wq,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const uint16_t* __restrict__ biases,
+                                                             const uint16_t* __restrict__ x,
+                                                             float* __restrict__ y, int64_t N,
+                                                             int64_t K, int64_t ng) {
+  extern __shared__ uint4 s_mem[];
+  const int64_t K8 = K >> 3, K32 = K >> 5, G = K >> 6;
+  const int C = (int)((K + kChunk - 1) / kChunk);
+  uint4* s_xp = s_mem;                                                   // [B][C][4][32]
+  float* s_xh = reinterpret_cast<float*>(s_mem + (int64_t)B * C * 128);  // [B][C][32]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 31;
+  const int64_t hw = (int64_t)blockIdx.x * kHalfWaves + (tid >> 5);
+  const int64_t row_begin = hw * ng * R;
+  const int64_t n_items = ng * C;
+  const int last_lanes = (int)((K - (int64_t)(C - 1) * kChunk) >> 5);  // active lanes, chunk C-1
+  const uint32_t m = kNibbles, g = kMagic128;
+
+  // this lane's position in the rows of the group being loaded (set once per
+  // group); an item adds the chunk's offset to each
+  const uint4* pw[R];
+  const uint16_t* ps[R];
+  const uint16_t* pb[R];
+  int64_t prow = row_begin;
+  auto set_rows = [&]() {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = prow + r < N ? prow + r : N - 1;
+      pw[r] = reinterpret_cast<const uint4*>(wq + row * K8) + lane;
+      ps[r] = scales + row * G + (lane >> 1);
+      pb[r] = biases + row * G + (lane >> 1);
+    }
+  };
+  set_rows();
+  int pc = 0;  // chunk of the next item to load
+  // Loads the next item.  The stream below never asks for an item past the
+  // last one, except in the prologue when a half wave has fewer than P items;
+  // those loads read clamped, valid rows and are never consumed.
+  auto issue = [&](Item<R>& it) {
+    int vo = pc * 32, go = pc * 16;  // vector and group offsets of the chunk
+    if (RAGGED && pc == C - 1 && lane >= last_lanes) {  // past the end: lane 0's data
+      vo = -lane;
+      go = -(lane >> 1);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      it.w[r] = pw[r][vo];
+      it.s[r] = ps[r][go];
+      it.b[r] = pb[r][go];
+    }
+    if (++pc == C) {
+      pc = 0;
+      prow += R;
+      set_rows();
+    }
+  };
+  Item<R> ring[P];
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl) issue(ring[sl]);
+
+  // ---- stage x: pair each 8-element block, and sum each 32-element lane segment
+  for (int64_t seg = tid; seg < B * K32; seg += kThreads) {
+    const int bb = (int)(seg / K32);
+    const int64_t sg = seg % K32;
+    const int64_t c = sg >> 5, l = sg & 31;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)bb * K + sg * 32);
+    uint4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = src[i];
+    float h = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 p = pair_x(raw[i]);
+      s_xp[((int64_t)bb * C + c) * 128 + i * 32 + l] = p;
+      h = dot2(p.x, kOnes, h);
+      h = dot2(p.y, kOnes, h);
+      h = dot2(p.z, kOnes, h);
+      h = dot2(p.w, kOnes, h);
+    }
+    s_xh[((int64_t)bb * C + c) * 32 + l] = h;
+  }
+  __syncthreads();
+
+  // ---- stream
   float acc[R][B];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
+    for (int bb = 0; bb < B; ++bb) acc[r][bb] = 0.0f;
+  int64_t crow = row_begin;
+  int cc = 0;
+  const uint4* xlane = s_xp + lane;
+  const float* hlane = s_xh + lane;
+  auto consume = [&](const Item<R>& it, int64_t item) {
+    if (item < n_items) {
+      // a lane past the end of a short last chunk reads lane 0 of chunk 0
+      // (always staged, so finite) and scales it by exact zeros
+      bool active = true;
+      int xo = cc * 128, ho = cc * 32;
+      if (RAGGED && cc == C - 1 && lane >= last_lanes) {
+        active = false;
+        xo = -lane;
+        ho = -lane;
+      }
+      float sc[R], cb[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        sc[r] = bf16_to_f32(it.s[r]);
+        cb[r] = __builtin_fmaf(-128.0f, sc[r], bf16_to_f32(it.b[r]));
+        if (RAGGED && !active) sc[r] = cb[r] = 0.0f;
+      }
+#pragma unroll
+      for (int bb = 0; bb < B; ++bb) {
+        const uint4* xv = xlane + (int64_t)bb * C * 128 + xo;
+        const uint4 x0 = xv[0], x1 = xv[32], x2 = xv[64], x3 = xv[96];
+        const float xh = hlane[(int64_t)bb * C * 32 + ho];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float d = 0.0f;
+          d = dot_word(it.w[r].x, x0, d, m, g);
+          d = dot_word(it.w[r].y, x1, d, m, g);
+          d = dot_word(it.w[r].z, x2, d, m, g);
+          d = dot_word(it.w[r].w, x3, d, m, g);
+          acc[r][bb] = __builtin_fmaf(sc[r], d, acc[r][bb]);
+          acc[r][bb] = __builtin_fmaf(cb[r], xh, acc[r][bb]);
+        }
+      }
+      if (++cc == C) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+          for (int bb = 0; bb < B; ++bb) {
+            const float v = half_wave_sum(acc[r][bb]);
+            if (lane == 0 && crow + r < N) y[(int64_t)bb * N + crow + r] = v;
+            acc[r][bb] = 0.0f;
+          }
+        }
+        cc = 0;
+        crow += R;
+      }
+    }
+  };
+  // steady state: every issued item exists; the loads stay unconditional so
+  // each wait counts exactly the loads of the items still in flight
+  int64_t it = 0;
+  for (; it + 2 * P - 1 < n_items; it += P) {
+#pragma unroll
+    for (int sl = 0; sl < P; ++sl) {
+      consume(ring[sl], it + sl);
+      issue(ring[sl]);
+    }
+  }
+  // the last items (fewer than 2P)
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl) {
+    consume(ring[sl], it + sl);
+    if (it + sl + P < n_items) issue(ring[sl]);
+  }
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl) consume(ring[sl], it + P + sl);
+}
 
+// Register-staged variant of the same arithmetic, for shapes whose paired
+// activations do not fit in LDS (B * 2.125 * K bytes above the limit): each
+// 64-lane workgroup owns 2R rows, a half wave R of them, and reads the x pairs
+// of a chunk straight into registers.  Every floating-point step, and its
+// order, is the one described at the top of this file, so both variants give
+// the same bits.
+template <int B, int R>
+__global__ __launch_bounds__(64) void gemv_valu_regs_kernel(const uint32_t* __restrict__ wq,
+                                                            const uint16_t* __restrict__ scales,
+                                                            const uint16_t* __restrict__ biases,
+                                                            const uint16_t* __restrict__ x,
+                                                            float* __restrict__ y, int64_t N,
+                                                            int64_t K) {
+  const int lane = threadIdx.x & 31;
+  const int64_t row0 = ((int64_t)blockIdx.x * 2 + (threadIdx.x >> 5)) * R;
+  const int64_t G = K >> 6;
+  const int64_t K8 = K >> 3;
+  const uint32_t m = kNibbles, g = kMagic128;
+  float acc[R][B];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) acc[r][bb] = 0.0f;
   int64_t rows[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rows[r] = (row0 + r < N) ? row0 + r : N - 1;
@@ -84,69 +313,79 @@ __global__ __launch_bounds__(64) void gemv_valu_kernel(const uint32_t* __restric
         sv[r] = scales[rows[r] * G + (kb >> 6)];
         bv[r] = biases[rows[r] * G + (kb >> 6)];
       }
-      uint32_t xp[B][16];
-      float xh[B];
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const uint4* xs = reinterpret_cast<const uint4*>(x + (int64_t)b * K + kb);
-        uint4 v0 = xs[0], v1 = xs[1], v2 = xs[2], v3 = xs[3];
-        pair_x(v0.x, v0.y, v0.z, v0.w, &xp[b][0]);
-        pair_x(v1.x, v1.y, v1.z, v1.w, &xp[b][4]);
-        pair_x(v2.x, v2.y, v2.z, v2.w, &xp[b][8]);
-        pair_x(v3.x, v3.y, v3.z, v3.w, &xp[b][12]);
-        float h = 0.0f;
+      for (int bb = 0; bb < B; ++bb) {
+        const uint4* xs = reinterpret_cast<const uint4*>(x + (int64_t)bb * K + kb);
+        uint4 xp[4];
+        float xh = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) h = dot2(xp[b][j], kOnes, h);
-        xh[b] = h;
-      }
+        for (int i = 0; i < 4; ++i) {
+          xp[i] = pair_x(xs[i]);
+          xh = dot2(xp[i].x, kOnes, xh);
+          xh = dot2(xp[i].y, kOnes, xh);
+          xh = dot2(xp[i].z, kOnes, xh);
+          xh = dot2(xp[i].w, kOnes, xh);
+        }
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        uint32_t qp[16];
-        pair_q(wv[r].x, &qp[0]);
-        pair_q(wv[r].y, &qp[4]);
-        pair_q(wv[r].z, &qp[8]);
-        pair_q(wv[r].w, &qp[12]);
-        const float s = bf16_to_f32(sv[r]);
-        const float cb = __builtin_fmaf(-128.0f, s, bf16_to_f32(bv[r]));
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
+        for (int r = 0; r < R; ++r) {
+          const float sc = bf16_to_f32(sv[r]);
+          const float cb = __builtin_fmaf(-128.0f, sc, bf16_to_f32(bv[r]));
           float d = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) d = dot2(qp[j], xp[b][j], d);
-          acc[r][b] = __builtin_fmaf(s, d, acc[r][b]);
-          acc[r][b] = __builtin_fmaf(cb, xh[b], acc[r][b]);
+          d = dot_word(wv[r].x, xp[0], d, m, g);
+          d = dot_word(wv[r].y, xp[1], d, m, g);
+          d = dot_word(wv[r].z, xp[2], d, m, g);
+          d = dot_word(wv[r].w, xp[3], d, m, g);
+          acc[r][bb] = __builtin_fmaf(sc, d, acc[r][bb]);
+          acc[r][bb] = __builtin_fmaf(cb, xh, acc[r][bb]);
         }
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      float v = acc[r][b];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 1);
-      acc[r][b] = v;
-    }
-  }
+    for (int bb = 0; bb < B; ++bb) acc[r][bb] = half_wave_sum(acc[r][bb]);
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (row0 + r < N)
 #pragma unroll
-        for (int b = 0; b < B; ++b) y[(int64_t)b * N + row0 + r] = acc[r][b];
+        for (int bb = 0; bb < B; ++bb) y[(int64_t)bb * N + row0 + r] = acc[r][bb];
   }
 }
 
-template <int B, int R>
-hipError_t launch_b(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                    const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream) {
-  const int64_t rows_per_block = 2 * R;
+size_t lds_bytes(int B, int64_t K) {
+  const int64_t C = (K + kChunk - 1) / kChunk;
+  return (size_t)B * (size_t)C * (128 * 16 + 32 * 4);
+}
+
+template <int B, int R, int P>
+hipError_t launch_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                      const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream) {
+  const bool ragged = (K % kChunk) != 0;
+  // one group of R rows per half wave: many short workgroups, which the
+  // dispatcher spreads over the CUs as they free up (measured faster than
+  // fewer, longer-lived ones, whose slowest CU sets the end)
+  int64_t ng = 1;
+#ifdef W4G_TUNING
+  if (getenv("W4G_NG")) ng = atoll(getenv("W4G_NG"));
+#endif
+  const int64_t rows_per_block = (int64_t)kHalfWaves * R * ng;
   const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((gemv_valu_kernel<B, R>), dim3((unsigned)blocks), dim3(64), 0, stream, wq,
+  if (ragged)
+    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, true>), dim3((unsigned)blocks), dim3(kThreads),
+                       lds_bytes(B, K), stream, wq, scales, biases, x, y, N, K, ng);
+  else
+    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, false>), dim3((unsigned)blocks), dim3(kThreads),
+                       lds_bytes(B, K), stream, wq, scales, biases, x, y, N, K, ng);
+  return hipGetLastError();
+}
+
+template <int B, int R>
+hipError_t launch_regs(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                       const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t blocks = (N + 2 * R - 1) / (2 * R);
+  hipLaunchKernelGGL((gemv_valu_regs_kernel<B, R>), dim3((unsigned)blocks), dim3(64), 0, stream, wq,
                      scales, biases, x, y, N, K);
   return hipGetLastError();
 }
@@ -154,17 +393,48 @@ hipError_t launch_b(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
 }  // namespace
 
 hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                       const uint16_t* x, float* y, int B, int64_t N, int64_t K,
+                       const uint16_t* x, float* y, int B, int64_t N, int64_t K, bool force_regs,
                        hipStream_t stream) {
+  if (force_regs || lds_bytes(B, K) > kMaxLds) {
+    switch (B) {
+      case 1: return launch_regs<1, 4>(wq, scales, biases, x, y, N, K, stream);
+      case 2: return launch_regs<2, 4>(wq, scales, biases, x, y, N, K, stream);
+      case 3: return launch_regs<3, 2>(wq, scales, biases, x, y, N, K, stream);
+      case 4: return launch_regs<4, 2>(wq, scales, biases, x, y, N, K, stream);
+      case 5: return launch_regs<5, 2>(wq, scales, biases, x, y, N, K, stream);
+      case 6: return launch_regs<6, 2>(wq, scales, biases, x, y, N, K, stream);
+      case 7: return launch_regs<7, 2>(wq, scales, biases, x, y, N, K, stream);
+      case 8: return launch_regs<8, 2>(wq, scales, biases, x, y, N, K, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+#ifdef W4G_TUNING
+  if (B == 1 && getenv("W4G_RP")) {
+    const int rp = atoi(getenv("W4G_RP"));
+    switch (rp) {
+      case 12: return launch_lds<1, 1, 2>(wq, scales, biases, x, y, N, K, stream);
+      case 14: return launch_lds<1, 1, 4>(wq, scales, biases, x, y, N, K, stream);
+      case 16: return launch_lds<1, 1, 6>(wq, scales, biases, x, y, N, K, stream);
+      case 22: return launch_lds<1, 2, 2>(wq, scales, biases, x, y, N, K, stream);
+      case 23: return launch_lds<1, 2, 3>(wq, scales, biases, x, y, N, K, stream);
+      case 42: return launch_lds<1, 4, 2>(wq, scales, biases, x, y, N, K, stream);
+      case 43: return launch_lds<1, 4, 3>(wq, scales, biases, x, y, N, K, stream);
+      default: break;
+    }
+  }
+#endif
+  // few rows: one row per item and a deeper ring, so every CU has work
+  const bool few_rows = N < (int64_t)kHalfWaves * 2 * 1024;
   switch (B) {
-    case 1: return launch_b<1, 4>(wq, scales, biases, x, y, N, K, stream);
-    case 2: return launch_b<2, 4>(wq, scales, biases, x, y, N, K, stream);
-    case 3: return launch_b<3, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 4: return launch_b<4, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 5: return launch_b<5, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 6: return launch_b<6, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 7: return launch_b<7, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 8: return launch_b<8, 2>(wq, scales, biases, x, y, N, K, stream);
+    case 1: return few_rows ? launch_lds<1, 1, 4>(wq, scales, biases, x, y, N, K, stream)
+                            : launch_lds<1, 2, 2>(wq, scales, biases, x, y, N, K, stream);
+    case 2: return launch_lds<2, 4, 2>(wq, scales, biases, x, y, N, K, stream);
+    case 3: return launch_lds<3, 2, 2>(wq, scales, biases, x, y, N, K, stream);
+    case 4: return launch_lds<4, 2, 2>(wq, scales, biases, x, y, N, K, stream);
+    case 5: return launch_lds<5, 2, 2>(wq, scales, biases, x, y, N, K, stream);
+    case 6: return launch_lds<6, 2, 2>(wq, scales, biases, x, y, N, K, stream);
+    case 7: return launch_lds<7, 2, 2>(wq, scales, biases, x, y, N, K, stream);
+    case 8: return launch_lds<8, 2, 2>(wq, scales, biases, x, y, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,225 @@
+// Decode product on the matrix cores for 1 <= B <= 8 activation rows.
+//
+// Same format and result as the vector-ALU decode kernel (4-bit affine,
+// group 64: TensorFold PR #1437, Receipt; fp32 result: same PR, commit "Add
+// the pair seam and register its kernels with the kernel contract"), for
+// batches where the vector ALUs cannot keep up with HBM: a 32 x 32 x 16 bf16
+// matrix-core instruction multiplies 16 K-elements of 32 weight rows by up to
+// 32 activation rows, so every code is expanded once whatever B is.
+//
+// Operands: A = the activations (rows b < B, the rest zero), B = the codes of
+// 32 weight rows, expanded to the exact bf16 values 128 + q.  Lane (h, n) of
+// the wave loads 16 bytes of row n: half h of one 64-group, which feeds the
+// four instructions of that group (one 32-bit code word each).  The
+// activations are staged in LDS per 1024-element chunk, permuted once into
+// the order the expansion produces.
+//
+// Arithmetic per (row n, batch row b): for each group g the matrix core forms
+// P = sum_{k in g} x*(128 + q) from zero; the lane then adds s*P and
+// (b_g - 128 s) * X_g, X_g the fp32 sum of the group's activations, in fp32.
+// X_g is the sum of the group's two 32-element halves, each summed over its
+// natural bf16 pairs in ascending order.  Wave w of the workgroup takes the
+// groups g = w (mod W) in ascending order; the W wave sums are added in
+// ascending wave order at the end.  The order
+// depends on K alone (TensorFold PR #1433, step-2 description), and every
+// batch row is computed independently of the others.
+#include "w4g_internal.h"
+
+namespace w4g {
+namespace {
+
+constexpr int kStageGroups = 16;  // groups per staged activation chunk (1024 elements)
+constexpr int kXRows = 10;        // LDS rows per activation block
+constexpr uint32_t kMagic128 = 0x43004300u;
+constexpr uint32_t kOnes = 0x3F803F80u;
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint4 permute_block(uint4 v) {
+  uint4 p;
+  p.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+  p.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+  p.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+  p.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+  return p;
+}
+
+// (a & m) | g in one instruction (the compiler would emit two with literals)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t g) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(g));
+  return d;
+}
+
+// 8 codes -> bf16 values 128 + q in the order q0,q4,q1,q5,q2,q6,q3,q7
+__device__ __forceinline__ bf16x8_t expand128(uint32_t w, uint32_t m, uint32_t g) {
+  uint4 p;
+  p.x = and_or(w, m, g);
+  p.y = and_or(w >> 4, m, g);
+  p.z = and_or(w >> 8, m, g);
+  p.w = and_or(w >> 12, m, g);
+  return __builtin_bit_cast(bf16x8_t, p);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int t) {
+  return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
+}
+
+// Codes, scales and biases of one stage of one wave: GPS groups.
+template <int GPS>
+struct Ring {
+  uint4 c[GPS];
+  uint32_t s[GPS], b[GPS];
+};
+
+// The workgroup's four waves split the K groups round robin; each stage of 16
+// groups gives every wave GPS = 16 / W of them.  The activations of a stage are
+// staged in one of two LDS buffers while the other feeds the matrix cores.
+template <int W>
+__global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __restrict__ wq,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint16_t* __restrict__ biases,
+                                                           const uint16_t* __restrict__ x,
+                                                           float* __restrict__ y, int B, int64_t N,
+                                                           int64_t K) {
+  constexpr int GPS = kStageGroups / W;
+  // [buf][8-element block][row]: rows 0..7 the batch rows (permuted), row 8
+  // zeros, row 9 padding so the two half-group reads of a wave fall in
+  // different LDS banks
+  __shared__ uint4 s_x[2][kStageGroups * 8][kXRows];
+  __shared__ float s_X[2][8][kStageGroups];      // [buf][b][group]: group sums
+  __shared__ float s_red[W][4][64];              // wave sums
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int arow = l32 < 8 ? l32 : 8;  // activation row this lane feeds; rows >= B are zero
+  const uint32_t m = 0x000F000Fu, g = kMagic128;
+  const int64_t n0 = (int64_t)blockIdx.x * 32;
+  const int64_t n = (n0 + l32 < N) ? n0 + l32 : N - 1;
+  const int64_t G = K >> 6;
+  const int nstage = (int)((G + kStageGroups - 1) / kStageGroups);
+  const uint32_t* wrow = wq + n * (K >> 3);
+  const uint16_t* srow = scales + n * G;
+  const uint16_t* brow = biases + n * G;
+
+  // codes of stage st for this wave (groups past the end reread the row's last
+  // group, a cache hit, so no other rows are pulled in)
+  auto issue = [&](Ring<GPS>& r, int st) {
+#pragma unroll
+    for (int j = 0; j < GPS; ++j) {
+      int64_t g = (int64_t)st * kStageGroups + wave + W * j;
+      g = g < G ? g : G - 1;
+      r.c[j] = *reinterpret_cast<const uint4*>(wrow + g * 8 + h * 4);
+      r.s[j] = srow[g];
+      r.b[j] = brow[g];
+    }
+  };
+
+  // activation staging: thread -> (row xb, group xg, half xh) of a stage, 32 elements
+  const int xb = tid >> 5, xg = (tid & 31) >> 1, xhalf = tid & 1;
+  const bool xload = (64 * W >= 256) && xb < B;
+  uint4 xr[4];
+  auto load_x = [&](int st) {
+    const int64_t g = (int64_t)st * kStageGroups + xg;
+    const bool ok = xload && st < nstage && g < G;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (ok ? (int64_t)xb * K + g * 64 + xhalf * 32 : 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[i] = ok ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto store_x = [&](int buf) {
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s_x[buf][xg * 8 + xhalf * 4 + i][xb] = permute_block(xr[i]);
+      part = dot2(xr[i].x, kOnes, part);
+      part = dot2(xr[i].y, kOnes, part);
+      part = dot2(xr[i].z, kOnes, part);
+      part = dot2(xr[i].w, kOnes, part);
+    }
+    const float other = __shfl_xor(part, 1);
+    if (xhalf == 0) s_X[buf][xb][xg] = part + other;  // first half + second half
+  };
+
+  float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const Ring<GPS>& r, int st, int buf) {
+#pragma unroll
+    for (int j = 0; j < GPS; ++j) {
+      const int gl = wave + W * j;  // group within the stage
+      if ((int64_t)st * kStageGroups + gl < G) {
+        f32x16_t p;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) p[v] = 0.0f;
+        uint4 av[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) av[t] = s_x[buf][gl * 8 + h * 4 + t][arow];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[t]),
+                                                      expand128(word(r.c[j], t), m, g), p, 0, 0, 0);
+        const float sc = bf16_to_f32(r.s[j]);
+        const float cb = __builtin_fmaf(-128.0f, sc, bf16_to_f32(r.b[j]));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          tot[v] = __builtin_fmaf(sc, p[v], tot[v]);
+          tot[v] = __builtin_fmaf(cb, s_X[buf][4 * h + v][gl], tot[v]);
+        }
+      }
+    }
+  };
+
+  // the zero row that lanes 8..31 read as their activation operand
+  for (int i = tid; i < 2 * kStageGroups * 8; i += 64 * W)
+    s_x[i / (kStageGroups * 8)][i % (kStageGroups * 8)][8] = make_uint4(0u, 0u, 0u, 0u);
+
+  Ring<GPS> ra, rb;
+  issue(ra, 0);
+  issue(rb, 1);
+  load_x(0);
+  store_x(0);
+  load_x(1);
+  __syncthreads();
+  for (int st = 0; st < nstage; st += 2) {
+    compute(ra, st, 0);
+    issue(ra, st + 2);
+    store_x(1);  // stage st + 1 (zeros past the end)
+    load_x(st + 2);
+    __syncthreads();
+    compute(rb, st + 1, 1);  // no-op past the last stage
+    issue(rb, st + 3);
+    store_x(0);  // stage st + 2
+    load_x(st + 3);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int v = 0; v < 4; ++v) s_red[wave][v][lane] = tot[v];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float acc = s_red[0][v][lane];
+#pragma unroll
+      for (int w = 1; w < W; ++w) acc += s_red[w][v][lane];
+      const int b = 4 * h + v;
+      if (b < B && n0 + l32 < N) y[(int64_t)b * N + n0 + l32] = acc;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                            const uint16_t* x, float* y, int B, int64_t N, int64_t K,
+                            hipStream_t stream) {
+  const int64_t blocks = (N + 31) / 32;
+  hipLaunchKernelGGL(gemv_mfma_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, wq, scales,
+                     biases, x, y, B, N, K);
+  return hipGetLastError();
+}
+
+}  // namespace w4g
