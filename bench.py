@@ -52,7 +52,57 @@ def parse():
     p.add_argument("--skip-extras", action="store_true",
                    help="only the headline sweep (used for profiler runs)")
     p.add_argument("--skip-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--probe", choices=["gate_up", "copy"],
+                   help="run only one kernel a few times (for hardware-counter runs) and exit")
     return p.parse_args()
+
+
+PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                       "gemv_gate_up_b1_hbm_counters.txt")
+GEMV_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "w4_gemv_greedy_amd", "csrc",
+                        "gemv.hip")
+
+
+def counted_traffic():
+    """HBM bytes per gate-up launch from the committed counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line and not line.startswith(" "))
+    want = fields.get("source_sha256", "").strip()
+    have = hashlib.sha256(open(GEMV_SRC, "rb").read()).hexdigest()
+    if not want or want != have:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
+
+
+def probe(kind):
+    """A short, fixed workload for hardware-counter collection."""
+    import torch
+    import w4_gemv_greedy_amd as w4g
+    from w4_gemv_greedy_amd import synth
+    dev = torch.device("cuda:0")
+    if kind == "copy":
+        # plain device copy of 1 GiB: reads 1 GiB and writes 1 GiB
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        return
+    mats = [Mat(2 * INTER, HIDDEN, 5, synth.GATE_UP, l, dev) for l in range(4)]
+    x = make_x(1, HIDDEN, 5, synth.GATE_UP, 0, dev)
+    y = torch.empty((1, 2 * INTER), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        for m in mats:
+            w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y)
+    torch.cuda.synchronize()
 
 
 class Mat:
@@ -122,6 +172,9 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.probe:
+        probe(args.probe)
+        return
     import torch
     import w4_gemv_greedy_amd as w4g
     from w4_gemv_greedy_amd import synth
@@ -159,7 +212,7 @@ def main():
                 torch.empty(Bn, dtype=torch.int32, device=dev),
                 torch.empty(w4g.workspace_bytes(w4g.OP_ARGMAX, Bn, VOCAB, 0), dtype=torch.uint8, device=dev))
 
-    def make_step(Bn, events=None):
+    def make_step(Bn):
         xs, xh = inputs(Bn)
         yo, yg, yd, logits, ids, ws = outputs(Bn)
 
@@ -168,11 +221,7 @@ def main():
                 o, g, d = layers[l]
                 xo, xg, xd = xs[l]
                 w4g.qmm_gemv(o.wq, o.sc, o.bi, xo, yo)
-                if events is not None:
-                    events[l][0].record()
                 w4g.qmm_gemv(g.wq, g.sc, g.bi, xg, yg)
-                if events is not None:
-                    events[l][1].record()
                 w4g.qmm_gemv(d.wq, d.sc, d.bi, xd, yd)
             w4g.qmm_gemv(head.wq, head.sc, head.bi, xh, logits)
             w4g.vocab_argmax(logits, ids, ws)
@@ -212,19 +261,23 @@ def main():
     value = nbytes / (ms * 1e-3) / 1e9
     log(f"sweep B={B}: {ms * 1e3:.1f} us/step, {value:.0f} GB/s ({graph=}), wall {wall:.2f} s")
 
-    # dominant kernel: the gate-up product, timed launch by launch with events on its stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(LAYERS)]
-    istep, _, _ = make_step(B, events=ev)
-    durs = []
-    for _ in range(max(3, args.steps // 4)):
-        istep()
-        torch.cuda.synchronize()
-        durs += [a.elapsed_time(b) for a, b in ev]
-    gu_us = float(np.mean(durs)) * 1e3
+    # dominant kernel: the gate-up product.  Its 16 launches of a step (one per
+    # layer's weights, so nothing is served from cache) run back to back in a
+    # graph on the same stream; HIP events around the replays give the average
+    # launch duration.
+    xg_in = [make_x(B, HIDDEN, 5, synth.GATE_UP, l, dev) for l in range(LAYERS)]
+    yg_out = torch.empty((B, 2 * INTER), dtype=torch.float32, device=dev)
+
+    def gate_up_only():
+        for l in range(LAYERS):
+            g = layers[l][1]
+            w4g.qmm_gemv(g.wq, g.sc, g.bi, xg_in[l], yg_out)
+    ms_g, _ = timed(gate_up_only, max(5, args.steps), 2, True)
+    gu_us = ms_g * 1e3 / LAYERS
     gu_bytes = gemv_bytes(2 * INTER, HIDDEN, B)
     gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic() if B == 1 else None,
                 "kernel": "gemv_valu_kernel (gate_up 5120 -> 34816)", "avg_launch_us": round(gu_us, 2),
                 "bytes_per_launch": gu_bytes}
     log(f"gate_up launch avg {gu_us:.2f} us -> {gu_gbs:.0f} GB/s")

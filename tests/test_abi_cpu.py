@@ -1,0 +1,147 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, agrees with the binding's constants, and rejects bad arguments with
+the documented status before any HIP call (no GPU is touched here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from w4_gemv_greedy_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4g.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from w4_gemv_greedy_amd import build
+        build.build(quiet=True)
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert set(names) >= {"qmm_gemv", "qmm_gemv_ex", "qmm_gemm", "vocab_argmax",
+                          "qmm_workspace_bytes", "w4g_status_string", "w4g_abi_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in names:
+        getattr(lib, n)
+
+
+def test_constants_match_header(lib):
+    defs = dict(re.findall(r"#define\s+(W4G_\w+)\s+(\S+)", open(HEADER).read()))
+    val = lambda k: int(defs[k].rstrip("u"), 0)
+    assert val("W4G_ABI_VERSION") == _lib.ABI_VERSION == lib.w4g_abi_version()
+    assert val("W4G_SENTINEL") == _lib.SENTINEL
+    assert val("W4G_MAX_GEMV_BATCH") == _lib.MAX_GEMV_BATCH
+    for k, v in (("W4G_OK", _lib.OK), ("W4G_EINVAL_PTR", _lib.EINVAL_PTR), ("W4G_ESHAPE", _lib.ESHAPE),
+                 ("W4G_EALIGN", _lib.EALIGN), ("W4G_EWORKSPACE", _lib.EWORKSPACE),
+                 ("W4G_EDTYPE", _lib.EDTYPE), ("W4G_ELAUNCH", _lib.ELAUNCH), ("W4G_EALIAS", _lib.EALIAS),
+                 ("W4G_F32", _lib.F32), ("W4G_BF16", _lib.BF16), ("W4G_OP_GEMV", _lib.OP_GEMV),
+                 ("W4G_OP_GEMM", _lib.OP_GEMM), ("W4G_OP_ARGMAX", _lib.OP_ARGMAX),
+                 ("W4G_GEMV_AUTO", _lib.GEMV_AUTO), ("W4G_GEMV_VALU", _lib.GEMV_VALU),
+                 ("W4G_GEMV_MFMA", _lib.GEMV_MFMA), ("W4G_GEMV_VALU_REGS", _lib.GEMV_VALU_REGS)):
+        assert val(k) == v, k
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        msg = lib.w4g_status_string(s)
+        assert msg and msg != b"unknown status"
+    assert lib.w4g_status_string(99) == b"unknown status"
+
+
+# fake but aligned, distinct device addresses: validation never dereferences them
+A = 1 << 40
+WQ, SC, BI, X, Y, WS, LOG, IDS = (A + i * (1 << 36) for i in range(8))
+
+
+def gemv(lib, wq=WQ, sc=SC, bi=BI, x=X, y=Y, B=1, N=64, K=128, ws=None, wsb=0, kernel=None):
+    if kernel is None:
+        return lib.qmm_gemv(wq, sc, bi, x, y, B, N, K, ws, wsb, None)
+    return lib.qmm_gemv_ex(wq, sc, bi, x, y, B, N, K, ws, wsb, None, kernel)
+
+
+def test_gemv_rejects(lib):
+    assert gemv(lib, wq=None) == _lib.EINVAL_PTR
+    assert gemv(lib, y=None) == _lib.EINVAL_PTR
+    assert gemv(lib, B=0) == _lib.ESHAPE
+    assert gemv(lib, B=9) == _lib.ESHAPE
+    assert gemv(lib, N=0) == _lib.ESHAPE
+    assert gemv(lib, K=96) == _lib.ESHAPE
+    assert gemv(lib, K=0) == _lib.ESHAPE
+    assert gemv(lib, K=1 << 31) == _lib.ESHAPE
+    assert gemv(lib, wq=WQ + 4) == _lib.EALIGN
+    assert gemv(lib, x=X + 8) == _lib.EALIGN
+    assert gemv(lib, y=Y + 4) == _lib.EALIGN
+    assert gemv(lib, sc=SC + 1) == _lib.EALIGN
+    # y overlapping x, the codes, or the scales
+    assert gemv(lib, y=X) == _lib.EALIAS
+    assert gemv(lib, y=WQ + 64) == _lib.EALIAS
+    assert gemv(lib, y=SC) == _lib.EALIAS
+    assert gemv(lib, kernel=7) == _lib.EDTYPE
+    assert gemv(lib, kernel=-1) == _lib.EDTYPE
+
+
+def test_gemm_rejects(lib):
+    need = lib.qmm_workspace_bytes(_lib.OP_GEMM, 16, 64, 128)
+    assert 0 < need < (1 << 20)
+    call = lambda **k: lib.qmm_gemm(k.get("wq", WQ), SC, BI, X, k.get("y", Y), k.get("M", 16), 64,
+                                    k.get("K", 128), k.get("ws", WS), k.get("wsb", need), None)
+    assert call(wq=None) == _lib.EINVAL_PTR
+    assert call(M=0) == _lib.ESHAPE
+    assert call(K=100) == _lib.ESHAPE
+    assert call(ws=None) == _lib.EWORKSPACE
+    assert call(wsb=need - 1) == _lib.EWORKSPACE
+    assert call(ws=X) == _lib.EALIAS
+    assert call(y=WS) == _lib.EALIAS
+
+
+def test_argmax_rejects(lib):
+    need = lib.qmm_workspace_bytes(_lib.OP_ARGMAX, 2, 5000, 0)
+    assert need == 2 * 5 * 8
+    call = lambda **k: lib.vocab_argmax(k.get("lg", LOG), k.get("dt", _lib.F32), k.get("rows", 2),
+                                        k.get("V", 5000), k.get("ld", 5000), k.get("ids", IDS),
+                                        k.get("ws", WS), k.get("wsb", need), None)
+    assert call(lg=None) == _lib.EINVAL_PTR
+    assert call(ids=None) == _lib.EINVAL_PTR
+    assert call(dt=2) == _lib.EDTYPE
+    assert call(rows=0) == _lib.ESHAPE
+    assert call(rows=65536) == _lib.ESHAPE
+    assert call(V=0) == _lib.ESHAPE
+    assert call(V=1 << 31, ld=1 << 31) == _lib.ESHAPE
+    assert call(ld=4999) == _lib.ESHAPE
+    assert call(lg=LOG + 4) == _lib.EALIGN
+    assert call(ids=IDS + 2) == _lib.EALIGN
+    assert call(ws=None) == _lib.EWORKSPACE
+    assert call(wsb=need - 8) == _lib.EWORKSPACE
+    assert call(ids=LOG + 64) == _lib.EALIAS
+    assert call(ws=LOG) == _lib.EALIAS
+
+
+def test_workspace_sizes(lib):
+    size_max = ctypes.c_size_t(-1).value
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV, 8, 5120, 5120) == 0
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV, 9, 5120, 5120) == size_max
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMM, 512, 5120, 5120) == 512 * 3 * 80 * 2
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMM, 512, 5120, 17408) == 512 * 3 * 272 * 2
+    assert lib.qmm_workspace_bytes(_lib.OP_ARGMAX, 1, 248320, 0) == 243 * 8
+    assert lib.qmm_workspace_bytes(7, 1, 1, 64) == size_max
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load(str(tmp_path / "libw4g.so"))

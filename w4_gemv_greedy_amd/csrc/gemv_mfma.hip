@@ -87,9 +87,10 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
                                                            float* __restrict__ y, int B, int64_t N,
                                                            int64_t K) {
   constexpr int GPS = kStageGroups / W;
-  // [buf][8-element block][row]: rows 0..7 the batch rows (permuted), row 8
-  // zeros, row 9 padding so the two half-group reads of a wave fall in
-  // different LDS banks
+  // [buf][8-element block][slot]: slots 0..7 hold the batch rows (row r of
+  // block k at slot r ^ ((k >> 3) & 7), so the staging writes of different
+  // groups land in different banks), slot 8 zeros, slot 9 padding so the two
+  // half-group reads of a wave fall in different banks
   __shared__ uint4 s_x[2][kStageGroups * 8][kXRows];
   __shared__ float s_X[2][8][kStageGroups];      // [buf][b][group]: group sums
   __shared__ float s_red[W][4][64];              // wave sums
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
     float part = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s_x[buf][xg * 8 + xhalf * 4 + i][xb] = permute_block(xr[i]);
+      s_x[buf][xg * 8 + xhalf * 4 + i][xb ^ (xg & 7)] = permute_block(xr[i]);
       part = dot2(xr[i].x, kOnes, part);
       part = dot2(xr[i].y, kOnes, part);
       part = dot2(xr[i].z, kOnes, part);
@@ -146,53 +147,71 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
   };
 
   float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // The stage's GPS groups run their four-instruction matrix-core chains side
+  // by side (instruction t of every group, then t + 1), so the chains overlap;
+  // each group's partial is still its own, and the groups are added to the
+  // running sums in ascending order.
   auto compute = [&](const Ring<GPS>& r, int st, int buf) {
+    f32x16_t p[GPS];
+    bf16x8_t bop[GPS][4];
+    uint4 av[GPS][4];
 #pragma unroll
     for (int j = 0; j < GPS; ++j) {
-      const int gl = wave + W * j;  // group within the stage
+      const int gl = wave + W * j;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        av[j][t] = s_x[buf][gl * 8 + h * 4 + t][arow < 8 ? arow ^ (gl & 7) : 8];
+        bop[j][t] = expand128(word(r.c[j], t), m, g);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[j][v] = 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < GPS; ++j)
+        p[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[j][t]),
+                                                       bop[j][t], p[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < GPS; ++j) {
+      const int gl = wave + W * j;
       if ((int64_t)st * kStageGroups + gl < G) {
-        f32x16_t p;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) p[v] = 0.0f;
-        uint4 av[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) av[t] = s_x[buf][gl * 8 + h * 4 + t][arow];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[t]),
-                                                      expand128(word(r.c[j], t), m, g), p, 0, 0, 0);
         const float sc = bf16_to_f32(r.s[j]);
         const float cb = __builtin_fmaf(-128.0f, sc, bf16_to_f32(r.b[j]));
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          tot[v] = __builtin_fmaf(sc, p[v], tot[v]);
+          tot[v] = __builtin_fmaf(sc, p[j][v], tot[v]);
           tot[v] = __builtin_fmaf(cb, s_X[buf][4 * h + v][gl], tot[v]);
         }
       }
     }
   };
 
-  // the zero row that lanes 8..31 read as their activation operand
+  // the zero slot that lanes 8..31 read as their activation operand
   for (int i = tid; i < 2 * kStageGroups * 8; i += 64 * W)
     s_x[i / (kStageGroups * 8)][i % (kStageGroups * 8)][8] = make_uint4(0u, 0u, 0u, 0u);
 
+  // Per half step: activations of stage st + 2 load first, then its codes, so
+  // the wait for stage st + 1's activations (issued a half step earlier) does
+  // not also wait for codes that are only needed later.
   Ring<GPS> ra, rb;
-  issue(ra, 0);
-  issue(rb, 1);
   load_x(0);
+  issue(ra, 0);
   store_x(0);
   load_x(1);
+  issue(rb, 1);
   __syncthreads();
   for (int st = 0; st < nstage; st += 2) {
+    // xr holds stage st + 1
     compute(ra, st, 0);
-    issue(ra, st + 2);
     store_x(1);  // stage st + 1 (zeros past the end)
     load_x(st + 2);
+    issue(ra, st + 2);
     __syncthreads();
     compute(rb, st + 1, 1);  // no-op past the last stage
-    issue(rb, st + 3);
     store_x(0);  // stage st + 2
     load_x(st + 3);
+    issue(rb, st + 3);
     __syncthreads();
   }
 
