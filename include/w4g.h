@@ -67,7 +67,8 @@ extern "C" {
 #define W4G_OK 0
 #define W4G_EINVAL_PTR 1  /* a required pointer is NULL */
 #define W4G_ESHAPE 2      /* a size is out of range (K % 64, B, N, M, vocab, ld) */
-#define W4G_EALIGN 3      /* wq, x, y or logits not 16-byte aligned */
+#define W4G_EALIGN 3      /* a buffer below its alignment (16 bytes: wq, x, y, logits, the
+                             product workspace; 8: the argmax workspace; 4: ids; 2: tables) */
 #define W4G_EWORKSPACE 4  /* workspace missing or smaller than qmm_workspace_bytes */
 #define W4G_EDTYPE 5      /* unknown logits dtype or op code */
 #define W4G_ELAUNCH 6     /* the HIP runtime refused a launch */
@@ -95,7 +96,10 @@ extern "C" {
  * s*D + (b - 128*s)*X, where D is the dot of x with (128 + q) taken over
  * bf16 pairs in ascending pair order and X the fp32 sum of those 32 x; each
  * lane adds its chunk terms in ascending chunk order, and the 32 lane sums
- * meet in a fixed xor butterfly (16, 8, 4, 2, 1).  That is the order of the
+ * meet in a fixed tree: lanes j and j ^ 16 are added (a permlane16 swap),
+ * then, within 16 lanes, lane j adds lane 15 - j (DPP row_mirror), within 8
+ * lanes lane 7 - j (row_half_mirror), then lane j ^ 2 and lane j ^ 1
+ * (quad_perm), leaving the sum in every lane.  That is the order of the
  * vector-ALU family; qmm_gemv may pick the matrix-core family instead (see
  * qmm_gemv_ex), by B and shape only, so a given (B, N, K) always runs the
  * same kernel and its bits never change from call to call.
@@ -131,13 +135,15 @@ int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* bias
 /*
  * Prompt product on the matrix cores, any M >= 1 rows.
  *   Same layout and constraints as qmm_gemv with M in place of B.
- *   workspace: at least qmm_workspace_bytes(W4G_OP_GEMM, M, N, K) bytes.
+ *   workspace: at least qmm_workspace_bytes(W4G_OP_GEMM, M, N, K) bytes,
+ *   16-byte aligned.
  * Each code enters the bf16 matrix cores as the exact value 2 + q/8; a
  * 64-group's partial P_g is scaled by 8s in fp32 and added to the running sum
  * in ascending group order; the remaining affine term sum_g (b - 16 s) X_g
- * (X_g the fp32 group sum of x, split exactly into three bf16 parts) is
- * accumulated on the matrix cores after the last group.  Row m of the result
- * does not depend on M or on the other rows.
+ * (X_g the fp32 group sum of x, split exactly into three bf16 parts X1..X3) is
+ * accumulated on the matrix cores after the last group, block of 16 groups by
+ * block in ascending order, each block as b X1, b X2, b X3, -16s X1, -16s X2,
+ * -16s X3.  Row m of the result does not depend on M or on the other rows.
  */
 int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
              const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
@@ -150,7 +156,8 @@ int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
  *   ld >= vocab, rows >= 1.  logits must be 16-byte aligned.
  *   ids [rows] uint32: the winning id, or W4G_SENTINEL for a row holding NaN
  *   or +-Inf.
- *   workspace: at least qmm_workspace_bytes(W4G_OP_ARGMAX, rows, vocab, 0).
+ *   workspace: at least qmm_workspace_bytes(W4G_OP_ARGMAX, rows, vocab, 0),
+ *   8-byte aligned.
  * Two passes: pass 1 reduces blocks of 1024 ids to (value, id | flag) records,
  * pass 2 combines a row's records; both keep the lowest id among equal
  * values and propagate the flag.

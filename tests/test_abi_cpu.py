@@ -106,6 +106,7 @@ def test_gemm_rejects(lib):
     assert call(K=100) == _lib.ESHAPE
     assert call(ws=None) == _lib.EWORKSPACE
     assert call(wsb=need - 1) == _lib.EWORKSPACE
+    assert call(ws=WS + 8) == _lib.EALIGN
     assert call(ws=X) == _lib.EALIAS
     assert call(y=WS) == _lib.EALIAS
 
@@ -126,6 +127,7 @@ def test_argmax_rejects(lib):
     assert call(ld=4999) == _lib.ESHAPE
     assert call(lg=LOG + 4) == _lib.EALIGN
     assert call(ids=IDS + 2) == _lib.EALIGN
+    assert call(ws=WS + 4) == _lib.EALIGN
     assert call(ws=None) == _lib.EWORKSPACE
     assert call(wsb=need - 8) == _lib.EWORKSPACE
     assert call(ids=LOG + 64) == _lib.EALIAS
@@ -136,8 +138,8 @@ def test_workspace_sizes(lib):
     size_max = ctypes.c_size_t(-1).value
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV, 8, 5120, 5120) == 0
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV, 9, 5120, 5120) == size_max
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMM, 512, 5120, 5120) == 512 * 3 * 80 * 2
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMM, 512, 5120, 17408) == 512 * 3 * 272 * 2
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMM, 512, 5120, 5120) == 512 * 5120 * 2 + 512 * 3 * 80 * 2
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMM, 512, 5120, 17408) == 512 * 17408 * 2 + 512 * 3 * 272 * 2
     assert lib.qmm_workspace_bytes(_lib.OP_ARGMAX, 1, 248320, 0) == 243 * 8
     assert lib.qmm_workspace_bytes(7, 1, 1, 64) == size_max
 

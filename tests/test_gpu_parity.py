@@ -112,6 +112,30 @@ def test_gemm_deterministic_and_row_independent():
     assert np.array_equal(ys.view(np.uint32), y[:5].view(np.uint32)), "prompt rows depend on M"
 
 
+def _offset_copy(t):
+    """The same bf16 table starting 2 bytes past a 4-byte boundary."""
+    import torch
+    flat = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    flat[1:] = t.reshape(-1)
+    return flat[1:].view(t.shape)
+
+
+@pytest.mark.parametrize("M,N,K", [(130, 256, 1024), (64, 200, 5120)])
+def test_gemm_kernels_agree_bitwise(M, N, K):
+    """Even G with 4-byte aligned scales takes the LDS-load kernel; a scale table
+    2 bytes off alignment takes the register-staged one.  Same order, same bits."""
+    wq, sc, bi, x = _case(N, K, M, 3 * M + N)
+    X = up_bf16(x)
+    W = up_u32(wq)
+    S, Bi = up_bf16(sc), up_bf16(bi)
+    y_lds = down(w4g.qmm_gemm(W, S, Bi, X))
+    S2, B2 = _offset_copy(S), _offset_copy(Bi)
+    assert S2.data_ptr() % 4 == 2
+    y_reg = down(w4g.qmm_gemm(W, S2, B2, X))
+    assert np.array_equal(y_lds.view(np.uint32), y_reg.view(np.uint32))
+    assert_close(y_lds, oracle.qmm(wq, sc, bi, x), f"gemm M={M} N={N} K={K}")
+
+
 def _argmax_gpu(logits_np, bf16=False):
     t = up_bf16(logits_np) if bf16 else up_f32(logits_np)
     return ids_down(w4g.vocab_argmax(t))

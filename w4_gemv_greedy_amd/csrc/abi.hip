@@ -30,6 +30,7 @@ int check_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases
   if (!aligned16(wq) || !aligned16(x) || !aligned16(y) || !aligned2(scales) || !aligned2(biases))
     return W4G_EALIGN;
   if (need > 0 && (!workspace || workspace_bytes < need)) return W4G_EWORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return W4G_EALIGN;
   const size_t ybytes = (size_t)rows * (size_t)N * sizeof(float);
   const size_t wbytes = (size_t)N * (size_t)(K / 8) * sizeof(uint32_t);
   const size_t gbytes = (size_t)N * (size_t)(K / 64) * sizeof(uint16_t);
@@ -58,7 +59,7 @@ const char* w4g_status_string(int status) {
     case W4G_OK: return "ok";
     case W4G_EINVAL_PTR: return "a required pointer is NULL";
     case W4G_ESHAPE: return "a size is out of range";
-    case W4G_EALIGN: return "a buffer is not aligned (16 bytes for codes, x, y, logits)";
+    case W4G_EALIGN: return "a buffer is below its required alignment";
     case W4G_EWORKSPACE: return "workspace missing or too small";
     case W4G_EDTYPE: return "unknown dtype or op";
     case W4G_ELAUNCH: return "the HIP runtime refused a launch";
@@ -132,6 +133,7 @@ int vocab_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int
   if (!aligned16(logits) || (reinterpret_cast<uintptr_t>(ids) & 3u)) return W4G_EALIGN;
   const size_t need = w4g::argmax_workspace_bytes(rows, vocab);
   if (!workspace || workspace_bytes < need) return W4G_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return W4G_EALIGN;
   const size_t esz = dtype == W4G_F32 ? 4 : 2;
   const size_t lbytes = ((size_t)(rows - 1) * (size_t)ld + (size_t)vocab) * esz;
   if (overlap(ids, (size_t)rows * 4, logits, lbytes) || overlap(ids, (size_t)rows * 4, workspace, need) ||
