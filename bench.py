@@ -227,7 +227,9 @@ def main():
             w4g.vocab_argmax(logits, ids, ws)
         return step, ids, logits
 
-    def timed(fn, steps, warmup, graph):
+    def timed(fn, steps, warmup, graph, reps=1):
+        # graph mode captures `reps` back-to-back calls per replay, so the replay's own
+        # launch cost is spread over them; the result is per call
         if graph:
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
@@ -237,7 +239,8 @@ def main():
             torch.cuda.current_stream().wait_stream(s)
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                fn()
+                for _ in range(reps):
+                    fn()
             run = g.replay
         else:
             run = fn
@@ -252,7 +255,7 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
-        return e0.elapsed_time(e1) / steps, wall
+        return e0.elapsed_time(e1) / steps / (reps if graph else 1), wall
 
     graph = not args.no_graph
     step, ids, logits = make_step(B)
@@ -314,13 +317,29 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args):
     def head_step():
         w4g.qmm_gemv(head.wq, head.sc, head.bi, xh, logits)
         w4g.vocab_argmax(logits, ids, ws)
-    ms, _ = timed(head_step, 20, 3, True)
+    ms, _ = timed(head_step, 10, 2, True, reps=4)
     ex["lm_head_argmax_us_per_token"] = round(ms * 1e3, 2)
     ex["lm_head_argmax_GBps"] = round((gemv_bytes(VOCAB, HIDDEN, 1) + 4 * VOCAB) / (ms * 1e-3) / 1e9, 1)
 
+    # the same with the argmax's first pass fused into the product (logits kept / not written)
+    ws_f = torch.empty(w4g.workspace_bytes(w4g.OP_GEMV_ARGMAX, 1, VOCAB, HIDDEN), dtype=torch.uint8,
+                       device=dev)
+
+    def head_fused():
+        w4g.qmm_gemv_argmax(head.wq, head.sc, head.bi, xh, logits, ids, ws_f)
+
+    def head_fused_ids_only():
+        w4g.qmm_gemv_argmax(head.wq, head.sc, head.bi, xh, None, ids, ws_f, want_logits=False)
+    ms, _ = timed(head_fused, 10, 2, True, reps=4)
+    ex["lm_head_argmax_fused_us_per_token"] = round(ms * 1e3, 2)
+    ms, _ = timed(head_fused_ids_only, 10, 2, True, reps=4)
+    ex["lm_head_argmax_fused_ids_only_us_per_token"] = round(ms * 1e3, 2)
+    log(f"lm_head+argmax fused {ex['lm_head_argmax_fused_us_per_token']} us/token, ids only "
+        f"{ex['lm_head_argmax_fused_ids_only_us_per_token']} us/token")
+
     def argmax_only():
         w4g.vocab_argmax(logits, ids, ws)
-    ms, _ = timed(argmax_only, 50, 5, True)
+    ms, _ = timed(argmax_only, 20, 3, True, reps=20)
     ex["argmax_us"] = round(ms * 1e3, 2)
     log(f"lm_head+argmax {ex['lm_head_argmax_us_per_token']} us/token, argmax alone {ex['argmax_us']} us")
 

@@ -82,6 +82,7 @@ extern "C" {
 #define W4G_OP_GEMV 0
 #define W4G_OP_GEMM 1
 #define W4G_OP_ARGMAX 2
+#define W4G_OP_GEMV_ARGMAX 3
 
 /*
  * Decode product, 1 <= B <= 8 activation rows.
@@ -166,10 +167,35 @@ int vocab_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int
                  uint32_t* ids, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode product followed by the greedy argmax of each batch row, with the
+ * argmax's first pass fused into the product's epilogue, so the logits need not
+ * be written and read back.  The pages split the head the same way: each part
+ * reduces its own rows to one (value, id word) pair with the non-finite flag in
+ * bit 31, and a final pick combines the pairs (TensorFold PR #1433, step-1
+ * description: pair_argmax and pair_pick; step-2 description: the head over
+ * the whole vocabulary).
+ *   wq, scales, biases, x, B, N, K: as qmm_gemv (N is the vocabulary size,
+ *   N < 2^31).
+ *   logits [B][N] fp32, or NULL: when given, receives exactly the bits
+ *   qmm_gemv_ex(..., W4G_GEMV_VALU) writes.
+ *   ids [B] uint32: per batch row the id of the largest logit, the lowest id
+ *   among equal values (-0.0 ties +0.0), or W4G_SENTINEL if any logit of the
+ *   row is NaN or +-Inf; always equal to vocab_argmax over those logits.
+ *   workspace: at least qmm_workspace_bytes(W4G_OP_GEMV_ARGMAX, B, N, K)
+ *   bytes, 8-byte aligned: one (value, id | flag) record per workgroup of the
+ *   product and batch row.
+ * Order of the logits: that of the vector-ALU family (see qmm_gemv).
+ */
+int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                    const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N,
+                    int64_t K, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of workspace an operation needs for the given sizes; 0 when none.
  *   op W4G_OP_GEMV: rows = B, n = N, k = K.
  *   op W4G_OP_GEMM: rows = M, n = N, k = K.
  *   op W4G_OP_ARGMAX: rows = rows, n = vocab, k ignored.
+ *   op W4G_OP_GEMV_ARGMAX: rows = B, n = N, k = K.
  * Returns (size_t)-1 for an unknown op or sizes out of range.
  */
 size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k);

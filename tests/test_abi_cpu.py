@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert set(names) >= {"qmm_gemv", "qmm_gemv_ex", "qmm_gemm", "vocab_argmax",
+    assert set(names) >= {"qmm_gemv", "qmm_gemv_ex", "qmm_gemm", "qmm_gemv_argmax", "vocab_argmax",
                           "qmm_workspace_bytes", "w4g_status_string", "w4g_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -52,6 +52,7 @@ def test_constants_match_header(lib):
                  ("W4G_EDTYPE", _lib.EDTYPE), ("W4G_ELAUNCH", _lib.ELAUNCH), ("W4G_EALIAS", _lib.EALIAS),
                  ("W4G_F32", _lib.F32), ("W4G_BF16", _lib.BF16), ("W4G_OP_GEMV", _lib.OP_GEMV),
                  ("W4G_OP_GEMM", _lib.OP_GEMM), ("W4G_OP_ARGMAX", _lib.OP_ARGMAX),
+                 ("W4G_OP_GEMV_ARGMAX", _lib.OP_GEMV_ARGMAX),
                  ("W4G_GEMV_AUTO", _lib.GEMV_AUTO), ("W4G_GEMV_VALU", _lib.GEMV_VALU),
                  ("W4G_GEMV_MFMA", _lib.GEMV_MFMA), ("W4G_GEMV_VALU_REGS", _lib.GEMV_VALU_REGS)):
         assert val(k) == v, k
@@ -134,6 +135,29 @@ def test_argmax_rejects(lib):
     assert call(ws=LOG) == _lib.EALIAS
 
 
+def test_gemv_argmax_rejects(lib):
+    need = lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 2, 5000, 1024)
+    assert need > 0 and need % 16 == 0
+    call = lambda **k: lib.qmm_gemv_argmax(k.get("wq", WQ), SC, BI, X, k.get("lg", Y),
+                                           k.get("ids", IDS), k.get("B", 2), k.get("N", 5000),
+                                           k.get("K", 1024), k.get("ws", WS), k.get("wsb", need), None)
+    assert call(wq=None) == _lib.EINVAL_PTR
+    assert call(ids=None) == _lib.EINVAL_PTR
+    assert call(B=0) == _lib.ESHAPE
+    assert call(B=9) == _lib.ESHAPE
+    assert call(K=1000) == _lib.ESHAPE
+    assert call(N=1 << 31) == _lib.ESHAPE
+    assert call(lg=Y + 4) == _lib.EALIGN
+    assert call(ids=IDS + 2) == _lib.EALIGN
+    assert call(ws=WS + 4) == _lib.EALIGN
+    assert call(ws=None) == _lib.EWORKSPACE
+    assert call(wsb=need - 8) == _lib.EWORKSPACE
+    assert call(lg=X) == _lib.EALIAS
+    assert call(ids=WQ + 64) == _lib.EALIAS
+    assert call(ws=Y) == _lib.EALIAS
+    assert call(ids=WS) == _lib.EALIAS
+
+
 def test_workspace_sizes(lib):
     size_max = ctypes.c_size_t(-1).value
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV, 8, 5120, 5120) == 0
@@ -141,6 +165,11 @@ def test_workspace_sizes(lib):
     assert lib.qmm_workspace_bytes(_lib.OP_GEMM, 512, 5120, 5120) == 512 * 5120 * 2 + 512 * 3 * 80 * 2
     assert lib.qmm_workspace_bytes(_lib.OP_GEMM, 512, 5120, 17408) == 512 * 17408 * 2 + 512 * 3 * 272 * 2
     assert lib.qmm_workspace_bytes(_lib.OP_ARGMAX, 1, 248320, 0) == 243 * 8
+    # fused head: one record per product workgroup and batch row (16 rows per
+    # workgroup at B=1; 4 rows per 64-lane workgroup where x does not fit in LDS)
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 248320, 5120) == 15520 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 248320, 5120) == 8 * 62080 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 9, 248320, 5120) == size_max
     assert lib.qmm_workspace_bytes(7, 1, 1, 64) == size_max
 
 

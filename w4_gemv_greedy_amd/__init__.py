@@ -17,9 +17,10 @@ import ctypes
 from . import _lib
 from ._lib import (BF16, F32, GEMV_AUTO, GEMV_MFMA, GEMV_VALU, GEMV_VALU_REGS,  # noqa: F401
                    MAX_GEMV_BATCH,
-                   OP_ARGMAX, OP_GEMM, OP_GEMV, SENTINEL, W4GError)
+                   OP_ARGMAX, OP_GEMM, OP_GEMV, OP_GEMV_ARGMAX, SENTINEL, W4GError)
 
-__all__ = ["qmm_gemv", "qmm_gemm", "vocab_argmax", "workspace_bytes", "SENTINEL", "W4GError"]
+__all__ = ["qmm_gemv", "qmm_gemm", "qmm_gemv_argmax", "vocab_argmax", "workspace_bytes", "SENTINEL",
+           "W4GError"]
 
 
 def _torch():
@@ -114,6 +115,40 @@ def qmm_gemv(wq, scales, biases, x, y=None, workspace=None, kernel=GEMV_AUTO):
 def qmm_gemm(wq, scales, biases, x, y=None, workspace=None):
     """Prompt product for any M >= 1 rows of x (matrix cores); returns y [M][N] fp32."""
     return _call_qmm("qmm_gemm", OP_GEMM, wq, scales, biases, x, y, workspace)
+
+
+def qmm_gemv_argmax(wq, scales, biases, x, logits=None, ids=None, workspace=None, want_logits=True):
+    """Decode product and greedy argmax per batch row, the argmax's first pass
+    fused into the product; returns (ids, logits).
+
+    ids: int32 tensor [B] holding uint32 bits (0xFFFFFFFF = a non-finite logit
+    in the row).  logits: [B][N] fp32, allocated when not given and
+    want_logits is true; with want_logits false and no tensor given the
+    logits are never written and None is returned in their place.
+    """
+    torch = _torch()
+    N, K = _check_qmm(wq, scales, biases, x)
+    rows = x.shape[0]
+    if not 1 <= rows <= MAX_GEMV_BATCH:
+        raise ValueError(f"qmm_gemv_argmax takes 1..{MAX_GEMV_BATCH} rows")
+    if logits is None and want_logits:
+        logits = torch.empty((rows, N), dtype=torch.float32, device=wq.device)
+    if logits is not None:
+        _need(logits, "logits", (torch.float32,), 2, wq.device)
+        if tuple(logits.shape) != (rows, N):
+            raise ValueError(f"logits must be [{rows}][{N}]")
+    if ids is None:
+        ids = torch.empty(rows, dtype=torch.int32, device=wq.device)
+    _need(ids, "ids", (torch.int32, torch.uint32), 1, wq.device)
+    if ids.shape[0] != rows:
+        raise ValueError("ids must have one entry per row")
+    ws, nbytes = _workspace(OP_GEMV_ARGMAX, rows, N, K, wq.device, workspace)
+    lib = _lib.load()
+    status = lib.qmm_gemv_argmax(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
+                                 logits.data_ptr() if logits is not None else None, ids.data_ptr(),
+                                 rows, N, K, ws.data_ptr(), nbytes, _stream(wq))
+    _lib.check("qmm_gemv_argmax", status)
+    return ids, logits
 
 
 def vocab_argmax(logits, ids=None, workspace=None, vocab=None):

@@ -48,6 +48,10 @@ int check_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases
 
 int from_hip(hipError_t e) { return e == hipSuccess ? W4G_OK : W4G_ELAUNCH; }
 
+size_t gemv_argmax_bytes(int64_t B, int64_t N, int64_t K) {
+  return (size_t)B * (size_t)w4g::gemv_argmax_records((int)B, N, K) * sizeof(uint2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,6 +86,11 @@ size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k) {
     case W4G_OP_ARGMAX:
       if (rows < 1 || rows > 65535 || n < 1 || n >= kMaxDim) return (size_t)-1;
       return w4g::argmax_workspace_bytes(rows, n);
+    case W4G_OP_GEMV_ARGMAX:
+      if (rows < 1 || rows > W4G_MAX_GEMV_BATCH || n < 1 || n >= kMaxDim || k < 64 ||
+          k >= kMaxDim || k % 64)
+        return (size_t)-1;
+      return gemv_argmax_bytes(rows, n, k);
     default:
       return (size_t)-1;
   }
@@ -122,6 +131,39 @@ int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
   if (rc) return rc;
   return from_hip(w4g::launch_gemm(wq, scales, biases, x, y, M, N, K, workspace,
                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                    const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N, int64_t K,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!wq || !scales || !biases || !x || !ids) return W4G_EINVAL_PTR;
+  if (B < 1 || B > W4G_MAX_GEMV_BATCH || N < 1 || N >= kMaxDim || K < 64 || K >= kMaxDim || K % 64)
+    return W4G_ESHAPE;
+  if (!aligned16(wq) || !aligned16(x) || (logits && !aligned16(logits)) || !aligned2(scales) ||
+      !aligned2(biases) || (reinterpret_cast<uintptr_t>(ids) & 3u))
+    return W4G_EALIGN;
+  const size_t need = gemv_argmax_bytes(B, N, K);
+  if (!workspace || workspace_bytes < need) return W4G_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return W4G_EALIGN;
+  const size_t wbytes = (size_t)N * (size_t)(K / 8) * sizeof(uint32_t);
+  const size_t gbytes = (size_t)N * (size_t)(K / 64) * sizeof(uint16_t);
+  const size_t xbytes = (size_t)B * (size_t)K * sizeof(uint16_t);
+  const size_t lbytes = logits ? (size_t)B * (size_t)N * sizeof(float) : 0;
+  const size_t ibytes = (size_t)B * sizeof(uint32_t);
+  const void* outs[3] = {logits, ids, workspace};
+  const size_t osz[3] = {lbytes, ibytes, need};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], osz[i], wq, wbytes) || overlap(outs[i], osz[i], scales, gbytes) ||
+        overlap(outs[i], osz[i], biases, gbytes) || overlap(outs[i], osz[i], x, xbytes))
+      return W4G_EALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j])) return W4G_EALIAS;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint2* rec = reinterpret_cast<uint2*>(workspace);
+  const hipError_t e = w4g::launch_gemv_argmax(wq, scales, biases, x, logits, rec, (int)B, N, K, s);
+  if (e != hipSuccess) return W4G_ELAUNCH;
+  return from_hip(w4g::launch_argmax_combine(rec, B, w4g::gemv_argmax_records((int)B, N, K), ids, s));
 }
 
 int vocab_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,

@@ -8,39 +8,23 @@
 // failures there).  The session reads the sentinel as a failure, never as a
 // logit (step-2 description).
 //
-// Comparison: each finite fp32 value maps to an unsigned key that orders
-// exactly as IEEE comparison does, with -0.0 and +0.0 given the same key, so
-// denormals compare exactly whatever the float denormal mode.  A candidate is
-// the 64-bit word (key << 32) | (0xFFFFFFFF - id); the maximum word is the
-// largest value with the lowest id, so every reduction step is an unsigned max
-// and the result does not depend on the reduction tree.
+// Comparison: the ordering helpers of w4g_internal.h (an unsigned key per
+// value, -0.0 and +0.0 equal, and a 64-bit candidate word whose maximum is the
+// largest value with the lowest id).
 #include "w4g_internal.h"
 
 namespace w4g {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr uint32_t kFlag = 0x80000000u;
+constexpr uint32_t kFlag = kArgmaxFlag;
 
-__device__ __forceinline__ uint32_t order_key(uint32_t u) {
-  if ((u & 0x7FFFFFFFu) == 0) return 0x80000000u;  // +0 and -0 tie
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ uint32_t key_bits(uint32_t k) {
-  return (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-}
-__device__ __forceinline__ bool finite_bits(uint32_t u) {
-  return (u & 0x7F800000u) != 0x7F800000u;
-}
-__device__ __forceinline__ uint64_t cand(uint32_t bits, uint32_t id) {
-  return ((uint64_t)order_key(bits) << 32) | (uint64_t)(0xFFFFFFFFu - id);
-}
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Block-wide reduction of (best, bad); returns the result in every thread.
+// Block-wide reduction of (best, bad) over NT threads; returns the result in
+// every thread.
+template <int NT = kThreads>
 __device__ __forceinline__ void block_reduce(uint64_t& best, bool& bad) {
-  __shared__ uint64_t s_best[kThreads / 64];
-  __shared__ int s_bad[kThreads / 64];
+  __shared__ uint64_t s_best[NT / 64];
+  __shared__ int s_bad[NT / 64];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     uint32_t lo = (uint32_t)best, hi = (uint32_t)(best >> 32);
@@ -58,7 +42,7 @@ __device__ __forceinline__ void block_reduce(uint64_t& best, bool& bad) {
   best = s_best[0];
   int b = s_bad[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) {
+  for (int w = 1; w < NT / 64; ++w) {
     best = umax64(best, s_best[w]);
     b |= s_bad[w];
   }
@@ -106,30 +90,34 @@ __global__ __launch_bounds__(kThreads) void argmax_pass1(const void* __restrict_
     }
   }
   block_reduce(best, bad);
-  if (threadIdx.x == 0) {
-    uint2 r;
-    if (bad) {
-      r.x = 0x7FC00000u;
-      r.y = kFlag | (uint32_t)(blk * kArgmaxBlock);
-    } else {
-      r.x = key_bits((uint32_t)(best >> 32));
-      r.y = 0xFFFFFFFFu - (uint32_t)best;
-    }
-    rec[row * nblk + blk] = r;
-  }
+  if (threadIdx.x == 0) rec[row * nblk + blk] = make_record(best, bad, (uint32_t)(blk * kArgmaxBlock));
 }
 
-__global__ __launch_bounds__(kThreads) void argmax_pass2(const uint2* __restrict__ rec, int nblk,
-                                                         uint32_t* __restrict__ ids) {
+// One workgroup of NT threads per row; each thread folds its records with U
+// loads in flight at a time (all of a row's records in one round when there
+// are at most NT * U of them).
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void argmax_pass2(const uint2* __restrict__ rec, int64_t nblk,
+                                                   uint32_t* __restrict__ ids) {
   const int64_t row = blockIdx.x;
+  const uint2* r0 = rec + row * nblk;
   uint64_t best = 0;
   bool bad = false;
-  for (int i = threadIdx.x; i < nblk; i += kThreads) {
-    const uint2 r = rec[row * nblk + i];
-    if (r.y & kFlag) bad = true;
-    else best = umax64(best, cand(r.x, r.y));
+  for (int64_t i0 = threadIdx.x; i0 < nblk; i0 += (int64_t)NT * U) {
+    uint2 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * NT;
+      r[u] = i < nblk ? r0[i] : make_uint2(0u, 0u);  // (+0.0, id 0): below any real candidate's id
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + (int64_t)u * NT >= nblk) continue;
+      if (r[u].y & kFlag) bad = true;
+      else best = umax64(best, cand(r[u].x, r[u].y));
+    }
   }
-  block_reduce(best, bad);
+  block_reduce<NT>(best, bad);
   if (threadIdx.x == 0) ids[row] = bad ? 0xFFFFFFFFu : 0xFFFFFFFFu - (uint32_t)best;
 }
 
@@ -151,7 +139,17 @@ hipError_t launch_argmax(const void* logits, int dtype, int64_t rows, int64_t vo
     hipLaunchKernelGGL(argmax_pass1<1>, g1, dim3(kThreads), 0, stream, logits, ld, vocab, nblk, rec);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(argmax_pass2, dim3((unsigned)rows), dim3(kThreads), 0, stream, rec, nblk, ids);
+  return launch_argmax_combine(rec, rows, nblk, ids, stream);
+}
+
+hipError_t launch_argmax_combine(const uint2* rec, int64_t rows, int64_t nrec, uint32_t* ids,
+                                 hipStream_t stream) {
+  if (nrec > 4 * kThreads)
+    hipLaunchKernelGGL((argmax_pass2<1024, 16>), dim3((unsigned)rows), dim3(1024), 0, stream, rec, nrec,
+                       ids);
+  else
+    hipLaunchKernelGGL((argmax_pass2<kThreads, 4>), dim3((unsigned)rows), dim3(kThreads), 0, stream, rec,
+                       nrec, ids);
   return hipGetLastError();
 }
 

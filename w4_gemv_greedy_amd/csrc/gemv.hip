@@ -109,13 +109,19 @@ struct Item {
 // the same number of items, so every branch in the stream is wave-uniform).
 // A lane past the end of a short last chunk reads lane 0 of chunk 0 (always
 // staged, so finite) and adds exact zeros.
-template <int B, int R, int P, bool RAGGED>
+//
+// AM adds the argmax's pass 1 as an epilogue (launched with ng = 1): the
+// workgroup's values go to LDS, and after the stream one thread per batch row
+// writes the record of the best (value, lowest row), or the non-finite flag,
+// to rec[bb][blockIdx.x]; y may then be null.
+template <int B, int R, int P, bool RAGGED, bool AM>
 __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __restrict__ wq,
                                                              const uint16_t* __restrict__ scales,
                                                              const uint16_t* __restrict__ biases,
                                                              const uint16_t* __restrict__ x,
                                                              float* __restrict__ y, int64_t N,
-                                                             int64_t K, int64_t ng) {
+                                                             int64_t K, int64_t ng,
+                                                             uint2* __restrict__ rec) {
   extern __shared__ uint4 s_mem[];
   const int64_t K8 = K >> 3, K32 = K >> 5, G = K >> 6;
   const int C = (int)((K + kChunk - 1) / kChunk);
@@ -172,6 +178,9 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
 #pragma unroll
   for (int sl = 0; sl < P; ++sl) issue(ring[sl]);
 
+  // argmax epilogue: the workgroup's values (one group of R rows per half wave)
+  __shared__ float s_vals[AM ? kHalfWaves * R : 1][AM ? B : 1];
+
   // ---- stage x: pair each 8-element block, and sum each 32-element lane segment
   for (int64_t seg = tid; seg < B * K32; seg += kThreads) {
     const int bb = (int)(seg / K32);
@@ -203,6 +212,7 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
     for (int bb = 0; bb < B; ++bb) acc[r][bb] = 0.0f;
   int64_t crow = row_begin;
   int cc = 0;
+
   const uint4* xlane = s_xp + lane;
   const float* hlane = s_xh + lane;
   auto consume = [&](const Item<R>& it, int64_t item) {
@@ -245,7 +255,8 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
 #pragma unroll
           for (int bb = 0; bb < B; ++bb) {
             const float v = half_wave_sum(acc[r][bb]);
-            if (lane == 0 && crow + r < N) y[(int64_t)bb * N + crow + r] = v;
+            if (lane == 0 && crow + r < N && (!AM || y != nullptr)) y[(int64_t)bb * N + crow + r] = v;
+            if (AM && lane == 0) s_vals[(tid >> 5) * R + r][bb] = v;
             acc[r][bb] = 0.0f;
           }
         }
@@ -272,6 +283,26 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
   }
 #pragma unroll
   for (int sl = 0; sl < P; ++sl) consume(ring[sl], it + P + sl);
+
+  if constexpr (AM) {
+    // the best (value, lowest row) per batch row, or the non-finite flag
+    // (launched with one group of R rows per half wave)
+    __syncthreads();
+    if (tid < B) {
+      const int64_t first = (int64_t)blockIdx.x * kHalfWaves * R;
+      uint64_t best = 0;
+      bool bad = false;
+#pragma unroll
+      for (int i = 0; i < kHalfWaves * R; ++i) {
+        if (first + i < N) {
+          const uint32_t u = __float_as_uint(s_vals[i][tid]);
+          if (!finite_bits(u)) bad = true;
+          else best = umax64(best, cand(u, (uint32_t)(first + i)));
+        }
+      }
+      rec[(int64_t)tid * gridDim.x + blockIdx.x] = make_record(best, bad, (uint32_t)first);
+    }
+  }
 }
 
 // Register-staged variant of the same arithmetic, for shapes whose paired
@@ -280,13 +311,15 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
 // of a chunk straight into registers.  Every floating-point step, and its
 // order, is the one described at the top of this file, so both variants give
 // the same bits.
-template <int B, int R>
+// AM: the argmax epilogue as in gemv_valu_kernel (one record per batch row per
+// 64-lane workgroup).
+template <int B, int R, bool AM>
 __global__ __launch_bounds__(64) void gemv_valu_regs_kernel(const uint32_t* __restrict__ wq,
                                                             const uint16_t* __restrict__ scales,
                                                             const uint16_t* __restrict__ biases,
                                                             const uint16_t* __restrict__ x,
                                                             float* __restrict__ y, int64_t N,
-                                                            int64_t K) {
+                                                            int64_t K, uint2* __restrict__ rec) {
   const int lane = threadIdx.x & 31;
   const int64_t row0 = ((int64_t)blockIdx.x * 2 + (threadIdx.x >> 5)) * R;
   const int64_t G = K >> 6;
@@ -345,12 +378,34 @@ __global__ __launch_bounds__(64) void gemv_valu_regs_kernel(const uint32_t* __re
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int bb = 0; bb < B; ++bb) acc[r][bb] = half_wave_sum(acc[r][bb]);
-  if (lane == 0) {
+  if (lane == 0 && (!AM || y != nullptr)) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (row0 + r < N)
 #pragma unroll
         for (int bb = 0; bb < B; ++bb) y[(int64_t)bb * N + row0 + r] = acc[r][bb];
+  }
+  if constexpr (AM) {
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) {
+      uint64_t best = 0;
+      bool bad = false;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (row0 + r < N) {
+          const uint32_t u = __float_as_uint(acc[r][bb]);
+          if (!finite_bits(u)) bad = true;
+          else best = umax64(best, cand(u, (uint32_t)(row0 + r)));
+        }
+      }
+      // the two half waves meet in lane 0
+      const uint32_t lo = __shfl((uint32_t)best, 32), hi = __shfl((uint32_t)(best >> 32), 32);
+      const int bad2 = __shfl(bad ? 1 : 0, 32);
+      if (threadIdx.x == 0)
+        rec[(int64_t)bb * gridDim.x + blockIdx.x] =
+            make_record(umax64(best, ((uint64_t)hi << 32) | lo), bad || bad2 != 0,
+                        (uint32_t)((int64_t)blockIdx.x * 2 * R));
+    }
   }
 }
 
@@ -359,35 +414,88 @@ size_t lds_bytes(int B, int64_t K) {
   return (size_t)B * (size_t)C * (128 * 16 + 32 * 4);
 }
 
-template <int B, int R, int P>
+// Rows per item for the shared-memory variant, by batch (measured); few rows
+// (N below 16 per-item groups of 1024) take one row per item and a deeper ring.
+bool few_rows(int64_t N) { return N < (int64_t)kHalfWaves * 2 * 1024; }
+int lds_rows_per_item(int B, int64_t N) { return B == 1 ? (few_rows(N) ? 1 : 2) : B == 2 ? 4 : 2; }
+int regs_rows(int B) { return B <= 2 ? 4 : 2; }
+bool use_regs(int B, int64_t K, bool force_regs) { return force_regs || lds_bytes(B, K) > kMaxLds; }
+
+template <int B, int R, int P, bool AM>
 hipError_t launch_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                      const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream) {
+                      const uint16_t* x, float* y, uint2* rec, int64_t N, int64_t K, int64_t ng,
+                      hipStream_t stream) {
   const bool ragged = (K % kChunk) != 0;
-  // one group of R rows per half wave: many short workgroups, which the
-  // dispatcher spreads over the CUs as they free up (measured faster than
-  // fewer, longer-lived ones, whose slowest CU sets the end)
-  int64_t ng = 1;
-#ifdef W4G_TUNING
-  if (getenv("W4G_NG")) ng = atoll(getenv("W4G_NG"));
-#endif
   const int64_t rows_per_block = (int64_t)kHalfWaves * R * ng;
   const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
   if (ragged)
-    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, true>), dim3((unsigned)blocks), dim3(kThreads),
-                       lds_bytes(B, K), stream, wq, scales, biases, x, y, N, K, ng);
+    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, true, AM>), dim3((unsigned)blocks), dim3(kThreads),
+                       lds_bytes(B, K), stream, wq, scales, biases, x, y, N, K, ng, rec);
   else
-    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, false>), dim3((unsigned)blocks), dim3(kThreads),
-                       lds_bytes(B, K), stream, wq, scales, biases, x, y, N, K, ng);
+    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, false, AM>), dim3((unsigned)blocks), dim3(kThreads),
+                       lds_bytes(B, K), stream, wq, scales, biases, x, y, N, K, ng, rec);
   return hipGetLastError();
 }
 
-template <int B, int R>
+template <int B, int R, bool AM>
 hipError_t launch_regs(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                       const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream) {
+                       const uint16_t* x, float* y, uint2* rec, int64_t N, int64_t K,
+                       hipStream_t stream) {
   const int64_t blocks = (N + 2 * R - 1) / (2 * R);
-  hipLaunchKernelGGL((gemv_valu_regs_kernel<B, R>), dim3((unsigned)blocks), dim3(64), 0, stream, wq,
-                     scales, biases, x, y, N, K);
+  hipLaunchKernelGGL((gemv_valu_regs_kernel<B, R, AM>), dim3((unsigned)blocks), dim3(64), 0, stream,
+                     wq, scales, biases, x, y, N, K, rec);
   return hipGetLastError();
+}
+
+// The one dispatch both entry points share: the kernel, R and P are functions
+// of (B, N, K) and force_regs only, and the workgroup count follows from them.
+template <bool AM>
+hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                    const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                    bool force_regs, hipStream_t stream) {
+  if (use_regs(B, K, force_regs)) {
+    switch (B) {
+      case 1: return launch_regs<1, 4, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+      case 2: return launch_regs<2, 4, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+      case 3: return launch_regs<3, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+      case 4: return launch_regs<4, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+      case 5: return launch_regs<5, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+      case 6: return launch_regs<6, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+      case 7: return launch_regs<7, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+      case 8: return launch_regs<8, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  int64_t ng = 1;  // one group of R rows per half wave: many short workgroups,
+                   // which the dispatcher spreads over the CUs as they free up
+#ifdef W4G_TUNING
+  if (!AM && getenv("W4G_NG")) ng = atoll(getenv("W4G_NG"));
+  if (!AM && B == 1 && getenv("W4G_RP")) {
+    const int rp = atoi(getenv("W4G_RP"));
+    switch (rp) {
+      case 12: return launch_lds<1, 1, 2, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+      case 14: return launch_lds<1, 1, 4, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+      case 16: return launch_lds<1, 1, 6, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+      case 22: return launch_lds<1, 2, 2, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+      case 23: return launch_lds<1, 2, 3, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+      case 42: return launch_lds<1, 4, 2, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+      case 43: return launch_lds<1, 4, 3, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+      default: break;
+    }
+  }
+#endif
+  switch (B) {
+    case 1: return few_rows(N) ? launch_lds<1, 1, 4, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream)
+                               : launch_lds<1, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+    case 2: return launch_lds<2, 4, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+    case 3: return launch_lds<3, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+    case 4: return launch_lds<4, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+    case 5: return launch_lds<5, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+    case 6: return launch_lds<6, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+    case 7: return launch_lds<7, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+    case 8: return launch_lds<8, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -395,48 +503,22 @@ hipError_t launch_regs(const uint32_t* wq, const uint16_t* scales, const uint16_
 hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                        const uint16_t* x, float* y, int B, int64_t N, int64_t K, bool force_regs,
                        hipStream_t stream) {
-  if (force_regs || lds_bytes(B, K) > kMaxLds) {
-    switch (B) {
-      case 1: return launch_regs<1, 4>(wq, scales, biases, x, y, N, K, stream);
-      case 2: return launch_regs<2, 4>(wq, scales, biases, x, y, N, K, stream);
-      case 3: return launch_regs<3, 2>(wq, scales, biases, x, y, N, K, stream);
-      case 4: return launch_regs<4, 2>(wq, scales, biases, x, y, N, K, stream);
-      case 5: return launch_regs<5, 2>(wq, scales, biases, x, y, N, K, stream);
-      case 6: return launch_regs<6, 2>(wq, scales, biases, x, y, N, K, stream);
-      case 7: return launch_regs<7, 2>(wq, scales, biases, x, y, N, K, stream);
-      case 8: return launch_regs<8, 2>(wq, scales, biases, x, y, N, K, stream);
-      default: return hipErrorInvalidValue;
-    }
+  return dispatch<false>(wq, scales, biases, x, y, nullptr, B, N, K, force_regs, stream);
+}
+
+int64_t gemv_argmax_records(int B, int64_t N, int64_t K) {
+  if (use_regs(B, K, false)) {
+    const int R = regs_rows(B);
+    return (N + 2 * R - 1) / (2 * R);
   }
-#ifdef W4G_TUNING
-  if (B == 1 && getenv("W4G_RP")) {
-    const int rp = atoi(getenv("W4G_RP"));
-    switch (rp) {
-      case 12: return launch_lds<1, 1, 2>(wq, scales, biases, x, y, N, K, stream);
-      case 14: return launch_lds<1, 1, 4>(wq, scales, biases, x, y, N, K, stream);
-      case 16: return launch_lds<1, 1, 6>(wq, scales, biases, x, y, N, K, stream);
-      case 22: return launch_lds<1, 2, 2>(wq, scales, biases, x, y, N, K, stream);
-      case 23: return launch_lds<1, 2, 3>(wq, scales, biases, x, y, N, K, stream);
-      case 42: return launch_lds<1, 4, 2>(wq, scales, biases, x, y, N, K, stream);
-      case 43: return launch_lds<1, 4, 3>(wq, scales, biases, x, y, N, K, stream);
-      default: break;
-    }
-  }
-#endif
-  // few rows: one row per item and a deeper ring, so every CU has work
-  const bool few_rows = N < (int64_t)kHalfWaves * 2 * 1024;
-  switch (B) {
-    case 1: return few_rows ? launch_lds<1, 1, 4>(wq, scales, biases, x, y, N, K, stream)
-                            : launch_lds<1, 2, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 2: return launch_lds<2, 4, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 3: return launch_lds<3, 2, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 4: return launch_lds<4, 2, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 5: return launch_lds<5, 2, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 6: return launch_lds<6, 2, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 7: return launch_lds<7, 2, 2>(wq, scales, biases, x, y, N, K, stream);
-    case 8: return launch_lds<8, 2, 2>(wq, scales, biases, x, y, N, K, stream);
-    default: return hipErrorInvalidValue;
-  }
+  const int64_t rows_per_block = (int64_t)kHalfWaves * lds_rows_per_item(B, N);
+  return (N + rows_per_block - 1) / rows_per_block;
+}
+
+hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                              const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                              hipStream_t stream) {
+  return dispatch<true>(wq, scales, biases, x, y, rec, B, N, K, false, stream);
 }
 
 }  // namespace w4g

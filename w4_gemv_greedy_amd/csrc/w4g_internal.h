@@ -32,7 +32,53 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                          uint32_t* ids, void* workspace, hipStream_t stream);
 size_t argmax_workspace_bytes(int64_t rows, int64_t vocab);
+// Pass 2 alone: combines `nrec` (value, id | flag) records per row into ids.
+hipError_t launch_argmax_combine(const uint2* rec, int64_t rows, int64_t nrec, uint32_t* ids,
+                                 hipStream_t stream);
+// Decode product on the vector ALUs with the argmax's pass 1 as its epilogue:
+// each workgroup writes one record per batch row (`nrec` per row, see
+// gemv_argmax_records) instead of needing the logits read back; `y` may be
+// null.  The logits' bits are those of launch_gemv.
+hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                              const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                              hipStream_t stream);
+int64_t gemv_argmax_records(int B, int64_t N, int64_t K);
 
 constexpr int kArgmaxBlock = 1024;  // ids per pass-1 record
+constexpr uint32_t kArgmaxFlag = 0x80000000u;  // non-finite bit of a record's id word
+
+// Argmax ordering.  Each finite fp32 value maps to an unsigned key that orders
+// exactly as IEEE comparison does, with -0.0 and +0.0 given the same key, so
+// denormals compare exactly whatever the float denormal mode.  A candidate is
+// the 64-bit word (key << 32) | (0xFFFFFFFF - id); the maximum word is the
+// largest value with the lowest id, so every reduction step is an unsigned max
+// and no result depends on the reduction tree.
+__device__ __forceinline__ uint32_t order_key(uint32_t u) {
+  if ((u & 0x7FFFFFFFu) == 0) return 0x80000000u;  // +0 and -0 tie
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t key_bits(uint32_t k) {
+  return (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+}
+__device__ __forceinline__ bool finite_bits(uint32_t u) {
+  return (u & 0x7F800000u) != 0x7F800000u;
+}
+__device__ __forceinline__ uint64_t cand(uint32_t bits, uint32_t id) {
+  return ((uint64_t)order_key(bits) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// The pass-1 record of a candidate: value bits and id, or the flag if any
+// value was not finite.
+__device__ __forceinline__ uint2 make_record(uint64_t best, bool bad, uint32_t first_id) {
+  uint2 r;
+  if (bad) {
+    r.x = 0x7FC00000u;
+    r.y = kArgmaxFlag | first_id;
+  } else {
+    r.x = key_bits((uint32_t)(best >> 32));
+    r.y = 0xFFFFFFFFu - (uint32_t)best;
+  }
+  return r;
+}
 
 }  // namespace w4g
