@@ -54,6 +54,8 @@ def load(path=None):
     lib.w4o_qmm_rows.restype = None
     lib.w4o_argmax.argtypes = [P, I, I64, I64, I64, P, P]
     lib.w4o_argmax.restype = I
+    lib.w4o_argmax_top2.argtypes = [P, I, I64, I64, I64, P, P, P]
+    lib.w4o_argmax_top2.restype = I
     lib.w4o_plant.restype = I
     lib.w4o_threads.restype = I
     _libs[path] = lib
@@ -136,6 +138,31 @@ def argmax(logits, lib=None):
     if rc:
         raise ValueError(f"oracle argmax rejected its arguments ({rc})")
     return ids
+
+
+def argmax_top2(logits, lib=None):
+    """(ids [rows][2] uint32, gaps [rows] fp32): winner and runner-up of each row
+    (value descending, id ascending), gap = v(winner) - v(runner-up) with zeros as
+    +0.0; the sentinel twice and a NaN gap for a row holding a non-finite value.
+    logits: [rows][V >= 2] fp32, or bf16 bits as uint16."""
+    lib = lib or load()
+    logits = np.ascontiguousarray(logits)
+    if logits.ndim == 1:
+        logits = logits[None, :]
+    if logits.dtype == np.float32:
+        dtype = 0
+    elif logits.dtype == np.uint16:
+        dtype = 1
+    else:
+        raise TypeError("logits must be float32 or bf16 bits (uint16)")
+    rows, V = logits.shape
+    ids = np.empty((rows, 2), np.uint32)
+    gaps = np.empty(rows, np.float32)
+    scratch = np.empty(max(V, 1), np.float32)
+    rc = lib.w4o_argmax_top2(_ptr(logits), dtype, rows, V, V, _ptr(ids), _ptr(gaps), _ptr(scratch))
+    if rc:
+        raise ValueError(f"oracle top-2 rejected its arguments ({rc})")
+    return ids, gaps
 
 
 def threads(lib=None):

@@ -39,6 +39,14 @@
  *    IEEE float comparison, so -0.0 and +0.0 tie and denormals compare
  *    exactly.  bf16 logits are widened to fp32 exactly first.
  *
+ *  - Top two: the winner and the runner-up of the same ordering (value
+ *    descending, id ascending), that is the argmax and then the argmax over
+ *    the other ids, with the gap v(winner) - v(runner-up) in fp32, zeros
+ *    counted as +0.0 so the gap is never -0.0.  A row holding a non-finite
+ *    value gives the sentinel for both and a NaN gap.  (Reading: the pages'
+ *    session merges "the top two" across blocks for its tie test, TensorFold
+ *    PR #1433, step-1 description; the pages fix no format for it.)
+ *
  * Parallelism: optional OpenMP over independent output elements only.  Every
  * single dot product is computed by one thread in ascending k, so the result
  * does not depend on the thread count.
@@ -61,7 +69,7 @@
    4 tie to the higher id, 5 no non-finite flag, 6 bias sign flipped,
    7 scale/bias tables read as [G][N], 8 -0.0 ordered below +0.0,
    9 fp32 accumulation, 10 activation row picked by the output row's stride,
-   11 last K group dropped */
+   11 last K group dropped, 12 runner-up tie to the higher id */
 
 /* bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits. */
 static float o_bf16_to_f32(uint16_t h) {
@@ -208,6 +216,53 @@ static uint32_t o_argmax_f32(const float* v, int64_t V) {
 #endif
   }
   return (uint32_t)best;
+}
+
+/* The runner-up: the argmax over every id but `skip`, same rules.  V >= 2. */
+static uint32_t o_argmax_skip_f32(const float* v, int64_t V, int64_t skip) {
+  int64_t best = skip == 0 ? 1 : 0;
+  for (int64_t i = best + 1; i < V; ++i) {
+    if (i == skip) continue;
+#if W4O_PLANT == 12
+    if (v[i] >= v[best]) best = i;
+#else
+    if (v[i] > v[best]) best = i;
+#endif
+  }
+  return (uint32_t)best;
+}
+
+static float o_plus_zero(float v) { return v == 0.0f ? 0.0f : v; }
+
+static void o_top2_f32(const float* v, int64_t V, uint32_t* ids2, float* gap) {
+  const uint32_t a = o_argmax_f32(v, V);
+  if (a == 0xFFFFFFFFu) {
+    ids2[0] = ids2[1] = 0xFFFFFFFFu;
+    *gap = NAN;
+    return;
+  }
+  const uint32_t b = o_argmax_skip_f32(v, V, (int64_t)a);
+  ids2[0] = a;
+  ids2[1] = b;
+  *gap = o_plus_zero(v[a]) - o_plus_zero(v[b]);
+}
+
+/* Top two per row (V >= 2): ids2[r][0..1], gaps[r]. */
+int w4o_argmax_top2(const void* logits, int dtype, int64_t rows, int64_t V, int64_t ld,
+                    uint32_t* ids2, float* gaps, float* scratch) {
+  if (V < 2 || ld < V || rows < 0) return 1;
+  for (int64_t r = 0; r < rows; ++r) {
+    if (dtype == 0) {
+      o_top2_f32((const float*)logits + r * ld, V, ids2 + 2 * r, gaps + r);
+    } else if (dtype == 1) {
+      const uint16_t* row = (const uint16_t*)logits + r * ld;
+      for (int64_t i = 0; i < V; ++i) scratch[i] = o_bf16_to_f32(row[i]);
+      o_top2_f32(scratch, V, ids2 + 2 * r, gaps + r);
+    } else {
+      return 2;
+    }
+  }
+  return 0;
 }
 
 /* dtype 0: fp32 logits; dtype 1: bf16 logits.  Row r starts at element r*ld. */

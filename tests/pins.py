@@ -283,7 +283,50 @@ def pin_argmax_bf16_nonfinite(lib):
     assert int(oracle.argmax(r, lib=lib)[0]) == 10
 
 
+def pin_top2_lexsort(lib):
+    """Top two: the first two ids of numpy's stable sort by value descending (a
+    lexsort on (id, -value)), on random rows and on coarse rows full of ties,
+    fp32 and bf16; the gap is their fp32 difference with zeros counted as +0."""
+    r = np.random.default_rng(23)
+    x = (r.standard_normal((600, 2500)) * 3).astype(np.float32)
+    x[300:] = np.round(x[300:] * 2) / 2            # many exact ties, at the top too
+    x[550:, 100] = x[550:].max(axis=1)              # a tie for first place at id 100 or above
+    x[580:] = np.where(x[580:] == 0, np.float32(-0.0), x[580:])  # -0.0 among the zeros
+    for data, vals in ((x, x), (synth.f32_to_bf16_bits(x), None)):
+        vals = synth.bf16_bits_to_f32(data) if vals is None else vals
+        ids, gaps = oracle.argmax_top2(data, lib=lib)
+        for i in range(vals.shape[0]):
+            order = np.lexsort((np.arange(vals.shape[1]), -vals[i].astype(np.float64)))
+            a, b = order[0], order[1]
+            assert (ids[i, 0], ids[i, 1]) == (a, b), (i, ids[i], a, b)
+            want = np.float32(vals[i, a] + np.float32(0)) - np.float32(vals[i, b] + np.float32(0))
+            assert gaps[i].tobytes() == np.float32(want).tobytes(), (i, gaps[i], want)
+
+
+def pin_top2_rules(lib):
+    """Top two on hand-made rows: ties, +-0, denormals, the last id, non-finite rows."""
+    def t2(row):
+        ids, gaps = oracle.argmax_top2(np.asarray(row, np.float32), lib=lib)
+        return int(ids[0, 0]), int(ids[0, 1]), float(gaps[0])
+    assert t2([1, 2, 3]) == (2, 1, 1.0)
+    assert t2([5, 5, 1]) == (0, 1, 0.0)               # tied winners: lower id first
+    assert t2([3, 5, 5]) == (1, 2, 0.0)
+    assert t2([7, 1, 7, 7]) == (0, 2, 0.0)
+    assert t2([1, 4, 2, 4, 3]) == (1, 3, 0.0)
+    assert t2([0.0, -0.0]) == (0, 1, 0.0)
+    assert t2([-0.0, 0.0]) == (0, 1, 0.0)
+    ids, gaps = oracle.argmax_top2(np.array([[-0.0, 0.0, -1.0]], np.float32), lib=lib)
+    assert gaps[0].tobytes() == np.float32(0.0).tobytes()   # never -0.0
+    d1, d2 = np.float32(2.0 ** -148), np.float32(2.0 ** -149)  # two and one times the least denormal
+    assert t2([d2, d1, 0.0]) == (1, 0, float(d1 - d2))       # denormals compare exactly
+    assert t2([-3, -2, -1]) == (2, 1, 1.0)                   # winner at the last id
+    ids, gaps = oracle.argmax_top2(np.array([[1, np.nan, 2], [np.inf, 1, 2], [1, 2, -np.inf]],
+                                            np.float32), lib=lib)
+    assert np.all(ids == SENTINEL) and np.all(np.isnan(gaps))
+
+
 PRODUCT_PINS = [pin_hand_dequant, pin_closed_form, pin_integer_matvec, pin_scale_bias_layout,
                 pin_bruteforce, pin_numpy_dot, pin_dequant_bits, pin_invariants, pin_rows_subset]
-ARGMAX_PINS = [pin_argmax_rules, pin_argmax_numpy, pin_argmax_bf16_nonfinite]
+ARGMAX_PINS = [pin_argmax_rules, pin_argmax_numpy, pin_argmax_bf16_nonfinite, pin_top2_rules,
+               pin_top2_lexsort]
 ALL_PINS = PRODUCT_PINS + ARGMAX_PINS

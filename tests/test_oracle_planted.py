@@ -24,6 +24,7 @@ PLANTS = {
     9: "fp32 accumulation",
     10: "activation row stride taken from N",
     11: "last K group dropped",
+    12: "runner-up tie to the higher id",
 }
 
 
