@@ -341,7 +341,17 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args):
         w4g.vocab_argmax(logits, ids, ws)
     ms, _ = timed(argmax_only, 20, 3, True, reps=20)
     ex["argmax_us"] = round(ms * 1e3, 2)
-    log(f"lm_head+argmax {ex['lm_head_argmax_us_per_token']} us/token, argmax alone {ex['argmax_us']} us")
+    ids2 = torch.empty((1, 2), dtype=torch.int32, device=dev)
+    gaps = torch.empty(1, dtype=torch.float32, device=dev)
+    ws2 = torch.empty(w4g.workspace_bytes(w4g.OP_ARGMAX_TOP2, 1, VOCAB, 0), dtype=torch.uint8,
+                      device=dev)
+
+    def top2_only():
+        w4g.vocab_argmax_top2(logits, ids2, gaps, ws2)
+    ms, _ = timed(top2_only, 20, 3, True, reps=20)
+    ex["argmax_top2_us"] = round(ms * 1e3, 2)
+    log(f"lm_head+argmax {ex['lm_head_argmax_us_per_token']} us/token, argmax alone {ex['argmax_us']} us, "
+        f"top two {ex['argmax_top2_us']} us")
 
     # per-product averages at batch 1, 4, 8 for both kernel families, each cycling
     # through the 16 layers' weights (2.6 GB, so nothing stays in the 256 MB cache)

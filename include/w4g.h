@@ -83,6 +83,7 @@ extern "C" {
 #define W4G_OP_GEMM 1
 #define W4G_OP_ARGMAX 2
 #define W4G_OP_GEMV_ARGMAX 3
+#define W4G_OP_ARGMAX_TOP2 4
 
 /*
  * Decode product, 1 <= B <= 8 activation rows.
@@ -191,11 +192,32 @@ int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
                     int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Top two of each logit row: the winner and the runner-up of the argmax's own
+ * ordering (value descending, lowest id first among equal values, -0.0 equal
+ * to +0.0) and the gap between them, so that a greedy pick that differs
+ * between two computations of the logits can be told apart from a near tie.
+ * (Reading: the pages' session merges "the top two" across blocks for its
+ * tie test, TensorFold PR #1433, step-1 description; no format is given.)
+ *   logits, dtype, rows, ld: as vocab_argmax; 2 <= vocab < 2^31.
+ *   ids2 [rows][2] uint32: winner, runner-up (ids2[r][0] equals vocab_argmax's
+ *   id); both W4G_SENTINEL if the row holds NaN or +-Inf.
+ *   gaps [rows] fp32: v(winner) - v(runner-up) rounded to fp32, with either
+ *   zero taken as +0.0 (so never -0.0); NaN for a non-finite row.
+ *   workspace: at least qmm_workspace_bytes(W4G_OP_ARGMAX_TOP2, rows, vocab, 0)
+ *   bytes, 16-byte aligned.
+ * Two passes as in vocab_argmax, each keeping the two largest candidates.
+ */
+int vocab_argmax_top2(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                      uint32_t* ids2, float* gaps, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * Bytes of workspace an operation needs for the given sizes; 0 when none.
  *   op W4G_OP_GEMV: rows = B, n = N, k = K.
  *   op W4G_OP_GEMM: rows = M, n = N, k = K.
  *   op W4G_OP_ARGMAX: rows = rows, n = vocab, k ignored.
  *   op W4G_OP_GEMV_ARGMAX: rows = B, n = N, k = K.
+ *   op W4G_OP_ARGMAX_TOP2: rows = rows, n = vocab (>= 2), k ignored.
  * Returns (size_t)-1 for an unknown op or sizes out of range.
  */
 size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k);

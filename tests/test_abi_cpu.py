@@ -31,6 +31,7 @@ def _declared_functions():
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
     assert set(names) >= {"qmm_gemv", "qmm_gemv_ex", "qmm_gemm", "qmm_gemv_argmax", "vocab_argmax",
+                          "vocab_argmax_top2",
                           "qmm_workspace_bytes", "w4g_status_string", "w4g_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -52,7 +53,7 @@ def test_constants_match_header(lib):
                  ("W4G_EDTYPE", _lib.EDTYPE), ("W4G_ELAUNCH", _lib.ELAUNCH), ("W4G_EALIAS", _lib.EALIAS),
                  ("W4G_F32", _lib.F32), ("W4G_BF16", _lib.BF16), ("W4G_OP_GEMV", _lib.OP_GEMV),
                  ("W4G_OP_GEMM", _lib.OP_GEMM), ("W4G_OP_ARGMAX", _lib.OP_ARGMAX),
-                 ("W4G_OP_GEMV_ARGMAX", _lib.OP_GEMV_ARGMAX),
+                 ("W4G_OP_GEMV_ARGMAX", _lib.OP_GEMV_ARGMAX), ("W4G_OP_ARGMAX_TOP2", _lib.OP_ARGMAX_TOP2),
                  ("W4G_GEMV_AUTO", _lib.GEMV_AUTO), ("W4G_GEMV_VALU", _lib.GEMV_VALU),
                  ("W4G_GEMV_MFMA", _lib.GEMV_MFMA), ("W4G_GEMV_VALU_REGS", _lib.GEMV_VALU_REGS)):
         assert val(k) == v, k
@@ -156,6 +157,24 @@ def test_gemv_argmax_rejects(lib):
     assert call(ids=WQ + 64) == _lib.EALIAS
     assert call(ws=Y) == _lib.EALIAS
     assert call(ids=WS) == _lib.EALIAS
+
+
+def test_top2_rejects(lib):
+    need = lib.qmm_workspace_bytes(_lib.OP_ARGMAX_TOP2, 2, 5000, 0)
+    assert need == 2 * 5 * 16
+    assert lib.qmm_workspace_bytes(_lib.OP_ARGMAX_TOP2, 2, 1, 0) == ctypes.c_size_t(-1).value
+    GP = IDS + (1 << 20)
+    call = lambda **k: lib.vocab_argmax_top2(k.get("lg", LOG), k.get("dt", _lib.F32), k.get("rows", 2),
+                                             k.get("V", 5000), k.get("ld", 5000), k.get("ids", IDS),
+                                             k.get("gp", GP), k.get("ws", WS), k.get("wsb", need), None)
+    assert call(gp=None) == _lib.EINVAL_PTR
+    assert call(dt=3) == _lib.EDTYPE
+    assert call(V=1, ld=1) == _lib.ESHAPE
+    assert call(gp=GP + 2) == _lib.EALIGN
+    assert call(ws=WS + 8) == _lib.EALIGN
+    assert call(wsb=need - 16) == _lib.EWORKSPACE
+    assert call(gp=IDS + 8) == _lib.EALIAS
+    assert call(ws=LOG) == _lib.EALIAS
 
 
 def test_workspace_sizes(lib):

@@ -17,10 +17,11 @@ import ctypes
 from . import _lib
 from ._lib import (BF16, F32, GEMV_AUTO, GEMV_MFMA, GEMV_VALU, GEMV_VALU_REGS,  # noqa: F401
                    MAX_GEMV_BATCH,
-                   OP_ARGMAX, OP_GEMM, OP_GEMV, OP_GEMV_ARGMAX, SENTINEL, W4GError)
+                   OP_ARGMAX, OP_ARGMAX_TOP2, OP_GEMM, OP_GEMV, OP_GEMV_ARGMAX, SENTINEL,
+                   W4GError)
 
-__all__ = ["qmm_gemv", "qmm_gemm", "qmm_gemv_argmax", "vocab_argmax", "workspace_bytes", "SENTINEL",
-           "W4GError"]
+__all__ = ["qmm_gemv", "qmm_gemm", "qmm_gemv_argmax", "vocab_argmax", "vocab_argmax_top2",
+           "workspace_bytes", "SENTINEL", "W4GError"]
 
 
 def _torch():
@@ -169,3 +170,28 @@ def vocab_argmax(logits, ids=None, workspace=None, vocab=None):
                               ws.data_ptr(), nbytes, _stream(logits))
     _lib.check("vocab_argmax", status)
     return ids
+
+
+def vocab_argmax_top2(logits, ids2=None, gaps=None, workspace=None, vocab=None):
+    """Winner and runner-up per row and their gap: returns (ids2 [rows][2] int32
+    holding uint32 bits, gaps [rows] fp32); a non-finite row gives the sentinel
+    twice and a NaN gap."""
+    torch = _torch()
+    _need(logits, "logits", (torch.float32, torch.bfloat16), 2, None)
+    rows, ld = logits.shape
+    vocab = ld if vocab is None else vocab
+    dtype = F32 if logits.dtype == torch.float32 else BF16
+    if ids2 is None:
+        ids2 = torch.empty((rows, 2), dtype=torch.int32, device=logits.device)
+    if gaps is None:
+        gaps = torch.empty(rows, dtype=torch.float32, device=logits.device)
+    _need(ids2, "ids2", (torch.int32, torch.uint32), 2, logits.device)
+    _need(gaps, "gaps", (torch.float32,), 1, logits.device)
+    if tuple(ids2.shape) != (rows, 2) or gaps.shape[0] != rows:
+        raise ValueError("ids2 must be [rows][2] and gaps [rows]")
+    ws, nbytes = _workspace(OP_ARGMAX_TOP2, rows, vocab, 0, logits.device, workspace)
+    lib = _lib.load()
+    status = lib.vocab_argmax_top2(logits.data_ptr(), dtype, rows, vocab, ld, ids2.data_ptr(),
+                                   gaps.data_ptr(), ws.data_ptr(), nbytes, _stream(logits))
+    _lib.check("vocab_argmax_top2", status)
+    return ids2, gaps

@@ -8,7 +8,7 @@ LIB_PATH = os.path.join(HERE, "libw4g.so")
 # status codes and constants, as in include/w4g.h
 OK, EINVAL_PTR, ESHAPE, EALIGN, EWORKSPACE, EDTYPE, ELAUNCH, EALIAS = range(8)
 F32, BF16 = 0, 1
-OP_GEMV, OP_GEMM, OP_ARGMAX, OP_GEMV_ARGMAX = 0, 1, 2, 3
+OP_GEMV, OP_GEMM, OP_ARGMAX, OP_GEMV_ARGMAX, OP_ARGMAX_TOP2 = 0, 1, 2, 3, 4
 SENTINEL = 0xFFFFFFFF
 MAX_GEMV_BATCH = 8
 ABI_VERSION = 1
@@ -45,6 +45,8 @@ def load(path=None):
     lib.qmm_gemm.restype = I
     lib.qmm_gemv_argmax.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.qmm_gemv_argmax.restype = I
+    lib.vocab_argmax_top2.argtypes = [P, I, I64, I64, I64, P, P, P, SZ, P]
+    lib.vocab_argmax_top2.restype = I
     lib.vocab_argmax.argtypes = [P, I, I64, I64, I64, P, P, SZ, P]
     lib.vocab_argmax.restype = I
     lib.qmm_workspace_bytes.argtypes = [I, I64, I64, I64]

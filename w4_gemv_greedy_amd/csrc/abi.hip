@@ -86,6 +86,9 @@ size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k) {
     case W4G_OP_ARGMAX:
       if (rows < 1 || rows > 65535 || n < 1 || n >= kMaxDim) return (size_t)-1;
       return w4g::argmax_workspace_bytes(rows, n);
+    case W4G_OP_ARGMAX_TOP2:
+      if (rows < 1 || rows > 65535 || n < 2 || n >= kMaxDim) return (size_t)-1;
+      return w4g::argmax_top2_workspace_bytes(rows, n);
     case W4G_OP_GEMV_ARGMAX:
       if (rows < 1 || rows > W4G_MAX_GEMV_BATCH || n < 1 || n >= kMaxDim || k < 64 ||
           k >= kMaxDim || k % 64)
@@ -164,6 +167,32 @@ int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
   const hipError_t e = w4g::launch_gemv_argmax(wq, scales, biases, x, logits, rec, (int)B, N, K, s);
   if (e != hipSuccess) return W4G_ELAUNCH;
   return from_hip(w4g::launch_argmax_combine(rec, B, w4g::gemv_argmax_records((int)B, N, K), ids, s));
+}
+
+int vocab_argmax_top2(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                      uint32_t* ids2, float* gaps, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!logits || !ids2 || !gaps) return W4G_EINVAL_PTR;
+  if (dtype != W4G_F32 && dtype != W4G_BF16) return W4G_EDTYPE;
+  if (rows < 1 || rows > 65535 || vocab < 2 || vocab >= kMaxDim || ld < vocab || ld >= ((int64_t)1 << 40))
+    return W4G_ESHAPE;
+  if (!aligned16(logits) || (reinterpret_cast<uintptr_t>(ids2) & 3u) ||
+      (reinterpret_cast<uintptr_t>(gaps) & 3u))
+    return W4G_EALIGN;
+  const size_t need = w4g::argmax_top2_workspace_bytes(rows, vocab);
+  if (!workspace || workspace_bytes < need) return W4G_EWORKSPACE;
+  if (!aligned16(workspace)) return W4G_EALIGN;
+  const size_t esz = dtype == W4G_F32 ? 4 : 2;
+  const size_t lbytes = ((size_t)(rows - 1) * (size_t)ld + (size_t)vocab) * esz;
+  const void* outs[3] = {ids2, gaps, workspace};
+  const size_t osz[3] = {(size_t)rows * 8, (size_t)rows * 4, need};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], osz[i], logits, lbytes)) return W4G_EALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j])) return W4G_EALIAS;
+  }
+  return from_hip(w4g::launch_argmax_top2(logits, dtype, rows, vocab, ld, ids2, gaps, workspace,
+                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
 int vocab_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,

@@ -121,7 +121,135 @@ __global__ __launch_bounds__(NT) void argmax_pass2(const uint2* __restrict__ rec
   if (threadIdx.x == 0) ids[row] = bad ? 0xFFFFFFFFu : 0xFFFFFFFFu - (uint32_t)best;
 }
 
+// ---- top two.  A pair (a, b) holds the two largest candidate words seen, a > b
+// (0 = none; candidates of distinct ids never tie).  A row's non-finite value
+// sets its pass-1 record's a to ~0, which no finite candidate reaches.
+
+__device__ __forceinline__ void top2_push(uint64_t& a, uint64_t& b, uint64_t c) {
+  if (c > a) {
+    b = a;
+    a = c;
+  } else if (c > b) {
+    b = c;
+  }
+}
+// (a, b) <- the top two of {a, b, c, d}, given a >= b and c >= d
+__device__ __forceinline__ void top2_merge(uint64_t& a, uint64_t& b, uint64_t c, uint64_t d) {
+  const uint64_t lo = a > c ? c : a;
+  a = umax64(a, c);
+  b = umax64(lo, umax64(b, d));
+}
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int off) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)(v >> 32), off);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Block-wide top two of (a, b) and the non-finite flag; the result in every thread.
+__device__ __forceinline__ void block_top2(uint64_t& a, uint64_t& b, bool& bad) {
+  __shared__ uint64_t s_a[kThreads / 64], s_b[kThreads / 64];
+  __shared__ int s_bad[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t c = shfl_xor64(a, off), d = shfl_xor64(b, off);
+    top2_merge(a, b, c, d);
+  }
+  const bool any_bad = __any(bad);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_a[wave] = a;
+    s_b[wave] = b;
+    s_bad[wave] = any_bad ? 1 : 0;
+  }
+  __syncthreads();
+  a = s_a[0];
+  b = s_b[0];
+  int f = s_bad[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) {
+    top2_merge(a, b, s_a[w], s_b[w]);
+    f |= s_bad[w];
+  }
+  bad = f != 0;
+}
+
+// pass 1: one block of 1024 ids per workgroup -> record (a, b) as four words
+template <int DT>
+__global__ __launch_bounds__(kThreads) void top2_pass1(const void* __restrict__ logits, int64_t ld,
+                                                       int64_t vocab, int nblk,
+                                                       uint4* __restrict__ rec) {
+  const int64_t row = blockIdx.y;
+  const int64_t blk = blockIdx.x;
+  const int64_t i0 = blk * kArgmaxBlock + (int64_t)threadIdx.x * 4;
+  const int64_t base = row * ld;
+  uint64_t a = 0, b = 0;
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (i0 + j < vocab) {
+      const uint32_t u = elem_bits<DT>(logits, base + i0 + j);
+      if (!finite_bits(u)) bad = true;
+      else top2_push(a, b, cand(u, (uint32_t)(i0 + j)));
+    }
+  }
+  block_top2(a, b, bad);
+  if (threadIdx.x == 0) {
+    if (bad) {
+      a = ~0ull;
+      b = 0;
+    }
+    rec[row * nblk + blk] = make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+  }
+}
+
+// pass 2: one workgroup per row combines the row's records
+__global__ __launch_bounds__(kThreads) void top2_pass2(const uint4* __restrict__ rec, int64_t nblk,
+                                                       uint32_t* __restrict__ ids2,
+                                                       float* __restrict__ gaps) {
+  const int64_t row = blockIdx.x;
+  uint64_t a = 0, b = 0;
+  bool bad = false;
+  for (int64_t i = threadIdx.x; i < nblk; i += kThreads) {
+    const uint4 r = rec[row * nblk + i];
+    const uint64_t ra = ((uint64_t)r.y << 32) | r.x, rb = ((uint64_t)r.w << 32) | r.z;
+    if (ra == ~0ull) bad = true;
+    else top2_merge(a, b, ra, rb);
+  }
+  block_top2(a, b, bad);
+  if (threadIdx.x == 0) {
+    if (bad) {
+      ids2[2 * row] = ids2[2 * row + 1] = 0xFFFFFFFFu;
+      gaps[row] = __uint_as_float(0x7FC00000u);
+    } else {
+      ids2[2 * row] = 0xFFFFFFFFu - (uint32_t)a;
+      ids2[2 * row + 1] = 0xFFFFFFFFu - (uint32_t)b;
+      // key_bits gives +0.0 for either zero, so the gap is never -0.0
+      gaps[row] = __uint_as_float(key_bits((uint32_t)(a >> 32))) -
+                  __uint_as_float(key_bits((uint32_t)(b >> 32)));
+    }
+  }
+}
+
 }  // namespace
+
+size_t argmax_top2_workspace_bytes(int64_t rows, int64_t vocab) {
+  const int64_t nblk = (vocab + kArgmaxBlock - 1) / kArgmaxBlock;
+  return (size_t)(rows * nblk) * sizeof(uint4);
+}
+
+hipError_t launch_argmax_top2(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                              uint32_t* ids2, float* gaps, void* workspace, hipStream_t stream) {
+  const int nblk = (int)((vocab + kArgmaxBlock - 1) / kArgmaxBlock);
+  uint4* rec = reinterpret_cast<uint4*>(workspace);
+  const dim3 g1((unsigned)nblk, (unsigned)rows);
+  if (dtype == 0)
+    hipLaunchKernelGGL(top2_pass1<0>, g1, dim3(kThreads), 0, stream, logits, ld, vocab, nblk, rec);
+  else
+    hipLaunchKernelGGL(top2_pass1<1>, g1, dim3(kThreads), 0, stream, logits, ld, vocab, nblk, rec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(top2_pass2, dim3((unsigned)rows), dim3(kThreads), 0, stream, rec, (int64_t)nblk,
+                     ids2, gaps);
+  return hipGetLastError();
+}
 
 size_t argmax_workspace_bytes(int64_t rows, int64_t vocab) {
   const int64_t nblk = (vocab + kArgmaxBlock - 1) / kArgmaxBlock;

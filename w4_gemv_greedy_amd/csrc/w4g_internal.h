@@ -32,6 +32,10 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                          uint32_t* ids, void* workspace, hipStream_t stream);
 size_t argmax_workspace_bytes(int64_t rows, int64_t vocab);
+// Top two per row: ids2[r][0..1] (winner, runner-up) and gaps[r].
+hipError_t launch_argmax_top2(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                              uint32_t* ids2, float* gaps, void* workspace, hipStream_t stream);
+size_t argmax_top2_workspace_bytes(int64_t rows, int64_t vocab);
 // Pass 2 alone: combines `nrec` (value, id | flag) records per row into ids.
 hipError_t launch_argmax_combine(const uint2* rec, int64_t rows, int64_t nrec, uint32_t* ids,
                                  hipStream_t stream);
