@@ -119,7 +119,7 @@ int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
 /*
  * qmm_gemv with an explicit kernel family.  Same arguments and results as
  * qmm_gemv; `kernel` is one of W4G_GEMV_*, else W4G_EDTYPE.  The vector-ALU
- * family stages x in LDS when B * 2.125 * K bytes fit in 64 KiB and in
+ * family stages x in LDS when B * 2.125 * K bytes fit in 152 KiB and in
  * registers otherwise; W4G_GEMV_VALU_REGS forces the register variant (for
  * checking that both variants give the same bits).
  * The matrix-core family (W4G_GEMV_MFMA) feeds the codes to
