@@ -536,4 +536,14 @@ hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const 
   return dispatch<true>(wq, scales, biases, x, y, rec, B, N, K, false, stream);
 }
 
+// Measured: the vector ALUs keep up to B = 4 on every decode shape, and to
+// B = 6 while x fits in LDS; past that (x staged in registers, or B >= 7) the
+// matrix cores are faster.
+int gemv_auto_family(int B, int64_t N, int64_t K) {
+  (void)N;
+  if (B <= 4) return 1;
+  if (B <= 6 && !use_regs(B, K, false)) return 1;
+  return 2;
+}
+
 }  // namespace w4g

@@ -69,17 +69,26 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int t) {
   return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
 }
 
-// Codes, scales and biases of one stage of one wave: GPS groups.
-template <int GPS>
+// Codes, scales and biases of one stage of one wave.  VEC: the scales and
+// biases come as one 16-byte vector per lane (lane (h, n): groups 8h .. 8h + 7
+// of the stage for row n; a 2-byte load per group and row would cost an L1
+// tag lookup per lane), else one 2-byte load per group.
+template <int GPS, bool VEC>
 struct Ring {
   uint4 c[GPS];
-  uint32_t s[GPS], b[GPS];
+  uint32_t s[VEC ? 1 : GPS], b[VEC ? 1 : GPS];
+  uint4 sv, bv;
 };
+
+__device__ __forceinline__ uint32_t bf16_at(const uint4& v, int i) {
+  const uint32_t w = i >> 1 == 0 ? v.x : i >> 1 == 1 ? v.y : i >> 1 == 2 ? v.z : v.w;
+  return (w >> ((i & 1) * 16)) & 0xFFFFu;
+}
 
 // The workgroup's four waves split the K groups round robin; each stage of 16
 // groups gives every wave GPS = 16 / W of them.  The activations of a stage are
 // staged in one of two LDS buffers while the other feeds the matrix cores.
-template <int W>
+template <int W, bool VEC>
 __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __restrict__ wq,
                                                            const uint16_t* __restrict__ scales,
                                                            const uint16_t* __restrict__ biases,
@@ -110,14 +119,22 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
 
   // codes of stage st for this wave (groups past the end reread the row's last
   // group, a cache hit, so no other rows are pulled in)
-  auto issue = [&](Ring<GPS>& r, int st) {
+  auto issue = [&](Ring<GPS, VEC>& r, int st) {
 #pragma unroll
     for (int j = 0; j < GPS; ++j) {
       int64_t g = (int64_t)st * kStageGroups + wave + W * j;
       g = g < G ? g : G - 1;
       r.c[j] = *reinterpret_cast<const uint4*>(wrow + g * 8 + h * 4);
-      r.s[j] = srow[g];
-      r.b[j] = brow[g];
+      if constexpr (!VEC) {
+        r.s[j] = srow[g];
+        r.b[j] = brow[g];
+      }
+    }
+    if constexpr (VEC) {  // G % 8 == 0: clamp the block start to the row's last 8 groups
+      int64_t g8 = (int64_t)st * kStageGroups + 8 * h;
+      g8 = g8 <= G - 8 ? g8 : G - 8;
+      r.sv = *reinterpret_cast<const uint4*>(srow + g8);
+      r.bv = *reinterpret_cast<const uint4*>(brow + g8);
     }
   };
 
@@ -151,7 +168,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
   // by side (instruction t of every group, then t + 1), so the chains overlap;
   // each group's partial is still its own, and the groups are added to the
   // running sums in ascending order.
-  auto compute = [&](const Ring<GPS>& r, int st, int buf) {
+  auto compute = [&](const Ring<GPS, VEC>& r, int st, int buf) {
     f32x16_t p[GPS];
     bf16x8_t bop[GPS][4];
     uint4 av[GPS][4];
@@ -176,8 +193,19 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
     for (int j = 0; j < GPS; ++j) {
       const int gl = wave + W * j;
       if ((int64_t)st * kStageGroups + gl < G) {
-        const float sc = bf16_to_f32(r.s[j]);
-        const float cb = __builtin_fmaf(-128.0f, sc, bf16_to_f32(r.b[j]));
+        uint32_t sbits, bbits;
+        if constexpr (VEC) {
+          // this lane's vector holds the group when gl / 8 == h, else its partner's does
+          const uint32_t so = bf16_at(r.sv, gl & 7), bo = bf16_at(r.bv, gl & 7);
+          const uint32_t sp = __shfl_xor(so, 32), bp = __shfl_xor(bo, 32);
+          sbits = (gl >> 3) == h ? so : sp;
+          bbits = (gl >> 3) == h ? bo : bp;
+        } else {
+          sbits = r.s[j];
+          bbits = r.b[j];
+        }
+        const float sc = bf16_to_f32(sbits);
+        const float cb = __builtin_fmaf(-128.0f, sc, bf16_to_f32(bbits));
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           tot[v] = __builtin_fmaf(sc, p[j][v], tot[v]);
@@ -194,7 +222,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
   // Per half step: activations of stage st + 2 load first, then its codes, so
   // the wait for stage st + 1's activations (issued a half step earlier) does
   // not also wait for codes that are only needed later.
-  Ring<GPS> ra, rb;
+  Ring<GPS, VEC> ra, rb;
   load_x(0);
   issue(ra, 0);
   store_x(0);
@@ -236,8 +264,14 @@ hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const ui
                             const uint16_t* x, float* y, int B, int64_t N, int64_t K,
                             hipStream_t stream) {
   const int64_t blocks = (N + 31) / 32;
-  hipLaunchKernelGGL(gemv_mfma_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, wq, scales,
-                     biases, x, y, B, N, K);
+  const bool vec = ((K >> 6) % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
+                                             reinterpret_cast<uintptr_t>(biases)) & 15u) == 0;
+  if (vec)
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, true>), dim3((unsigned)blocks), dim3(256), 0, stream, wq,
+                       scales, biases, x, y, B, N, K);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, false>), dim3((unsigned)blocks), dim3(256), 0, stream, wq,
+                       scales, biases, x, y, B, N, K);
   return hipGetLastError();
 }
 

@@ -23,11 +23,7 @@ hipError_t launch_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_
                        void* workspace, hipStream_t stream);
 // Kernel family qmm_gemv runs for a shape (1 = vector ALU, 2 = matrix cores);
 // a function of (B, N, K) only.
-inline int gemv_auto_family(int B, int64_t N, int64_t K) {
-  (void)N;
-  (void)K;
-  return B >= 5 ? 2 : 1;  // measured: the vector ALUs keep up to B = 4
-}
+int gemv_auto_family(int B, int64_t N, int64_t K);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                          uint32_t* ids, void* workspace, hipStream_t stream);
