@@ -12,8 +12,8 @@ Printed: one JSON line.  `value` is the algorithmic bytes of a step
 (0.5625*N*K + 2*B*K + 4*B*N per product, 4*B*V for the argmax) over the
 measured step time, in GB/s.  The line also carries the roofline of the
 dominant kernel (the gate-up product), the oracle timed on the host cores, and
-secondary figures: lm_head+argmax microseconds per token, the 512-row prompt
-products in TFLOP/s, and the batch-8 sweep.
+secondary figures: lm_head+argmax microseconds per token, the prompt products
+at 512, 128, 64 and 16 rows (fp32 and, at 128, bf16 store), and the batch-8 sweep.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--batch 1]
 """
@@ -377,25 +377,34 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args):
     log("per-product: " + ", ".join(f"{k} {v['us']}us {v['GBps']}GB/s" for k, v in ex.items()
                                     if k.startswith("gemv_")))
 
-    # prompt products, M = 512
-    pr = {}
-    for name, idx, N, K, mid in (("o_proj", 0, HIDDEN, HIDDEN, synth.O_PROJ),
-                                 ("gate_up", 1, 2 * INTER, HIDDEN, synth.GATE_UP),
-                                 ("down", 2, HIDDEN, INTER, synth.DOWN)):
-        M = 512
-        x = make_x(M, K, 4, mid, 0, dev)
-        y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(1, w4g.workspace_bytes(w4g.OP_GEMM, M, N, K)), dtype=torch.uint8, device=dev)
-        m = layers[0][idx]
+    # prompt products: the 512-row pass, the 128-row round and short prompts of 64
+    # and 16 rows (where the weight stream, not the matrix cores, sets the time).
+    # Each timed call walks the 16 layers' weights, so no call finds its matrix in
+    # the 256 MB cache; the 128-row round is also timed with the bf16 store.
+    for M in (512, 128, 64, 16):
+        pr = {}
+        for name, idx, N, K, mid in (("o_proj", 0, HIDDEN, HIDDEN, synth.O_PROJ),
+                                     ("gate_up", 1, 2 * INTER, HIDDEN, synth.GATE_UP),
+                                     ("down", 2, HIDDEN, INTER, synth.DOWN)):
+            x = make_x(M, K, 4, mid, 0, dev)
+            ws = torch.empty(max(1, w4g.workspace_bytes(w4g.OP_GEMM, M, N, K)), dtype=torch.uint8, device=dev)
+            for dt in ((torch.float32, torch.bfloat16) if M == 128 else (torch.float32,)):
+                y = torch.empty((M, N), dtype=dt, device=dev)
 
-        def run(m=m, x=x, y=y, ws=ws):
-            w4g.qmm_gemm(m.wq, m.sc, m.bi, x, y, ws)
-        ms, _ = timed(run, 10, 2, True)
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        pr[name] = {"us": round(ms * 1e3, 1), "TFLOPS": round(tf, 1),
-                    "pct_mfma_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1)}
-    ex["prompt_gemm_m512"] = pr
-    log("prompt: " + ", ".join(f"{k} {v['us']}us {v['TFLOPS']}TF" for k, v in pr.items()))
+                def run(idx=idx, x=x, y=y, ws=ws):
+                    for lay in layers:
+                        m = lay[idx]
+                        w4g.qmm_gemm(m.wq, m.sc, m.bi, x, y, ws)
+                ms, _ = timed(run, 3 if M == 512 else 10, 1, True)
+                us = ms * 1e3 / len(layers)
+                tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+                gbs = (0.5625 * N * K + 2.0 * M * K + y.element_size() * M * N) / (us * 1e-6) / 1e9
+                pr[name + ("" if dt == torch.float32 else "_bf16out")] = {
+                    "us": round(us, 1), "TFLOPS": round(tf, 1),
+                    "pct_mfma_peak": round(100 * tf / BF16_PEAK_TFLOPS, 1), "GBps": round(gbs, 1)}
+        ex[f"prompt_gemm_m{M}"] = pr
+        log(f"prompt M={M}: " + ", ".join(f"{k} {v['us']}us {v['TFLOPS']}TF {v['GBps']}GB/s"
+                                          for k, v in pr.items()))
 
     # the batch-8 sweep
     if args.batch != 8:

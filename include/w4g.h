@@ -33,7 +33,7 @@
  *   scales  [N][K/64] bf16 (passed as uint16 bit patterns).
  *   biases  [N][K/64] bf16.
  *   x       [B][K] or [M][K] bf16.
- *   y       [B][N] or [M][N] fp32.
+ *   y       [B][N] or [M][N] fp32 (qmm_gemm_ex: fp32 or bf16).
  *   logits  [rows][ld] fp32 or bf16; row r occupies elements [r*ld, r*ld+vocab).
  *   ids     [rows] uint32.
  *
@@ -150,6 +150,22 @@ int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* bias
 int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
              const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qmm_gemm with a choice of output dtype.
+ *   y_dtype: W4G_F32 (y is float [M][N], exactly qmm_gemm) or W4G_BF16 (y is
+ *   bf16 [M][N], passed as uint16 bit patterns); anything else is W4G_EDTYPE.
+ *   y must be 16-byte aligned either way.
+ * The bf16 store rounds the fp32 result that qmm_gemm would have stored to
+ * nearest-even (a NaN stays a quiet NaN of its sign; a finite value beyond
+ * the bf16 range becomes +-Inf, as that rounding gives).  The pages' kernel
+ * has a store in the activation dtype, to which TensorFold PR #1437 (commit
+ * "Add the pair seam and register its kernels with the kernel contract") adds
+ * the fp32-out variant; reading: that original store is bf16.
+ */
+int qmm_gemm_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                const uint16_t* x, void* y, int64_t M, int64_t N, int64_t K,
+                void* workspace, size_t workspace_bytes, void* stream, int y_dtype);
 
 /*
  * Greedy argmax of `rows` logit rows of `vocab` entries (row pitch `ld`).

@@ -12,7 +12,9 @@ Definitions followed (see the C file for the full statement and citations):
   * products: fp32 result of sum_k x*w (TensorFold PR #1437, commit "Add the
     pair seam ...": fp32 payload and fp32-out store), summed in fp64;
   * argmax: any non-finite value in a row gives 0xFFFFFFFF, else the largest
-    value with ties to the lowest id (TensorFold PR #1433, step-1 description).
+    value with ties to the lowest id (TensorFold PR #1433, step-1 description);
+  * bf16 store: fp32 result rounded to bf16 nearest-even, NaN kept (reading of
+    the pages' activation-dtype store beside the fp32-out variant).
 """
 import ctypes
 import os
@@ -56,6 +58,8 @@ def load(path=None):
     lib.w4o_argmax.restype = I
     lib.w4o_argmax_top2.argtypes = [P, I, I64, I64, I64, P, P, P]
     lib.w4o_argmax_top2.restype = I
+    lib.w4o_to_bf16.argtypes = [P, P, I64]
+    lib.w4o_to_bf16.restype = None
     lib.w4o_plant.restype = I
     lib.w4o_threads.restype = I
     _libs[path] = lib
@@ -163,6 +167,15 @@ def argmax_top2(logits, lib=None):
     if rc:
         raise ValueError(f"oracle top-2 rejected its arguments ({rc})")
     return ids, gaps
+
+
+def to_bf16(y, lib=None):
+    """bf16 bits (uint16, same shape) of fp32 values rounded to nearest-even."""
+    lib = lib or load()
+    y = _c(np.asarray(y, np.float32), np.float32)
+    out = np.empty(y.shape, np.uint16)
+    lib.w4o_to_bf16(_ptr(y), _ptr(out), y.size)
+    return out
 
 
 def threads(lib=None):

@@ -47,6 +47,15 @@
  *    session merges "the top two" across blocks for its tie test, TensorFold
  *    PR #1433, step-1 description; the pages fix no format for it.)
  *
+ *  - bf16 store: a product's fp32 result rounded to bf16 to nearest, ties to
+ *    the even last bit (8 significant bits, the fp32 exponent range; a value
+ *    at or beyond the midpoint between the largest bf16 and 2^128 becomes
+ *    infinity); a NaN stays a quiet NaN of its sign.  (Reading: the pages'
+ *    kernel stores in the activation dtype, and TensorFold PR #1437, commit
+ *    "Add the pair seam and register its kernels with the kernel contract",
+ *    adds the fp32-out variant beside it; the pages name no rounding, and
+ *    nearest-even is the IEEE default.)
+ *
  * Parallelism: optional OpenMP over independent output elements only.  Every
  * single dot product is computed by one thread in ascending k, so the result
  * does not depend on the thread count.
@@ -69,7 +78,8 @@
    4 tie to the higher id, 5 no non-finite flag, 6 bias sign flipped,
    7 scale/bias tables read as [G][N], 8 -0.0 ordered below +0.0,
    9 fp32 accumulation, 10 activation row picked by the output row's stride,
-   11 last K group dropped, 12 runner-up tie to the higher id */
+   11 last K group dropped, 12 runner-up tie to the higher id,
+   13 bf16 store ties rounded away from zero */
 
 /* bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits. */
 static float o_bf16_to_f32(uint16_t h) {
@@ -281,6 +291,48 @@ int w4o_argmax(const void* logits, int dtype, int64_t rows, int64_t V, int64_t l
     }
   }
   return 0;
+}
+
+/* fp32 value of fp32 bit pattern u */
+static double o_f32_bits(uint32_t u) {
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* One fp32 value to bf16 bits, nearest-even.  The two candidates are the bf16
+   magnitudes just below and just above |f| (the fp32 bits with the low 16 bits
+   cleared, and the next bf16 up, 2^128 standing in for infinity); the nearer
+   one wins, a tie goes to the one whose last bit is 0.  The distances are
+   exact in double. */
+static uint16_t o_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040u);
+  const uint32_t sign = u & 0x80000000u, mag = u & 0x7FFFFFFFu;
+  const uint32_t lo = mag & 0xFFFF0000u;
+  if (lo == mag) return (uint16_t)((sign | mag) >> 16); /* already a bf16 value (0, inf too) */
+  const uint32_t hi = lo + 0x00010000u;
+  const double v = o_f32_bits(mag);
+  const double dlo = v - o_f32_bits(lo);
+  const double dhi = (hi == 0x7F800000u ? ldexp(1.0, 128) : o_f32_bits(hi)) - v;
+  uint32_t pick;
+  if (dlo < dhi)
+    pick = lo;
+  else if (dhi < dlo)
+    pick = hi;
+  else
+#if W4O_PLANT == 13
+    pick = hi;
+#else
+    pick = ((lo >> 16) & 1u) ? hi : lo;
+#endif
+  return (uint16_t)((sign | pick) >> 16);
+}
+
+/* bf16 store of n fp32 values. */
+void w4o_to_bf16(const float* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = o_to_bf16(in[i]);
 }
 
 int w4o_plant(void) { return W4O_PLANT; }

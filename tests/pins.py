@@ -14,7 +14,8 @@ What fixes the expected values (never the oracle itself, never the GPU):
   * numpy's float64 dot on the dequantized matrix (library routine);
   * invariants: row permutation, power-of-two scaling, negation;
   * argmax: hand-built rows for each rule and numpy's argmax (first
-    occurrence) on finite rows.
+    occurrence) on finite rows;
+  * bf16 store: hand-worked roundings and torch's CPU bfloat16 conversion.
 """
 import json
 import os
@@ -325,8 +326,46 @@ def pin_top2_rules(lib):
     assert np.all(ids == SENTINEL) and np.all(np.isnan(gaps))
 
 
+def pin_bf16_store(lib):
+    """bf16 store: hand-worked roundings (ties to even, overflow to infinity, signed
+    zero, denormals, NaN kept) and torch's CPU fp32 -> bfloat16 conversion (a
+    nearest-even library routine) on random values, exact midpoints and
+    specials."""
+    import torch
+
+    def b(v):
+        return int(oracle.to_bf16(np.array([v], np.float32), lib=lib)[0])
+    assert b(1.0) == 0x3F80
+    assert b(1.0 + 2.0 ** -8) == 0x3F80            # midpoint of 0x3F80 and 0x3F81: to even
+    assert b(1.0 + 3 * 2.0 ** -8) == 0x3F82        # midpoint of 0x3F81 and 0x3F82: to even
+    assert b(1.0 + 2.0 ** -8 + 2.0 ** -20) == 0x3F81  # just past the midpoint
+    assert b(-(1.0 + 2.0 ** -8)) == 0xBF80
+    assert b(-0.0) == 0x8000 and b(0.0) == 0x0000
+    assert b((2 - 2.0 ** -8) * 2.0 ** 127) == 0x7F80   # midpoint of the largest bf16 and 2^128
+    assert b((2 - 2.0 ** -7) * 2.0 ** 127) == 0x7F7F
+    assert b(2.0 ** -149) == 0x0000                # below half the least bf16 denormal
+    assert b(3 * 2.0 ** -134) == 0x0002            # 1.5 least denormals: tie to even (2)
+    assert b(float("inf")) == 0x7F80 and b(float("-inf")) == 0xFF80
+    nan = oracle.to_bf16(np.array([np.nan, -np.nan], np.float32), lib=lib)
+    assert np.all((nan & 0x7F80) == 0x7F80) and np.all((nan & 0x7F) != 0)
+    assert (int(nan[1]) >> 15) == (int(np.array([-np.nan], np.float32).view(np.uint32)[0]) >> 31)
+    r = np.random.default_rng(31)
+    v = (r.standard_normal(60000) * np.exp2(r.integers(-140, 120, 60000))).astype(np.float32)
+    u = r.integers(0, 1 << 32, 20000, dtype=np.uint64).astype(np.uint32)
+    mids = ((u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)   # exact midpoints
+    mids = mids[np.isfinite(mids)]
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 3.4028235e38, -3.4028235e38, 1e-45, -1e-45,
+                        1.1754944e-38, 2.0 ** -133, 2.0 ** -134, 65504.0], np.float32)
+    allv = np.concatenate([v, mids, special]).astype(np.float32)
+    want = torch.from_numpy(allv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.to_bf16(allv, lib=lib)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(allv[i], hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
 PRODUCT_PINS = [pin_hand_dequant, pin_closed_form, pin_integer_matvec, pin_scale_bias_layout,
-                pin_bruteforce, pin_numpy_dot, pin_dequant_bits, pin_invariants, pin_rows_subset]
+                pin_bruteforce, pin_numpy_dot, pin_dequant_bits, pin_invariants, pin_rows_subset,
+                pin_bf16_store]
 ARGMAX_PINS = [pin_argmax_rules, pin_argmax_numpy, pin_argmax_bf16_nonfinite, pin_top2_rules,
                pin_top2_lexsort]
 ALL_PINS = PRODUCT_PINS + ARGMAX_PINS

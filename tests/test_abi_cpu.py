@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert set(names) >= {"qmm_gemv", "qmm_gemv_ex", "qmm_gemm", "qmm_gemv_argmax", "vocab_argmax",
+    assert set(names) >= {"qmm_gemv", "qmm_gemv_ex", "qmm_gemm", "qmm_gemm_ex", "qmm_gemv_argmax", "vocab_argmax",
                           "vocab_argmax_top2",
                           "qmm_workspace_bytes", "w4g_status_string", "w4g_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -111,6 +111,14 @@ def test_gemm_rejects(lib):
     assert call(ws=WS + 8) == _lib.EALIGN
     assert call(ws=X) == _lib.EALIAS
     assert call(y=WS) == _lib.EALIAS
+    ex = lambda **k: lib.qmm_gemm_ex(WQ, SC, BI, X, k.get("y", Y), 16, 64, 128, WS, need, None,
+                                     k.get("dt", _lib.BF16))
+    assert ex(dt=2) == _lib.EDTYPE
+    assert ex(dt=-1) == _lib.EDTYPE
+    assert ex(y=None) == _lib.EINVAL_PTR
+    assert ex(y=Y + 2) == _lib.EALIGN
+    assert ex(y=WS) == _lib.EALIAS
+    assert ex(y=X + 16 * 128 * 2 - 16) == _lib.EALIAS   # the last bytes of x
 
 
 def test_argmax_rejects(lib):

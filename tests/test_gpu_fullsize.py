@@ -52,16 +52,28 @@ def test_gemv_full_shape(name, B, family):
 
 @pytest.mark.parametrize("name", ["o_proj", "gate_up", "down"])
 def test_gemm_prompt_full_shape(name):
+    """M = 512 against the oracle on sampled columns; then the shorter prompts the
+    benchmark times (128, 64, 16 rows: other tile variants) must reproduce the
+    first rows bit for bit, and the bf16 store at 128 rows must be the
+    nearest-even rounding of the fp32 result."""
+    import torch
     wq, sc, bi, W = _weights(name)
     N, K, mid = SHAPES[name]
     M = 512
     x = synth.activations(M, K, workload=4, matrix=mid, layer=0)
-    y = down(w4g.qmm_gemm(*W, up_bf16(x)))
+    X = up_bf16(x)
+    y = down(w4g.qmm_gemm(*W, X))
     cols = np.unique(np.concatenate([np.arange(32), np.arange(N - 32, N),
                                      np.random.default_rng(1).choice(N, 64, replace=False)]))
     ref = oracle.qmm_rows(wq, sc, bi, x, cols)
     e = assert_close(y[:, cols], ref, f"prompt {name}")
     print(f"prompt {name} M=512: normwise {e:.2e} over {cols.size} sampled columns x 512 rows")
+    for m in (128, 64, 16):
+        ym = down(w4g.qmm_gemm(*W, X[:m].contiguous()))
+        assert np.array_equal(ym.view(np.uint32), y[:m].view(np.uint32)), f"prompt {name} M={m}"
+    yb = w4g.qmm_gemm(*W, X[:128].contiguous(), out_dtype=torch.bfloat16)
+    want = torch.from_numpy(y[:128]).to(torch.bfloat16)
+    assert torch.equal(yb.cpu().view(torch.int16), want.view(torch.int16)), f"prompt {name} bf16 store"
 
 
 def test_lm_head_argmax_end_to_end():

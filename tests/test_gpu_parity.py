@@ -136,6 +136,68 @@ def test_gemm_kernels_agree_bitwise(M, N, K):
     assert_close(y_lds, oracle.qmm(wq, sc, bi, x), f"gemm M={M} N={N} K={K}")
 
 
+def test_gemm_tile_variants_bitwise():
+    """The three main loops (register-staged 128 x 128 tiles from 512 tiles up,
+    LDS-load 128 x 128 from 256, LDS-load 64 x 64 below) follow one order: the
+    rows they share are bitwise equal, and sampled columns match the oracle."""
+    N, K = 8155, 256                      # 64 column tiles of 128, the last ragged
+    wq, sc, bi, x = _case(N, K, 1000, 77)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    X = up_bf16(x)
+    y_reg = down(w4g.qmm_gemm(*W, X))                         # 8 x 64 = 512 tiles
+    y_lds = down(w4g.qmm_gemm(*W, X[:500].contiguous()))      # 4 x 64 = 256 tiles
+    y_small = down(w4g.qmm_gemm(*W, X[:100].contiguous()))    # 64 x 64 tiles
+    assert np.array_equal(y_lds.view(np.uint32), y_reg[:500].view(np.uint32))
+    assert np.array_equal(y_small.view(np.uint32), y_reg[:100].view(np.uint32))
+    cols = np.unique(np.concatenate([np.arange(40), np.arange(N - 40, N),
+                                     np.random.default_rng(5).choice(N, 60, replace=False)]))
+    assert_close(y_reg[:, cols], oracle.qmm_rows(wq, sc, bi, x, cols), "gemm tile variants")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 37, 64), (7, 130, 1088), (130, 256, 1024), (33, 70, 17408),
+                                   (500, 1100, 512)])
+def test_gemm_bf16_store(M, N, K):
+    """bf16 output: the fp32 result (itself held to the 2e-3 bar elsewhere) rounded
+    to nearest-even, bit for bit as torch's CPU conversion of the fp32 output
+    rounds it, and within one bf16 step of the oracle's rounded result away
+    from zero.  The
+    normwise error then stays below bf16's own unit roundoff 2^-8 plus the fp32
+    error; 2^-8 exceeds 2e-3, so the fp32 bar cannot apply to a bf16 store."""
+    import torch
+    wq, sc, bi, x = _case(N, K, M, 5 * M + N)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    X = up_bf16(x)
+    y32 = down(w4g.qmm_gemm(*W, X))
+    yb_t = w4g.qmm_gemm(*W, X, out_dtype=torch.bfloat16)
+    assert yb_t.dtype == torch.bfloat16
+    yb = down(yb_t.view(torch.int16)).view(np.uint16)
+    want = torch.from_numpy(y32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(yb, want), "bf16 store is not the rounding of the fp32 result"
+    ref = oracle.qmm(wq, sc, bi, x)
+    rb = oracle.to_bf16(ref)
+    # one bf16 step apart at most, away from zero (near zero the fp32 error of
+    # the sum, not the store, sets the distance, and signs may differ)
+    step = np.abs(yb.astype(np.int32) - rb.astype(np.int32))
+    away = np.abs(ref) > 1e-3 * np.max(np.abs(ref), axis=1, keepdims=True)
+    assert np.all(step[away] <= 1), int(np.max(step[away]))
+    yf = (yb.astype(np.uint32) << 16).view(np.float32)
+    bound = 2.0 ** -8 + 2e-5
+    assert_close(yf, ref, f"gemm bf16 M={M} N={N} K={K}", tol=bound, tight=bound)
+
+
+def test_gemm_bf16_store_nan():
+    """A NaN activation makes its whole output row NaN in both stores."""
+    import torch
+    wq, sc, bi, x = _case(96, 1024, 6, 4)
+    x = x.copy()
+    x[2, 700] = 0x7FC0
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y32 = down(w4g.qmm_gemm(*W, up_bf16(x)))
+    yb = down(w4g.qmm_gemm(*W, up_bf16(x), out_dtype=torch.bfloat16).float())
+    assert np.all(np.isnan(y32[2])) and np.all(np.isnan(yb[2]))
+    assert np.all(np.isfinite(np.delete(y32, 2, axis=0))) and np.all(np.isfinite(np.delete(yb, 2, axis=0)))
+
+
 def _argmax_gpu(logits_np, bf16=False):
     t = up_bf16(logits_np) if bf16 else up_f32(logits_np)
     return ids_down(w4g.vocab_argmax(t))

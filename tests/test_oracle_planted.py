@@ -25,6 +25,7 @@ PLANTS = {
     10: "activation row stride taken from N",
     11: "last K group dropped",
     12: "runner-up tie to the higher id",
+    13: "bf16 store ties away from zero",
 }
 
 

@@ -82,13 +82,14 @@ def _workspace(op, rows, n, k, device, workspace):
     return workspace, need
 
 
-def _call_qmm(fn, op, wq, scales, biases, x, y, workspace, extra=()):
+def _call_qmm(fn, op, wq, scales, biases, x, y, workspace, extra=(), y_dtypes=None):
     torch = _torch()
     N, K = _check_qmm(wq, scales, biases, x)
     rows = x.shape[0]
+    y_dtypes = y_dtypes or (torch.float32,)
     if y is None:
-        y = torch.empty((rows, N), dtype=torch.float32, device=wq.device)
-    _need(y, "y", (torch.float32,), 2, wq.device)
+        y = torch.empty((rows, N), dtype=y_dtypes[0], device=wq.device)
+    _need(y, "y", y_dtypes, 2, wq.device)
     if tuple(y.shape) != (rows, N):
         raise ValueError(f"y must be [{rows}][{N}]")
     ws, nbytes = _workspace(op, rows, N, K, wq.device, workspace)
@@ -113,9 +114,21 @@ def qmm_gemv(wq, scales, biases, x, y=None, workspace=None, kernel=GEMV_AUTO):
     return _call_qmm("qmm_gemv_ex", OP_GEMV, wq, scales, biases, x, y, workspace, (int(kernel),))
 
 
-def qmm_gemm(wq, scales, biases, x, y=None, workspace=None):
-    """Prompt product for any M >= 1 rows of x (matrix cores); returns y [M][N] fp32."""
-    return _call_qmm("qmm_gemm", OP_GEMM, wq, scales, biases, x, y, workspace)
+def qmm_gemm(wq, scales, biases, x, y=None, workspace=None, out_dtype=None):
+    """Prompt product for any M >= 1 rows of x (matrix cores); returns y [M][N].
+
+    out_dtype: torch.float32 (the default) or torch.bfloat16, the fp32 result
+    rounded to nearest-even in the kernel's store.  A given y sets the dtype.
+    """
+    torch = _torch()
+    if out_dtype is None:
+        out_dtype = y.dtype if y is not None else torch.float32
+    if out_dtype == torch.float32:
+        return _call_qmm("qmm_gemm", OP_GEMM, wq, scales, biases, x, y, workspace)
+    if out_dtype != torch.bfloat16:
+        raise TypeError(f"out_dtype must be float32 or bfloat16, not {out_dtype}")
+    return _call_qmm("qmm_gemm_ex", OP_GEMM, wq, scales, biases, x, y, workspace, (BF16,),
+                     y_dtypes=(torch.bfloat16,))
 
 
 def qmm_gemv_argmax(wq, scales, biases, x, logits=None, ids=None, workspace=None, want_logits=True):

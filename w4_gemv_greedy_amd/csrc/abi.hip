@@ -22,8 +22,8 @@ bool overlap(const void* p, size_t bytes, const void* q, size_t qbytes) {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // rows, columns and batch below 2^31
 
 int check_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-              const uint16_t* x, const float* y, int64_t rows, int64_t N, int64_t K,
-              const void* workspace, size_t workspace_bytes, size_t need) {
+              const uint16_t* x, const void* y, int64_t rows, int64_t N, int64_t K,
+              const void* workspace, size_t workspace_bytes, size_t need, size_t ysize = 4) {
   if (!wq || !scales || !biases || !x || !y) return W4G_EINVAL_PTR;
   if (rows < 1 || rows >= kMaxDim || N < 1 || N >= kMaxDim || K < 64 || K >= kMaxDim || K % 64)
     return W4G_ESHAPE;
@@ -31,7 +31,7 @@ int check_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases
     return W4G_EALIGN;
   if (need > 0 && (!workspace || workspace_bytes < need)) return W4G_EWORKSPACE;
   if (need > 0 && !aligned16(workspace)) return W4G_EALIGN;
-  const size_t ybytes = (size_t)rows * (size_t)N * sizeof(float);
+  const size_t ybytes = (size_t)rows * (size_t)N * ysize;
   const size_t wbytes = (size_t)N * (size_t)(K / 8) * sizeof(uint32_t);
   const size_t gbytes = (size_t)N * (size_t)(K / 64) * sizeof(uint16_t);
   const size_t xbytes = (size_t)rows * (size_t)K * sizeof(uint16_t);
@@ -124,16 +124,24 @@ int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                      W4G_GEMV_AUTO);
 }
 
-int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-             const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K, void* workspace,
-             size_t workspace_bytes, void* stream) {
+int qmm_gemm_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                const uint16_t* x, void* y, int64_t M, int64_t N, int64_t K, void* workspace,
+                size_t workspace_bytes, void* stream, int y_dtype) {
+  if (y_dtype != W4G_F32 && y_dtype != W4G_BF16) return W4G_EDTYPE;
   if (M < 1 || M >= kMaxDim || N < 1 || N >= kMaxDim || K < 64 || K >= kMaxDim || K % 64)
     return (!wq || !scales || !biases || !x || !y) ? W4G_EINVAL_PTR : W4G_ESHAPE;
   const size_t need = w4g::gemm_workspace_bytes(M, N, K);
-  const int rc = check_qmm(wq, scales, biases, x, y, M, N, K, workspace, workspace_bytes, need);
+  const int rc = check_qmm(wq, scales, biases, x, y, M, N, K, workspace, workspace_bytes, need,
+                           y_dtype == W4G_BF16 ? 2 : 4);
   if (rc) return rc;
-  return from_hip(w4g::launch_gemm(wq, scales, biases, x, y, M, N, K, workspace,
+  return from_hip(w4g::launch_gemm(wq, scales, biases, x, y, y_dtype == W4G_BF16, M, N, K, workspace,
                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+             const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  return qmm_gemm_ex(wq, scales, biases, x, y, M, N, K, workspace, workspace_bytes, stream, W4G_F32);
 }
 
 int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,

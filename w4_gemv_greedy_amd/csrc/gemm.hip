@@ -24,12 +24,15 @@
 //
 // Work split: a pre-pass writes x permuted into the element order of the code
 // expansion, and the exact three-part group sums.  A workgroup of four waves
-// owns a 128 x 128 tile of Y, each wave 64 x 64 (2 x 2 matrix-core tiles); the
-// tile's activations, codes and scales go through LDS one or two groups at a
-// time.  Two main loops share that arithmetic: one stages the operands
-// through registers (small enough for two workgroups per CU), the other loads
-// them straight into a three-stage LDS ring (one workgroup per CU, deeper
-// prefetch), taken when the grid is too small to place two workgroups per CU.
+// owns a tile of Y; its activations, codes and scales go through LDS one or two
+// groups at a time.  Three main loops share that arithmetic: 128 x 128 tiles
+// (each wave 64 x 64, 2 x 2 matrix-core tiles) with the operands staged
+// through registers (two workgroups per CU) when there are tiles enough for
+// that; 128 x 128 tiles loaded straight into an LDS ring (one workgroup per
+// CU) when fewer; and 64 x 64 tiles (each wave one 32 x 32 matrix-core tile)
+// through a ring of LDS loads for short prompts and small grids.  The bias
+// terms and the store follow the main loop; the result is fp32, or bf16
+// rounded to nearest-even from it.
 #include <algorithm>
 
 #include "w4g_internal.h"
@@ -39,6 +42,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr uint32_t kMagic2 = 0x40004000u;  // bf16 pair (2.0, 2.0)
+constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 (gfx9 family): raw dword data
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // plain vector: copies stay in registers
 constexpr uint32_t kOnes = 0x3F803F80u;
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -125,67 +131,106 @@ __global__ __launch_bounds__(kThreads) void xprep_kernel(const uint16_t* __restr
   dst[2 * G16] = (uint16_t)parts[2];
 }
 
-// The affine remainder and the store, shared by both main loops: for each block of 16
+// The stored value: fp32 as computed, or bf16 rounded to nearest-even from it
+// (a NaN stays a quiet NaN of the same sign; a finite value past the bf16
+// range rounds to infinity, as nearest-even rounding does).
+__device__ __forceinline__ void put(float* y, int64_t i, float v) { y[i] = v; }
+__device__ __forceinline__ void put(uint16_t* y, int64_t i, float v) {
+  const uint32_t u = __float_as_uint(v);
+  y[i] = (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? (u >> 16) | 0x0040u : f32_to_bf16_rne(v));
+}
+
+// The affine remainder and the store, shared by the main loops: for each block of 16
 // groups (ascending), b X1, b X2, b X3, (-16 s) X1, (-16 s) X2, (-16 s) X3, each an
-// exact bf16 product on the matrix cores; `vec` (G % 8 == 0 and 16-byte aligned scale
-// and bias tables) allows 16-byte loads.  The wave's tile starts at row mw, column nw.
+// exact bf16 product on the matrix cores.  The wave's tile starts at row mw, column
+// nw; lane (h, l32) feeds row l32 of a row tile and column l32 of a column tile,
+// groups 8h .. 8h + 7 of each block.
+//
+// The operands of the next PF blocks are in flight while a block is multiplied
+// (a ring of registers).  Rows at or past M read zero sums (a buffer load past
+// the end of the slice's rows); columns past N read row N - 1 and store nothing;
+// groups at or past G (the padding of the last block) get zero biases and scales
+// and have zero sums.  VEC (G % 8 == 0 and 16-byte aligned tables): one 16-byte
+// load per lane for the block's eight biases or scales, else eight 2-byte loads.
+struct BiasCols {
+  uint32_t b[4], s[4];  // bf16 pairs: groups 8h + 2q, 8h + 2q + 1 in word q
+};
+
+template <bool VEC>
+__device__ __forceinline__ void load_cols(BiasCols& o, const uint16_t* __restrict__ scales,
+                                          const uint16_t* __restrict__ biases, int64_t n, int64_t G,
+                                          int64_t g0) {
+  if constexpr (VEC) {
+    const int64_t gc = g0 <= G - 8 ? g0 : G - 8;  // a valid 8-group block; masked if past G
+    const uint4 rb = *reinterpret_cast<const uint4*>(biases + n * G + gc);
+    const uint4 rs = *reinterpret_cast<const uint4*>(scales + n * G + gc);
+    const uint32_t keep = g0 < G ? 0xFFFFFFFFu : 0u;
+    o.b[0] = rb.x & keep, o.b[1] = rb.y & keep, o.b[2] = rb.z & keep, o.b[3] = rb.w & keep;
+    o.s[0] = rs.x & keep, o.s[1] = rs.y & keep, o.s[2] = rs.z & keep, o.s[3] = rs.w & keep;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t g = g0 + 2 * q;
+      const uint32_t b0 = g < G ? biases[n * G + g] : 0u, b1 = g + 1 < G ? biases[n * G + g + 1] : 0u;
+      const uint32_t s0 = g < G ? scales[n * G + g] : 0u, s1 = g + 1 < G ? scales[n * G + g + 1] : 0u;
+      o.b[q] = b0 | (b1 << 16);
+      o.s[q] = s0 | (s1 << 16);
+    }
+  }
+}
+
 template <int TI, int TJ>
+struct BiasOps {
+  v4u ax[TI][3];
+  BiasCols c[TJ];
+};
+
+template <int TI, int TJ, bool VEC, int PF, typename OUT>
 __device__ __forceinline__ void bias_and_store(f32x16_t (&tot)[TI][TJ], const uint16_t* __restrict__ scales,
                                                const uint16_t* __restrict__ biases,
-                                               const uint16_t* __restrict__ xs, float* __restrict__ y,
+                                               const uint16_t* __restrict__ xs, OUT* __restrict__ y,
                                                int64_t M, int64_t N, int64_t G, int64_t G16, int64_t ldy,
-                                               int64_t mw, int64_t nw, int l32, int h, bool vec) {
-  for (int64_t kk = 0; kk < G16; kk += 16) {
-    uint4 ax[TI][3];
+                                               int64_t mw, int64_t nw, int l32, int h) {
+  // sums: rows mw.. of xs ([M][3][G16] bf16) through a buffer descriptor, so rows
+  // past M read zero
+  const int64_t rows = M > mw ? M - mw : 0;
+  const __amdgpu_buffer_rsrc_t rxs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(xs + (rows ? mw : 0) * 3 * G16), (short)0, (int)(rows * 3 * G16 * 2),
+      kRsrcWord3);
+  int xoff[TI];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int64_t m = mw + i * 32 + l32;
+  for (int i = 0; i < TI; ++i) xoff[i] = (int)((i * 32 + l32) * 3 * G16 * 2 + h * 16);
+  int64_t ncol[TJ];
 #pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        ax[i][q] = make_uint4(0u, 0u, 0u, 0u);
-        if (m < M)
-          ax[i][q] = *reinterpret_cast<const uint4*>(xs + m * 3 * G16 + q * G16 + kk + h * 8);
-      }
-    }
+  for (int j = 0; j < TJ; ++j) {
+    const int64_t n = nw + j * 32 + l32;
+    ncol[j] = n < N ? n : N - 1;
+  }
+  const int nb = (int)(G16 / 16);
+  auto load = [&](BiasOps<TI, TJ>& o, int blk) __attribute__((always_inline)) {
+    blk = blk < nb ? blk : nb - 1;  // past the last block: reload it (never used)
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        o.ax[i][q] = __builtin_amdgcn_raw_buffer_load_b128(rxs, xoff[i] + q * (int)G16 * 2, blk * 32, 0);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) load_cols<VEC>(o.c[j], scales, biases, ncol[j], G, (int64_t)blk * 16 + h * 8);
+  };
+  auto consume = [&](const BiasOps<TI, TJ>& o) __attribute__((always_inline)) {
     bf16x8_t bb[TJ], bs[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      int64_t n = nw + j * 32 + l32;
-      n = n < N ? n : N - 1;
-      const int64_t g0 = kk + h * 8;
-      uint32_t eb[8], es[8];
-      if (vec && g0 + 8 <= G) {
-        const uint4 rb = *reinterpret_cast<const uint4*>(biases + n * G + g0);
-        const uint4 rs = *reinterpret_cast<const uint4*>(scales + n * G + g0);
-        const uint32_t wb[4] = {rb.x, rb.y, rb.z, rb.w};
-        const uint32_t ws[4] = {rs.x, rs.y, rs.z, rs.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          eb[2 * q] = wb[q] & 0xFFFFu;
-          eb[2 * q + 1] = wb[q] >> 16;
-          es[2 * q] = ws[q] & 0xFFFFu;
-          es[2 * q + 1] = ws[q] >> 16;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const bool in = g0 + q < G;
-          eb[q] = in ? (uint32_t)biases[n * G + g0 + q] : 0u;
-          es[q] = in ? (uint32_t)scales[n * G + g0 + q] : 0u;
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q)  // -16 s, exact: a power-of-two multiple of a bf16
-        es[q] = __float_as_uint(-16.0f * bf16_to_f32(es[q])) >> 16;
       uint4 vb, vs;
-      vb.x = eb[0] | (eb[1] << 16);
-      vb.y = eb[2] | (eb[3] << 16);
-      vb.z = eb[4] | (eb[5] << 16);
-      vb.w = eb[6] | (eb[7] << 16);
-      vs.x = es[0] | (es[1] << 16);
-      vs.y = es[2] | (es[3] << 16);
-      vs.z = es[4] | (es[5] << 16);
-      vs.w = es[6] | (es[7] << 16);
+      uint32_t ws[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // -16 s, exact: a power-of-two multiple of a bf16
+        const uint32_t lo = __float_as_uint(-16.0f * bf16_to_f32(o.c[j].s[q] & 0xFFFFu)) >> 16;
+        const uint32_t hi = __float_as_uint(-16.0f * bf16_to_f32(o.c[j].s[q] >> 16)) >> 16;
+        ws[q] = lo | (hi << 16);
+      }
+      vb = make_uint4(o.c[j].b[0], o.c[j].b[1], o.c[j].b[2], o.c[j].b[3]);
+      vs = make_uint4(ws[0], ws[1], ws[2], ws[3]);
       bb[j] = __builtin_bit_cast(bf16x8_t, vb);
       bs[j] = __builtin_bit_cast(bf16x8_t, vs);
     }
@@ -196,8 +241,21 @@ __device__ __forceinline__ void bias_and_store(f32x16_t (&tot)[TI][TJ], const ui
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           tot[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, ax[i][pass % 3]), pass < 3 ? bb[j] : bs[j], tot[i][j],
+              __builtin_bit_cast(bf16x8_t, o.ax[i][pass % 3]), pass < 3 ? bb[j] : bs[j], tot[i][j],
               0, 0, 0);
+  };
+
+  BiasOps<TI, TJ> ring[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load(ring[p], p);
+  // every iteration consumes PF blocks and loads the PF after them (loads past
+  // the last block reread it, so the number in flight never changes)
+  for (int b = 0; b < nb; b += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      if (b + p < nb) consume(ring[p]);
+      load(ring[p], b + p + PF);
+    }
   }
 
   // store: lane holds rows 8*(v/4) + 4*h + v%4 of column l32 of each 32 x 32 tile
@@ -210,9 +268,22 @@ __device__ __forceinline__ void bias_and_store(f32x16_t (&tot)[TI][TJ], const ui
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t m = mw + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m < M) y[m * ldy + n] = tot[i][j][v];
+        if (m < M) put(y, m * ldy + n, tot[i][j][v]);
       }
     }
+}
+
+template <int TI, int TJ, int PF, typename OUT>
+__device__ __forceinline__ void bias_and_store_any(f32x16_t (&tot)[TI][TJ], const uint16_t* __restrict__ scales,
+                                                   const uint16_t* __restrict__ biases,
+                                                   const uint16_t* __restrict__ xs, OUT* __restrict__ y,
+                                                   int64_t M, int64_t N, int64_t G, int64_t G16,
+                                                   int64_t ldy, int64_t mw, int64_t nw, int l32, int h,
+                                                   bool vec) {
+  if (vec)
+    bias_and_store<TI, TJ, true, PF, OUT>(tot, scales, biases, xs, y, M, N, G, G16, ldy, mw, nw, l32, h);
+  else  // the uncommon layouts: one block in flight
+    bias_and_store<TI, TJ, false, 1, OUT>(tot, scales, biases, xs, y, M, N, G, G16, ldy, mw, nw, l32, h);
 }
 
 // Workgroup tile 128 x 128 of Y, four waves in a 2 x 2 grid, each owning 64 x 64
@@ -229,9 +300,6 @@ constexpr int kAStage = kTM * 128;
 constexpr int kBStage = 2 * kTN * 16;
 constexpr int kSStage = kTN * 2;
 constexpr int kStage = kAStage + kBStage + kSStage;
-constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 (gfx9 family): raw dword data
-
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // plain vector: copies stay in registers
 
 // one group's activations for the workgroup tile (this thread's share) ...
 struct StagedA {
@@ -243,10 +311,11 @@ struct StagedB {
   uint16_t s;
 };
 
+template <typename OUT>
 __global__ __launch_bounds__(256) void gemm_kernel(
     const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const uint16_t* __restrict__ xp,
-    const uint16_t* __restrict__ xs, float* __restrict__ y, int64_t M, int64_t N, int64_t K,
+    const uint16_t* __restrict__ xs, OUT* __restrict__ y, int64_t M, int64_t N, int64_t K,
     int64_t ldy, int64_t G16, int64_t NT, int64_t tiles, int64_t per, bool vec) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
   const int tid = threadIdx.x;
@@ -392,28 +461,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     __syncthreads();
   }
 
-  bias_and_store<2, 2>(tot, scales, biases, xs, y, M, N, G, G16, ldy, m0 + wm * 64, n0 + wn * 64, l32,
-                       h, vec);
+  bias_and_store_any<2, 2, 2, OUT>(tot, scales, biases, xs, y, M, N, G, G16, ldy, m0 + wm * 64,
+                                   n0 + wn * 64, l32, h, vec);
 }
 
-// The same tile walk with the operands moved by buffer loads straight into LDS
-// (no staging registers), two groups per stage and three stages in flight, so a
-// stage's loads are issued two stages before it is used.  Used when G is even
-// (whole stages) and the scale table is 4-byte aligned (one dword per column
-// carries a stage's two scales).  Per stage, in LDS:
-//   A: 128 rows x 256 bytes, 16-byte chunk c (of the two groups' 16) of row r
+// The same arithmetic with the operands moved by buffer loads straight into
+// LDS (no staging registers), two groups per stage and NS stages in a ring, so
+// a stage's loads are issued NS - 1 stages before it is used.  The tile is
+// (32 TI WM) x (32 TJ WN): four waves in a WM x WN grid, each owning
+// (32 TI) x (32 TJ).  Used when G is even (whole stages) and the scale table is
+// 4-byte aligned (one dword per column carries a stage's two scales).  Per
+// stage, in LDS:
+//   A: TM rows x 256 bytes, 16-byte chunk c (of the two groups' 16) of row r
 //      at position c ^ (r & 15);
-//   B: 128 columns x 64 bytes (group-in-stage, half) pieces, piece q of column n
+//   B: TN columns x 64 bytes (group-in-stage, half) pieces, piece q of column n
 //      at position q ^ ((n >> 2) & 3);
-//   S: 128 columns x the two groups' scales.
-// Every wave issues exactly 11 of these loads per stage, so waiting for all but
-// the newest 11 completes the older stage.  Per output the arithmetic and its
-// order are those of gemm_kernel: both kernels give the same bits.
-constexpr int kDStageA = kTM * 256;
-constexpr int kDStageB = kTN * 64;
-constexpr int kDStageS = kTN * 4;
-constexpr int kDStage = kDStageA + kDStageB + kDStageS;
-constexpr int kDStages = 3;
+//   S: TN columns x the two groups' scales.
+// Every wave issues the same number of these loads per stage (TM / 16 + TN / 64
+// + 1), so waiting for all but the newest stages' loads completes the oldest.
+// Per output the arithmetic and its order are those of gemm_kernel, whatever
+// the tile: every variant gives the same bits.
 constexpr int kCUs = 256;  // compute units of the MI355X
 
 // Buffer load of 16 bytes per lane into LDS at m0 + 16 * lane.
@@ -426,20 +493,46 @@ __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, __amdgpu_buffe
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
 }
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// ... with N = ahead * L for a run-time ahead in [0, A] (the immediate is fixed
+// per instruction)
+template <int L, int A>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (A > 0) {
+    if (ahead >= A) {
+      wait_vm<A * L>();
+      return;
+    }
+    wait_stages<L, A - 1>(ahead);
+  } else {
+    wait_vm<0>();
+  }
+}
 
+template <int TI, int TJ, int WM, int WN, int NS, typename OUT>
 __global__ __launch_bounds__(256) void gemm_dma_kernel(
     const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const uint16_t* __restrict__ xp,
-    const uint16_t* __restrict__ xs, float* __restrict__ y, int64_t M, int64_t N, int64_t K,
+    const uint16_t* __restrict__ xs, OUT* __restrict__ y, int64_t M, int64_t N, int64_t K,
     int64_t ldy, int64_t G16, int64_t NT, int64_t tiles, int64_t per, bool vec) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kDStages * kDStage];
+  static_assert(WM * WN == 4, "four waves");
+  constexpr int TM = 32 * TI * WM, TN = 32 * TJ * WN;
+  constexpr int SA = TM * 256, SB = TN * 64, SS = TN * 4, STAGE = SA + SB + SS;
+  constexpr int LA = TM / 16, LB = TN / 64, SL = TN / 4;  // per wave and stage
+  constexpr int L = LA + LB + 1;
+  static_assert(LA >= 1 && LB >= 1 && SL <= 64 && (NS - 2) * L <= 63, "tile");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NS * STAGE];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int tile = (b & 7) * (int)per + (b >> 3);
   if (tile >= (int)tiles) return;
   const int mt = __builtin_amdgcn_readfirstlane(tile / (int)NT);
   const int nt = __builtin_amdgcn_readfirstlane(tile - mt * (int)NT);
-  const int64_t m0 = (int64_t)mt * kTM, n0 = (int64_t)nt * kTN;
+  const int64_t m0 = (int64_t)mt * TM, n0 = (int64_t)nt * TN;
   const int G = (int)(K >> 6);
   const int K8 = (int)(K >> 3);
   const int ns = G >> 1;
@@ -452,65 +545,66 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  // loads: lane offsets per instruction (rows 4 blk .. 4 blk + 3 of A, columns
-  // 16 blk .. 16 blk + 15 of B, columns 32 wave + lane of S for lanes < 32)
-  uint32_t va[8], vb[2];
+  // loads: lane offsets per instruction (rows 4 (LA wave + i) + lane / 16 of A,
+  // columns 16 (LB wave + j) + lane / 4 of B, columns SL wave + lane of S for
+  // lanes < SL)
+  uint32_t va[LA], vb[LB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rr = 32 * wave + 4 * i + (lane >> 4);
+  for (int i = 0; i < LA; ++i) {
+    const int rr = 4 * (LA * wave + i) + (lane >> 4);
     const int c = (lane & 15) ^ (rr & 15);
     va[i] = (uint32_t)(rr * K * 2 + c * 16);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = 16 * (2 * wave + j) + (lane >> 2);
+  for (int j = 0; j < LB; ++j) {
+    const int col = 16 * (LB * wave + j) + (lane >> 2);
     const int q = (lane & 3) ^ ((col >> 2) & 3);
     vb[j] = (uint32_t)(col * (K8 * 4) + q * 16);
   }
-  const uint32_t vsc = (uint32_t)((32 * wave + (lane & 31)) * G * 2);
+  const uint32_t vsc = (uint32_t)((SL * wave + (lane & (SL - 1))) * G * 2);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
   auto issue = [&](int s) __attribute__((always_inline)) {
-    const uint32_t base = lds0 + (uint32_t)((s % kDStages) * kDStage);
+    const uint32_t base = lds0 + (uint32_t)((s % NS) * STAGE);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma16(__builtin_amdgcn_readfirstlane(base + (8 * wave + i) * 1024), va[i], rx, (uint32_t)(s * 256));
+    for (int i = 0; i < LA; ++i)
+      dma16(__builtin_amdgcn_readfirstlane(base + (LA * wave + i) * 1024), va[i], rx, (uint32_t)(s * 256));
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      dma16(__builtin_amdgcn_readfirstlane(base + kDStageA + (2 * wave + j) * 1024), vb[j], rw,
+    for (int j = 0; j < LB; ++j)
+      dma16(__builtin_amdgcn_readfirstlane(base + SA + (LB * wave + j) * 1024), vb[j], rw,
             (uint32_t)(s * 64));
-    const uint32_t sbase = __builtin_amdgcn_readfirstlane(base + kDStageA + kDStageB + wave * 128);
-    if (lane < 32) dma4(sbase, vsc, rs, (uint32_t)(s * 4));
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(base + SA + SB + wave * SL * 4);
+    if (lane < SL) dma4(sbase, vsc, rs, (uint32_t)(s * 4));
   };
 
-  // compute: wave (wm, wn) owns rows 64 wm.., columns 64 wn.. of the tile; lane
-  // (h, l32) feeds row l32 of a row tile and column l32 of a column tile, half h
-  // of each 16-element step
-  const int wm = wave >> 1, wn = wave & 1;
+  // compute: wave (wm, wn) owns rows 32 TI wm.., columns 32 TJ wn.. of the tile;
+  // lane (h, l32) feeds row l32 of a row tile and column l32 of a column tile,
+  // half h of each 16-element step
+  const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, h = lane >> 5;
   int ar[2][4], br[2];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      ar[gi][t] = (wm * 64 + l32) * 256 + (((gi * 8 + t + 4 * h) ^ (l32 & 15)) << 4);
-    br[gi] = kDStageA + (wn * 64 + l32) * 64 + (((gi * 2 + h) ^ ((l32 >> 2) & 3)) << 4);
+      ar[gi][t] = (wm * 32 * TI + l32) * 256 + (((gi * 8 + t + 4 * h) ^ (l32 & 15)) << 4);
+    br[gi] = SA + (wn * 32 * TJ + l32) * 64 + (((gi * 2 + h) ^ ((l32 >> 2) & 3)) << 4);
   }
-  const int sr = kDStageA + kDStageB + (wn * 64 + l32) * 4;
+  const int sr = SA + SB + (wn * 32 * TJ + l32) * 4;
   const uint32_t msk = 0x00780078u, mg = kMagic2;
 
-  f32x16_t tot[2][2];
+  f32x16_t tot[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) tot[i][j][v] = 0.0f;
 
   auto compute = [&](const unsigned char* base, int gi) __attribute__((always_inline)) {
-    bf16x8_t bop[2][4];
-    float s8[2];
+    bf16x8_t bop[TJ][4];
+    float s8[TJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       const v4u c = *reinterpret_cast<const v4u*>(base + br[gi] + j * 2048);
       s8[j] = 8.0f * bf16_to_f32(*reinterpret_cast<const uint16_t*>(base + sr + j * 128 + gi * 2));
       bop[j][0] = expand_codes(c.x, msk, mg);
@@ -519,47 +613,111 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(
       bop[j][3] = expand_codes(c.w, msk, mg);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < TI; ++i) {
       v4u a[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4u*>(base + ar[gi][t] + i * 8192);
-      f32x16_t p[2];
+      f32x16_t p[TJ];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) p[j][v] = 0.0f;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
           p[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[t]),
                                                          bop[j][t], p[j], 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) tot[i][j][v] = __builtin_fmaf(s8[j], p[j][v], tot[i][j][v]);
     }
   };
 
-  issue(0);
-  if (ns > 1) issue(1);
-  for (int st = 0; st < ns; ++st) {
-    if (st + 1 < ns)
-      asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // one wave tile (TI = TJ = 1): the stage's two group products are independent
+  // matrix-core chains, so they run side by side; the scaled sums still enter
+  // the total in group order
+  auto compute_pair = [&](const unsigned char* base) __attribute__((always_inline)) {
+    bf16x8_t bop[2][4];
+    float s8[2];
+    v4u a[2][4];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const v4u c = *reinterpret_cast<const v4u*>(base + br[gi]);
+      s8[gi] = 8.0f * bf16_to_f32(*reinterpret_cast<const uint16_t*>(base + sr + gi * 2));
+      bop[gi][0] = expand_codes(c.x, msk, mg);
+      bop[gi][1] = expand_codes(c.y, msk, mg);
+      bop[gi][2] = expand_codes(c.z, msk, mg);
+      bop[gi][3] = expand_codes(c.w, msk, mg);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[gi][t] = *reinterpret_cast<const v4u*>(base + ar[gi][t]);
+    }
+    f32x16_t p[2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[gi][v] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+        p[gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[gi][t]),
+                                                        bop[gi][t], p[gi], 0, 0, 0);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tot[0][0][v] = __builtin_fmaf(s8[gi], p[gi][v], tot[0][0][v]);
+  };
+
+  auto compute_stage = [&](const unsigned char* base) __attribute__((always_inline)) {
+    if constexpr (TI == 1 && TJ == 1) {
+      compute_pair(base);
+    } else {
+      compute(base, 0);
+      compute(base, 1);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < ns) issue(s);
+  // Stage st waits until only the stages issued after it are in flight, then
+  // (all waves past the barrier) its buffer's predecessor is free for stage
+  // st + NS - 1.  Steady state, unrolled by NS so every buffer offset is a
+  // constant: NS - 2 stages ahead, and the next issue exists.
+  int st = 0;
+  for (; st + NS - 1 <= ns - NS; st += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      wait_vm<(NS - 2) * L>();
+      __syncthreads();
+      issue(st + u + NS - 1);
+      compute_stage(smem + u * STAGE);
+    }
+  }
+  for (; st < ns; ++st) {
+    const int ahead = ns - 1 - st < NS - 2 ? ns - 1 - st : NS - 2;
+    wait_stages<L, NS - 2>(ahead);
     __syncthreads();
-    if (st + 2 < ns) issue(st + 2);
-    const unsigned char* base = smem + (st % kDStages) * kDStage;
-    compute(base, 0);
-    compute(base, 1);
+    if (st + NS - 1 < ns) issue(st + NS - 1);
+    compute_stage(smem + (st % NS) * STAGE);
   }
 
-  bias_and_store<2, 2>(tot, scales, biases, xs, y, M, N, G, G16, ldy, m0 + wm * 64, n0 + wn * 64, l32,
-                       h, vec);
+  bias_and_store_any<TI, TJ, TI * TJ == 1 ? 6 : 2, OUT>(tot, scales, biases, xs, y, M, N, G, G16, ldy,
+                                                         m0 + wm * 32 * TI, n0 + wn * 32 * TJ, l32, h,
+                                                         vec);
 }
 
 int64_t g16_of(int64_t K) { return (((K >> 6) + 15) / 16) * 16; }
+
+// Where the 64 x 64 tiles take over (rows of the slice, 128 x 128 tiles it makes)
+#ifndef W4G_SMALL_RULE
+bool small_tiles(int64_t M, int64_t tiles128) { return tiles128 < kCUs / 2 || (M <= 128 && tiles128 < 2 * kCUs); }
+#else
+bool small_tiles(int64_t M, int64_t tiles128) { return W4G_SMALL_RULE; }
+#endif
+
 
 }  // namespace
 
@@ -568,8 +726,61 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (size_t)(M * K) * sizeof(uint16_t) + (size_t)(M * 3 * g16_of(K)) * sizeof(uint16_t);
 }
 
+namespace {
+
+// One launch per slice of rows and columns; every buffer a slice reads stays
+// below 2^31 bytes.  The variant follows from the shape and the pointers:
+//   the register-staged loop with 128 x 128 tiles when there are enough tiles
+//   for two workgroups per CU (or when the LDS-load kernel does not apply),
+//   the LDS-load loop with 128 x 128 tiles while they still cover every CU,
+//   and the LDS-load loop with 64 x 64 tiles (a deeper ring) below that.
+template <typename OUT>
+hipError_t launch_main(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                       const uint16_t* xp, const uint16_t* xs, OUT* y, int64_t M, int64_t N,
+                       int64_t K, int64_t G16, bool vec, bool dma, hipStream_t stream) {
+  const int64_t G = K >> 6;
+  const int64_t max_rows_x = std::max<int64_t>(kTM, (((int64_t)1 << 31) - 1) / (K * 2) / kTM * kTM);
+  const int64_t max_cols_w = std::max<int64_t>(kTN, (((int64_t)1 << 31) - 1) / (K / 2) / kTN * kTN);
+  for (int64_t ms = 0; ms < M; ms += max_rows_x) {
+    const int64_t Ms = std::min(M - ms, max_rows_x);
+    for (int64_t ns = 0; ns < N; ns += max_cols_w) {
+      const int64_t Ns = std::min(N - ns, max_cols_w);
+      const uint32_t* w_s = wq + ns * (K / 8);
+      const uint16_t *s_s = scales + ns * G, *b_s = biases + ns * G;
+      const uint16_t *xp_s = xp + ms * K, *xs_s = xs + ms * 3 * G16;
+      OUT* y_s = y + ms * N + ns;
+      const int64_t tiles128 = ((Ms + kTM - 1) / kTM) * ((Ns + kTN - 1) / kTN);
+      if (dma && small_tiles(Ms, tiles128)) {
+        // 64 x 64 tiles: a 4-stage ring (83 KiB, one workgroup per CU) while the
+        // tiles fit on the CUs once, else 3 stages (62 KiB) so two share a CU
+        const int64_t NT = (Ns + 63) / 64, tiles = ((Ms + 63) / 64) * NT, per = (tiles + 7) / 8;
+        if (tiles <= kCUs)
+          hipLaunchKernelGGL((gemm_dma_kernel<1, 1, 2, 2, 4, OUT>), dim3((unsigned)(8 * per)), dim3(256), 0,
+                             stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles, per, vec);
+        else
+          hipLaunchKernelGGL((gemm_dma_kernel<1, 1, 2, 2, 3, OUT>), dim3((unsigned)(8 * per)), dim3(256), 0,
+                             stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles, per, vec);
+      } else if (!dma || tiles128 >= 2 * kCUs) {
+        const int64_t NT = (Ns + kTN - 1) / kTN, per = (tiles128 + 7) / 8;
+        hipLaunchKernelGGL(gemm_kernel<OUT>, dim3((unsigned)(8 * per)), dim3(256), 0, stream, w_s, s_s,
+                           b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles128, per, vec);
+      } else {
+        const int64_t NT = (Ns + kTN - 1) / kTN, per = (tiles128 + 7) / 8;
+        hipLaunchKernelGGL((gemm_dma_kernel<2, 2, 2, 2, 3, OUT>), dim3((unsigned)(8 * per)), dim3(256), 0,
+                           stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles128, per,
+                           vec);
+      }
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                       const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
+                       const uint16_t* x, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
                        void* workspace, hipStream_t stream) {
   const int64_t G16 = g16_of(K);
   uint16_t* xp = reinterpret_cast<uint16_t*>(workspace);
@@ -577,37 +788,17 @@ hipError_t launch_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_
   const int64_t nt = M * G16;
   hipLaunchKernelGGL(xprep_kernel, dim3((unsigned)((nt + kThreads - 1) / kThreads)), dim3(kThreads),
                      0, stream, x, xp, xs, M, K, G16);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool vec = ((K >> 6) & 7) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
                                              reinterpret_cast<uintptr_t>(biases)) & 15u) == 0;
-  // every buffer the main loop reads stays below 2^31 bytes: cut M and N into slices
-  const int64_t G = K >> 6;
-  // whole two-group stages and 4-byte aligned scale pairs: the LDS-load kernel
-  const bool dma = (G % 2) == 0 && (reinterpret_cast<uintptr_t>(scales) & 3u) == 0;
-  const int64_t max_rows_x = std::max<int64_t>(kTM, (((int64_t)1 << 31) - 1) / (K * 2) / kTM * kTM);
-  const int64_t max_cols_w = std::max<int64_t>(kTN, (((int64_t)1 << 31) - 1) / (K / 2) / kTN * kTN);
-  for (int64_t ms = 0; ms < M; ms += max_rows_x) {
-    const int64_t Ms = std::min(M - ms, max_rows_x);
-    for (int64_t ns = 0; ns < N; ns += max_cols_w) {
-      const int64_t Ns = std::min(N - ns, max_cols_w);
-      const int64_t MT = (Ms + kTM - 1) / kTM, NT = (Ns + kTN - 1) / kTN;
-      const int64_t tiles = MT * NT, per = (tiles + 7) / 8;
-      // the register-staged kernel fits two workgroups per CU, the LDS-load kernel one:
-      // take the latter only when the grid leaves CUs without a second workgroup
-      if (dma && tiles < 2 * kCUs)
-        hipLaunchKernelGGL(gemm_dma_kernel, dim3((unsigned)(8 * per)), dim3(256), 0, stream,
-                           wq + ns * (K / 8), scales + ns * G, biases + ns * G, xp + ms * K,
-                           xs + ms * 3 * G16, y + ms * N + ns, Ms, Ns, K, N, G16, NT, tiles, per, vec);
-      else
-        hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)(8 * per)), dim3(256), 0, stream, wq + ns * (K / 8),
-                           scales + ns * G, biases + ns * G, xp + ms * K, xs + ms * 3 * G16,
-                           y + ms * N + ns, Ms, Ns, K, N, G16, NT, tiles, per, vec);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  return hipGetLastError();
+  // whole two-group stages and 4-byte aligned scale pairs: the LDS-load kernels apply
+  const bool dma = ((K >> 6) % 2) == 0 && (reinterpret_cast<uintptr_t>(scales) & 3u) == 0;
+  if (y_bf16)
+    return launch_main(wq, scales, biases, xp, xs, reinterpret_cast<uint16_t*>(y), M, N, K, G16, vec, dma,
+                       stream);
+  return launch_main(wq, scales, biases, xp, xs, reinterpret_cast<float*>(y), M, N, K, G16, vec, dma,
+                     stream);
 }
 
 }  // namespace w4g

@@ -18,8 +18,9 @@ hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_
 hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                             const uint16_t* x, float* y, int B, int64_t N, int64_t K,
                             hipStream_t stream);
+// y: fp32 [M][N], or bf16 [M][N] (nearest-even from the fp32 result) when y_bf16
 hipError_t launch_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                       const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
+                       const uint16_t* x, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
                        void* workspace, hipStream_t stream);
 // Kernel family qmm_gemv runs for a shape (1 = vector ALU, 2 = matrix cores);
 // a function of (B, N, K) only.
