@@ -82,6 +82,22 @@ def test_gemv_valu_variants_bitwise(N, K, B):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("N,K", [(9477, 1024), (8193, 3072), (5120, 2048), (300, 17408)])
+def test_gemv_per_cu_layout(N, K):
+    """B = 1 with one workgroup per CU (an equal share of rows each, half waves
+    striding through it; ragged shares and a last workgroup with an odd row
+    count) against the oracle, and bitwise equal to the same rows computed by
+    the short-workgroup layout of B = 2 and by the register-staged variant."""
+    wq, sc, bi, x = _case(N, K, 2, N % 97)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y1 = down(w4g.qmm_gemv(*W, up_bf16(x[:1]), kernel=1))
+    y2 = down(w4g.qmm_gemv(*W, up_bf16(x), kernel=1))
+    yr = down(w4g.qmm_gemv(*W, up_bf16(x[:1]), kernel=3))
+    assert np.array_equal(y1[0].view(np.uint32), y2[0].view(np.uint32))
+    assert np.array_equal(y1.view(np.uint32), yr.view(np.uint32))
+    assert_close(y1, oracle.qmm(wq, sc, bi, x[:1]), f"gemv per-CU N={N} K={K}")
+
+
 def test_gemv_families_agree():
     wq, sc, bi, x = _case(256, 5120, 4, 12)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x))

@@ -22,10 +22,14 @@
 //
 // Memory: a half wave owns whole rows; in each chunk lane l reads one 16-byte
 // code vector at byte 16l, so a wave-wide load covers 512 contiguous bytes of
-// each of two rows.  A work item is one chunk of R consecutive rows; items are
-// double buffered (one in flight while the other is consumed).  The
-// activations are paired and summed once per workgroup into LDS, laid out so
-// that a half wave's reads are contiguous, and each item's R rows share them.
+// each of two rows.  A work item is one chunk of R consecutive rows; P items
+// are in flight while one is consumed.  The activations are paired and summed
+// once per workgroup into LDS, laid out so that a half wave's reads are
+// contiguous, and each item's R rows share them; their loads go out before the
+// first codes', so staging does not wait behind the code stream.  Rows are
+// dealt out in equal shares: at B = 1 one workgroup per CU for the layer
+// widths (every CU streams the same bytes, no trailing second round), short
+// workgroups of 8 R rows elsewhere.
 #include "w4g_internal.h"
 #ifdef W4G_TUNING
 #include <stdlib.h>
@@ -37,6 +41,7 @@ namespace {
 constexpr int kChunk = 1024;
 constexpr int kThreads = 256;
 constexpr int kHalfWaves = kThreads / 32;
+constexpr int kCUs = 256;  // compute units of the MI355X
 // LDS one workgroup may take here: most of the CU's 160 KiB (above 64 KiB the
 // kernel asks for it with hipFuncSetAttribute); one such workgroup per CU still
 // streams faster than the register-staged variant (measured: down at B=4,
@@ -109,24 +114,27 @@ struct Item {
 
 // LDS: paired activations [B][C][4][32] uint4 (chunk, vector, lane), then lane
 // sums [B][C][32] float.  P items are in flight per half wave (a ring of P
-// buffers).  A half wave owns `ng` groups of R consecutive rows
-// (rows past N repeat row N-1 and store nothing; both half waves of a wave run
-// the same number of items, so every branch in the stream is wave-uniform).
-// A lane past the end of a short last chunk reads lane 0 of chunk 0 (always
-// staged, so finite) and adds exact zeros.
+// buffers).  Workgroup b owns rows [b rpw, (b + 1) rpw) (fewer at the end of
+// the matrix), taken as groups of R consecutive rows: half wave h of H owns
+// groups h, h + H, h + 2H, ...  Both half waves of a wave run as many groups as
+// the first of them (the second repeats its last valid row and stores
+// nothing), so every branch in the stream is wave-uniform.  A lane past the
+// end of a short last chunk reads lane 0 of chunk 0 (always staged, so finite)
+// and adds exact zeros.
 //
-// AM adds the argmax's pass 1 as an epilogue (launched with ng = 1): the
-// workgroup's values go to LDS, and after the stream one thread per batch row
-// writes the record of the best (value, lowest row), or the non-finite flag,
-// to rec[bb][blockIdx.x]; y may then be null.
-template <int B, int R, int P, bool RAGGED, bool AM>
-__global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __restrict__ wq,
-                                                             const uint16_t* __restrict__ scales,
-                                                             const uint16_t* __restrict__ biases,
-                                                             const uint16_t* __restrict__ x,
-                                                             float* __restrict__ y, int64_t N,
-                                                             int64_t K, int64_t ng,
-                                                             uint2* __restrict__ rec) {
+// AM adds the argmax's pass 1 as an epilogue (launched with 256 threads and
+// rpw = 8 R, one group per half wave): the workgroup's values go to LDS, and
+// after the stream one thread per batch row writes the record of the best
+// (value, lowest row), or the non-finite flag, to rec[bb][blockIdx.x]; y may
+// then be null.
+template <int B, int R, int P, bool RAGGED, bool AM, int MAXT = kThreads>
+__global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restrict__ wq,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint16_t* __restrict__ biases,
+                                                         const uint16_t* __restrict__ x,
+                                                         float* __restrict__ y, int64_t N,
+                                                         int64_t K, int64_t rpw,
+                                                         uint2* __restrict__ rec) {
   extern __shared__ uint4 s_mem[];
   const int64_t K8 = K >> 3, K32 = K >> 5, G = K >> 6;
   const int C = (int)((K + kChunk - 1) / kChunk);
@@ -135,8 +143,14 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
 
   const int tid = threadIdx.x;
   const int lane = tid & 31;
-  const int64_t hw = (int64_t)blockIdx.x * kHalfWaves + (tid >> 5);
-  const int64_t row_begin = hw * ng * R;
+  const int H = (int)(blockDim.x >> 5), hwi = tid >> 5;
+  const int64_t wg_begin = (int64_t)blockIdx.x * rpw;
+  const int64_t wg_end = N - wg_begin < rpw ? N : wg_begin + rpw;
+  const int64_t wg_groups = (wg_end - wg_begin + R - 1) / R;
+  const int lead = hwi & ~1;  // the wave's first half wave sets the group count
+  const int64_t ng = wg_groups > lead ? (wg_groups - lead + H - 1) / H : 0;
+  const int64_t row_begin = wg_begin + (int64_t)hwi * R;
+  const int64_t row_step = (int64_t)H * R;
   const int64_t n_items = ng * C;
   const int last_lanes = (int)((K - (int64_t)(C - 1) * kChunk) >> 5);  // active lanes, chunk C-1
   const uint32_t m = kNibbles, g = kMagic128;
@@ -150,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
   auto set_rows = [&]() {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int64_t row = prow + r < N ? prow + r : N - 1;
+      const int64_t row = prow + r < wg_end ? prow + r : wg_end - 1;
       pw[r] = reinterpret_cast<const uint4*>(wq + row * K8) + lane;
       ps[r] = scales + row * G + (lane >> 1);
       pb[r] = biases + row * G + (lane >> 1);
@@ -175,26 +189,19 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
     }
     if (++pc == C) {
       pc = 0;
-      prow += R;
+      prow += row_step;
       set_rows();
     }
   };
-  Item<R> ring[P];
-#pragma unroll
-  for (int sl = 0; sl < P; ++sl) issue(ring[sl]);
-
-  // argmax epilogue: the workgroup's values (one group of R rows per half wave)
-  __shared__ float s_vals[AM ? kHalfWaves * R : 1][AM ? B : 1];
-
-  // ---- stage x: pair each 8-element block, and sum each 32-element lane segment
-  for (int64_t seg = tid; seg < B * K32; seg += kThreads) {
+  // ---- stage x: pair each 8-element block, and sum each 32-element lane segment.
+  // The first XPRE segments of each thread are loaded before the first P items'
+  // codes are issued, so that waiting for them does not also wait for the codes.
+  constexpr int XPRE = 2;
+  const int64_t nseg = B * K32;
+  auto put_seg = [&](int64_t seg, const uint4 (&raw)[4]) {
     const int bb = (int)(seg / K32);
     const int64_t sg = seg % K32;
     const int64_t c = sg >> 5, l = sg & 31;
-    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)bb * K + sg * 32);
-    uint4 raw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = src[i];
     float h = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -206,6 +213,37 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
       h = dot2(p.w, kOnes, h);
     }
     s_xh[((int64_t)bb * C + c) * 32 + l] = h;
+  };
+  auto load_seg = [&](int64_t seg, uint4 (&raw)[4]) {
+    const int bb = (int)(seg / K32);
+    const int64_t sg = seg % K32;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)bb * K + sg * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = src[i];
+  };
+  uint4 pre[XPRE][4];
+#pragma unroll
+  for (int q = 0; q < XPRE; ++q) {
+    const int64_t seg = tid + (int64_t)q * blockDim.x;
+    if (seg < nseg) load_seg(seg, pre[q]);
+  }
+
+  Item<R> ring[P];
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl) issue(ring[sl]);
+
+  // argmax epilogue: the workgroup's values (one group of R rows per half wave)
+  __shared__ float s_vals[AM ? kHalfWaves * R : 1][AM ? B : 1];
+
+#pragma unroll
+  for (int q = 0; q < XPRE; ++q) {
+    const int64_t seg = tid + (int64_t)q * blockDim.x;
+    if (seg < nseg) put_seg(seg, pre[q]);
+  }
+  for (int64_t seg = tid + (int64_t)XPRE * blockDim.x; seg < nseg; seg += blockDim.x) {
+    uint4 raw[4];
+    load_seg(seg, raw);
+    put_seg(seg, raw);
   }
   __syncthreads();
 
@@ -260,13 +298,13 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
 #pragma unroll
           for (int bb = 0; bb < B; ++bb) {
             const float v = half_wave_sum(acc[r][bb]);
-            if (lane == 0 && crow + r < N && (!AM || y != nullptr)) y[(int64_t)bb * N + crow + r] = v;
-            if (AM && lane == 0) s_vals[(tid >> 5) * R + r][bb] = v;
+            if (lane == 0 && crow + r < wg_end && (!AM || y != nullptr)) y[(int64_t)bb * N + crow + r] = v;
+            if (AM && lane == 0) s_vals[hwi * R + r][bb] = v;
             acc[r][bb] = 0.0f;
           }
         }
         cc = 0;
-        crow += R;
+        crow += row_step;
       }
     }
   };
@@ -294,12 +332,12 @@ __global__ __launch_bounds__(kThreads) void gemv_valu_kernel(const uint32_t* __r
     // (launched with one group of R rows per half wave)
     __syncthreads();
     if (tid < B) {
-      const int64_t first = (int64_t)blockIdx.x * kHalfWaves * R;
+      const int64_t first = wg_begin;
       uint64_t best = 0;
       bool bad = false;
 #pragma unroll
       for (int i = 0; i < kHalfWaves * R; ++i) {
-        if (first + i < N) {
+        if (first + i < wg_end) {
           const uint32_t u = __float_as_uint(s_vals[i][tid]);
           if (!finite_bits(u)) bad = true;
           else best = umax64(best, cand(u, (uint32_t)(first + i)));
@@ -426,16 +464,15 @@ int lds_rows_per_item(int B, int64_t N) { return B == 1 ? (few_rows(N) ? 1 : 2) 
 int regs_rows(int B) { return B <= 2 ? 4 : 2; }
 bool use_regs(int B, int64_t K, bool force_regs) { return force_regs || lds_bytes(B, K) > kMaxLds; }
 
-template <int B, int R, int P, bool AM>
+template <int B, int R, int P, bool AM, int MAXT = kThreads>
 hipError_t launch_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                      const uint16_t* x, float* y, uint2* rec, int64_t N, int64_t K, int64_t ng,
-                      hipStream_t stream) {
+                      const uint16_t* x, float* y, uint2* rec, int64_t N, int64_t K, int64_t rpw,
+                      int threads, hipStream_t stream) {
   const bool ragged = (K % kChunk) != 0;
-  const int64_t rows_per_block = (int64_t)kHalfWaves * R * ng;
-  const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
+  const int64_t blocks = (N + rpw - 1) / rpw;
   const size_t lds = lds_bytes(B, K);
-  const void* fn = ragged ? reinterpret_cast<const void*>(&gemv_valu_kernel<B, R, P, true, AM>)
-                          : reinterpret_cast<const void*>(&gemv_valu_kernel<B, R, P, false, AM>);
+  const void* fn = ragged ? reinterpret_cast<const void*>(&gemv_valu_kernel<B, R, P, true, AM, MAXT>)
+                          : reinterpret_cast<const void*>(&gemv_valu_kernel<B, R, P, false, AM, MAXT>);
   if (lds > kDefaultLds) {
     // a host-side attribute of the kernel, set before each such launch (not a
     // stream operation, so it is also fine while a graph is being captured)
@@ -443,14 +480,36 @@ hipError_t launch_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t
     if (e != hipSuccess) return e;
   }
   if (ragged)
-    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, true, AM>), dim3((unsigned)blocks), dim3(kThreads), lds,
-                       stream, wq, scales, biases, x, y, N, K, ng, rec);
+    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, true, AM, MAXT>), dim3((unsigned)blocks), dim3(threads), lds,
+                       stream, wq, scales, biases, x, y, N, K, rpw, rec);
   else
-    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, false, AM>), dim3((unsigned)blocks), dim3(kThreads),
-                       lds, stream, wq, scales, biases, x, y, N, K, ng, rec);
+    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, false, AM, MAXT>), dim3((unsigned)blocks), dim3(threads),
+                       lds, stream, wq, scales, biases, x, y, N, K, rpw, rec);
   return hipGetLastError();
 }
 
+// 256 threads, one group of R rows per half wave: many short workgroups, which
+// the dispatcher spreads over the CUs as they free up (the fused head's layout:
+// one record per workgroup)
+template <int B, int R, int P, bool AM>
+hipError_t launch_short(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                        const uint16_t* x, float* y, uint2* rec, int64_t N, int64_t K,
+                        hipStream_t stream) {
+  return launch_lds<B, R, P, AM>(wq, scales, biases, x, y, rec, N, K, (int64_t)kHalfWaves * R, kThreads,
+                                 stream);
+}
+
+// One workgroup per CU, each with an equal share of the rows (so every CU
+// streams the same number of bytes and no second round of workgroups
+// trails; x is staged once per CU): up to 32 rows per CU one row per half
+// wave, else 16 half waves striding through the share, R rows per item.
+template <int R, int P>
+hipError_t launch_per_cu(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                         const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t rpw = (N + kCUs - 1) / kCUs;
+  const int threads = rpw <= 32 ? 64 * (int)((rpw + 1) / 2) : 512;
+  return launch_lds<1, R, P, false, 1024>(wq, scales, biases, x, y, nullptr, N, K, rpw, threads, stream);
+}
 
 template <int B, int R, bool AM>
 hipError_t launch_regs(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
@@ -481,34 +540,40 @@ hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
       default: return hipErrorInvalidValue;
     }
   }
-  int64_t ng = 1;  // one group of R rows per half wave: many short workgroups,
-                   // which the dispatcher spreads over the CUs as they free up
+  if (!AM && B == 1) {
+    const int64_t rpw = (N + kCUs - 1) / kCUs;
 #ifdef W4G_TUNING
-  if (!AM && getenv("W4G_NG")) ng = atoll(getenv("W4G_NG"));
-  if (!AM && B == 1 && getenv("W4G_RP")) {
-    const int rp = atoi(getenv("W4G_RP"));
-    switch (rp) {
-      case 12: return launch_lds<1, 1, 2, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-      case 14: return launch_lds<1, 1, 4, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-      case 16: return launch_lds<1, 1, 6, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-      case 22: return launch_lds<1, 2, 2, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-      case 23: return launch_lds<1, 2, 3, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-      case 42: return launch_lds<1, 4, 2, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-      case 43: return launch_lds<1, 4, 3, false>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-      default: break;
+    const char* knob = getenv(rpw >= 2 * 16 * 16 ? "W4G_CUH" : "W4G_CU");
+    if (knob) {
+      switch (atoi(knob)) {
+        case 0: break;  // the short-workgroup layout below
+        case 14: return launch_per_cu<1, 4>(wq, scales, biases, x, y, N, K, stream);
+        case 16: return launch_per_cu<1, 6>(wq, scales, biases, x, y, N, K, stream);
+        case 18: return launch_per_cu<1, 8>(wq, scales, biases, x, y, N, K, stream);
+        case 22: return launch_per_cu<2, 2>(wq, scales, biases, x, y, N, K, stream);
+        case 23: return launch_per_cu<2, 3>(wq, scales, biases, x, y, N, K, stream);
+        case 24: return launch_per_cu<2, 4>(wq, scales, biases, x, y, N, K, stream);
+        default: break;
+      }
+      if (atoi(knob) == 0)
+        return few_rows(N) ? launch_short<1, 1, 4, false>(wq, scales, biases, x, y, rec, N, K, stream)
+                           : launch_short<1, 2, 2, false>(wq, scales, biases, x, y, rec, N, K, stream);
     }
-  }
 #endif
+    // measured in the decode sweep: the per-CU layout for the layer widths; the
+    // vocabulary-wide head keeps the short workgroups
+    if (rpw < 2 * 16 * 16) return launch_per_cu<1, 4>(wq, scales, biases, x, y, N, K, stream);
+  }
   switch (B) {
-    case 1: return few_rows(N) ? launch_lds<1, 1, 4, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream)
-                               : launch_lds<1, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-    case 2: return launch_lds<2, 4, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-    case 3: return launch_lds<3, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-    case 4: return launch_lds<4, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-    case 5: return launch_lds<5, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-    case 6: return launch_lds<6, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-    case 7: return launch_lds<7, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
-    case 8: return launch_lds<8, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, ng, stream);
+    case 1: return few_rows(N) ? launch_short<1, 1, 4, AM>(wq, scales, biases, x, y, rec, N, K, stream)
+                               : launch_short<1, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+    case 2: return launch_short<2, 4, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+    case 3: return launch_short<3, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+    case 4: return launch_short<4, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+    case 5: return launch_short<5, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+    case 6: return launch_short<6, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+    case 7: return launch_short<7, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+    case 8: return launch_short<8, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
     default: return hipErrorInvalidValue;
   }
 }
