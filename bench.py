@@ -15,7 +15,7 @@ dominant kernel (the gate-up product), the oracle timed on the host cores, and
 secondary figures: lm_head+argmax microseconds per token, the prompt products
 at 512, 128, 64 and 16 rows (fp32 and, at 128, bf16 store), and the batch-8 sweep.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--batch 1]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--batch 1]
 """
 import argparse
 import json
@@ -46,7 +46,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--batch", type=int, default=1)
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     p.add_argument("--skip-extras", action="store_true",
@@ -216,12 +216,13 @@ def main():
         xs, xh = inputs(Bn)
         yo, yg, yd, logits, ids, ws = outputs(Bn)
 
-        def step():
+        def step(skip_gate_up=False):
             for l in range(LAYERS):
                 o, g, d = layers[l]
                 xo, xg, xd = xs[l]
                 w4g.qmm_gemv(o.wq, o.sc, o.bi, xo, yo)
-                w4g.qmm_gemv(g.wq, g.sc, g.bi, xg, yg)
+                if not skip_gate_up:
+                    w4g.qmm_gemv(g.wq, g.sc, g.bi, xg, yg)
                 w4g.qmm_gemv(d.wq, d.sc, d.bi, xd, yd)
             w4g.qmm_gemv(head.wq, head.sc, head.bi, xh, logits)
             w4g.vocab_argmax(logits, ids, ws)
@@ -264,26 +265,27 @@ def main():
     value = nbytes / (ms * 1e-3) / 1e9
     log(f"sweep B={B}: {ms * 1e3:.1f} us/step, {value:.0f} GB/s ({graph=}), wall {wall:.2f} s")
 
-    # dominant kernel: the gate-up product.  Its 16 launches of a step (one per
-    # layer's weights, so nothing is served from cache) run back to back in a
-    # graph on the same stream; HIP events around the replays give the average
-    # launch duration.
-    xg_in = [make_x(B, HIDDEN, 5, synth.GATE_UP, l, dev) for l in range(LAYERS)]
-    yg_out = torch.empty((B, 2 * INTER), dtype=torch.float32, device=dev)
-
-    def gate_up_only():
-        for l in range(LAYERS):
-            g = layers[l][1]
-            w4g.qmm_gemv(g.wq, g.sc, g.bi, xg_in[l], yg_out)
-    ms_g, _ = timed(gate_up_only, max(5, args.steps), 2, True)
-    gu_us = ms_g * 1e3 / LAYERS
+    # dominant kernel: the gate-up product, timed inside the sweep.  HIP events
+    # around graph replays time the step with and without its 16 gate-up
+    # launches (alternating, three rounds each, medians); the difference over 16
+    # is the average gate-up launch as it runs in the step, neighbours and the
+    # gap to the next kernel included.  (The same 16 launches alone, back to
+    # back, run slower; that figure is among the secondary ones.)
     gu_bytes = gemv_bytes(2 * INTER, HIDDEN, B)
+    with_gu, without_gu = [], []
+    for _ in range(3):
+        with_gu.append(timed(step, args.steps, 2, graph)[0])
+        without_gu.append(timed(lambda: step(skip_gate_up=True), args.steps, 2, graph)[0])
+    with_gu.sort()
+    without_gu.sort()
+    gu_us = (with_gu[1] - without_gu[1]) * 1e3 / LAYERS
     gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": counted_traffic() if B == 1 else None,
                 "kernel": "gemv_valu_kernel (gate_up 5120 -> 34816)", "avg_launch_us": round(gu_us, 2),
-                "bytes_per_launch": gu_bytes}
-    log(f"gate_up launch avg {gu_us:.2f} us -> {gu_gbs:.0f} GB/s")
+                "bytes_per_launch": gu_bytes, "method": "graph-timed step with minus without its 16 launches"}
+    log(f"gate_up launch avg {gu_us:.2f} us in the sweep ({with_gu[1] * 1e3:.1f} - {without_gu[1] * 1e3:.1f} "
+        f"us per step over {LAYERS}) -> {gu_gbs:.0f} GB/s")
 
     extras = {}
     if not args.skip_extras:
@@ -308,6 +310,17 @@ def main():
 
 def secondary(torch, w4g, synth, layers, head, dev, timed, args):
     ex = {}
+    # the 16 gate-up launches of a step alone, back to back in a graph
+    xg_in = [make_x(1, HIDDEN, 5, synth.GATE_UP, l, dev) for l in range(LAYERS)]
+    yg_out = torch.empty((1, 2 * INTER), dtype=torch.float32, device=dev)
+
+    def gate_up_only():
+        for l in range(LAYERS):
+            g = layers[l][1]
+            w4g.qmm_gemv(g.wq, g.sc, g.bi, xg_in[l], yg_out)
+    ms_g, _ = timed(gate_up_only, 10, 2, True)
+    ex["gate_up_b1_graph16_us"] = round(ms_g * 1e3 / LAYERS, 2)
+
     # lm_head + argmax per token (batch 1)
     xh = make_x(1, HIDDEN, 5, synth.LM_HEAD, 1, dev)
     logits = torch.empty((1, VOCAB), dtype=torch.float32, device=dev)
