@@ -9,6 +9,8 @@ arrays.  bf16 tensors travel as their uint16 bit patterns.
 Definitions followed (see the C file for the full statement and citations):
   * weights: 4-bit affine, group 64 (TensorFold PR #1437, "Receipt"),
     w = q*s + b with q in 0..15 packed low nibble first, 8 per uint32 along K;
+    other widths (2 and 8 bits, reading of the pages' simd_qmm_bits variant and
+    the B70 page's INT8 LM head): the same format with 32/bits codes per word;
   * products: fp32 result of sum_k x*w (TensorFold PR #1437, commit "Add the
     pair seam ...": fp32 payload and fp32-out store), summed in fp64;
   * argmax: any non-finite value in a row gives 0xFFFFFFFF, else the largest
@@ -58,6 +60,12 @@ def load(path=None):
     lib.w4o_argmax.restype = I
     lib.w4o_argmax_top2.argtypes = [P, I, I64, I64, I64, P, P, P]
     lib.w4o_argmax_top2.restype = I
+    lib.w4o_dequant_bits.argtypes = [P, P, P, I64, I64, I, P]
+    lib.w4o_dequant_bits.restype = I
+    lib.w4o_qmm_bits.argtypes = [P, P, P, P, P, I64, I64, I64, I, I]
+    lib.w4o_qmm_bits.restype = I
+    lib.w4o_qmm_rows_bits.argtypes = [P, P, P, P, P, I64, I64, I64, P, I64, I, I]
+    lib.w4o_qmm_rows_bits.restype = I
     lib.w4o_to_bf16.argtypes = [P, P, I64]
     lib.w4o_to_bf16.restype = None
     lib.w4o_plant.restype = I
@@ -77,9 +85,11 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _shapes(wq, scales, biases, x):
-    N, K8 = wq.shape
-    K = K8 * 8
+def _shapes(wq, scales, biases, x, bits=4):
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
+    N, words = wq.shape
+    K = words * 32 // bits
     if K % 64 or scales.shape != (N, K // 64) or biases.shape != (N, K // 64):
         raise ValueError("bad weight/scale/bias shapes")
     if x.ndim != 2 or x.shape[1] != K:
@@ -87,39 +97,50 @@ def _shapes(wq, scales, biases, x):
     return x.shape[0], N, K
 
 
-def dequant(wq, scales, biases, lib=None):
-    """fp32 [N][K] matrix of w = q*s + b."""
+def dequant(wq, scales, biases, lib=None, bits=4):
+    """fp32 [N][K] matrix of w = q*s + b (codes of `bits` bits, 32/bits per word)."""
     lib = lib or load()
     wq, scales, biases = _c(wq, np.uint32), _c(scales, np.uint16), _c(biases, np.uint16)
-    N, K = wq.shape[0], wq.shape[1] * 8
+    N, K = wq.shape[0], wq.shape[1] * 32 // bits
     w = np.empty((N, K), np.float32)
-    lib.w4o_dequant(_ptr(wq), _ptr(scales), _ptr(biases), N, K, _ptr(w))
+    if bits == 4:
+        lib.w4o_dequant(_ptr(wq), _ptr(scales), _ptr(biases), N, K, _ptr(w))
+    elif lib.w4o_dequant_bits(_ptr(wq), _ptr(scales), _ptr(biases), N, K, int(bits), _ptr(w)):
+        raise ValueError("bits must be 2, 4 or 8")
     return w
 
 
-def qmm(wq, scales, biases, x, threads=0, lib=None):
+def qmm(wq, scales, biases, x, threads=0, lib=None, bits=4):
     """y [M][N] fp32 = x [M][K] (bf16 bits) times dequantized W^T."""
     lib = lib or load()
     wq, scales, biases, x = (_c(wq, np.uint32), _c(scales, np.uint16), _c(biases, np.uint16),
                              _c(x, np.uint16))
-    M, N, K = _shapes(wq, scales, biases, x)
+    M, N, K = _shapes(wq, scales, biases, x, bits)
     y = np.empty((M, N), np.float32)
-    lib.w4o_qmm(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y), M, N, K, int(threads))
+    if bits == 4:
+        lib.w4o_qmm(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y), M, N, K, int(threads))
+    else:
+        lib.w4o_qmm_bits(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y), M, N, K, int(bits),
+                         int(threads))
     return y
 
 
-def qmm_rows(wq, scales, biases, x, rows, threads=0, lib=None):
+def qmm_rows(wq, scales, biases, x, rows, threads=0, lib=None, bits=4):
     """y [M][len(rows)]: only the listed output rows."""
     lib = lib or load()
     wq, scales, biases, x = (_c(wq, np.uint32), _c(scales, np.uint16), _c(biases, np.uint16),
                              _c(x, np.uint16))
-    M, N, K = _shapes(wq, scales, biases, x)
+    M, N, K = _shapes(wq, scales, biases, x, bits)
     rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
     if rows.size and (rows.min() < 0 or rows.max() >= N):
         raise IndexError("row out of range")
     y = np.empty((M, rows.size), np.float32)
-    lib.w4o_qmm_rows(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y), M, N, K,
-                     _ptr(rows), rows.size, int(threads))
+    if bits == 4:
+        lib.w4o_qmm_rows(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y), M, N, K,
+                         _ptr(rows), rows.size, int(threads))
+    else:
+        lib.w4o_qmm_rows_bits(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(y), M, N, K,
+                              _ptr(rows), rows.size, int(bits), int(threads))
     return y
 
 

@@ -17,6 +17,14 @@
  *    scale s and one bf16 bias b per (output row, 64-element K group); the
  *    dequantized weight is w = q*s + b.
  *
+ *  - Other widths: the pages' kernel takes widths other than 4 bits in a
+ *    separate variant (TensorFold PR #1433, review of step 2: other widths
+ *    take simd_qmm_bits), and the B70 page serves an INT8 LM head with bf16
+ *    scales.  Reading: the same affine group-64 format with b-bit unsigned
+ *    codes, b in {2, 4, 8}: 32/b codes per uint32, element (32/b) i + j in
+ *    bits [b j, b j + b) of word i, K b / 32 words per row, the same bf16
+ *    scale and bias tables.
+ *
  *  - Products: y[m][n] = sum_k x[m][k] * w[n][k], with an fp32 result (the
  *    seam's payload is fp32, "the seam's accumulation", and simd_qmm gains an
  *    fp32-out store: TensorFold PR #1437, commit "Add the pair seam and
@@ -79,7 +87,8 @@
    7 scale/bias tables read as [G][N], 8 -0.0 ordered below +0.0,
    9 fp32 accumulation, 10 activation row picked by the output row's stride,
    11 last K group dropped, 12 runner-up tie to the higher id,
-   13 bf16 store ties rounded away from zero */
+   13 bf16 store ties rounded away from zero, 14 high field first in a word
+   for widths other than 4, 15 8-bit rows read at the 4-bit pitch */
 
 /* bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits. */
 static float o_bf16_to_f32(uint16_t h) {
@@ -89,12 +98,33 @@ static float o_bf16_to_f32(uint16_t h) {
   return f;
 }
 
-/* code of element k in packed row `row` (K/8 words). */
+static int o_bits = 4; /* code width of the call in progress */
+
+/* code of element k in packed row `row` (K*bits/32 words). */
 static uint32_t o_code(const uint32_t* row, int64_t k) {
+  if (o_bits == 4) {
 #if W4O_PLANT == 1
-  return (row[k >> 3] >> (4 * (7 - (k & 7)))) & 0xFu;
+    return (row[k >> 3] >> (4 * (7 - (k & 7)))) & 0xFu;
 #else
-  return (row[k >> 3] >> (4 * (k & 7))) & 0xFu;
+    return (row[k >> 3] >> (4 * (k & 7))) & 0xFu;
+#endif
+  }
+  const int64_t per = 32 / o_bits; /* codes per word */
+  const uint32_t mask = (1u << o_bits) - 1u;
+#if W4O_PLANT == 14
+  const int64_t j = per - 1 - (k % per);
+#else
+  const int64_t j = k % per;
+#endif
+  return (row[k / per] >> (o_bits * j)) & mask;
+}
+
+/* words per packed row */
+static int64_t o_row_words(int64_t K) {
+#if W4O_PLANT == 15
+  return o_bits == 8 ? K / 8 : K * o_bits / 32; /* half the 8-bit pitch: stays in bounds */
+#else
+  return K * o_bits / 32;
 #endif
 }
 
@@ -111,7 +141,7 @@ static int64_t o_group(int64_t k) {
 static float o_weight(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                       int64_t N, int64_t K, int64_t n, int64_t k) {
   const int64_t G = K / 64;
-  float q = (float)o_code(wq + n * (K / 8), k);
+  float q = (float)o_code(wq + n * o_row_words(K), k);
 #if W4O_PLANT == 7
   float s = o_bf16_to_f32(scales[(o_group(k) * N + n) % (N * G)]);
   float b = o_bf16_to_f32(biases[(o_group(k) * N + n) % (N * G)]);
@@ -126,13 +156,14 @@ static float o_weight(const uint32_t* wq, const uint16_t* scales, const uint16_t
 #if W4O_PLANT == 6
   b = -b;
 #endif
-  float prod = q * s; /* exact: at most 4 x 8 significant bits */
+  float prod = q * s; /* exact: at most 8 x 8 significant bits */
   return prod + b;    /* the only rounding */
 }
 
 /* Dequantize a whole matrix to fp32, w[n][k] row-major. */
 void w4o_dequant(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                  int64_t N, int64_t K, float* w) {
+  o_bits = 4;
   o_groups = K / 64;
   for (int64_t n = 0; n < N; ++n)
     for (int64_t k = 0; k < K; ++k) w[n * K + k] = o_weight(wq, scales, biases, N, K, n, k);
@@ -174,6 +205,7 @@ static float o_dot(const uint32_t* wq, const uint16_t* scales, const uint16_t* b
 /* y[m][n] for all m < M and n < N.  x is [M][K] bf16, y is [M][N] fp32. */
 void w4o_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
              const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K, int threads) {
+  o_bits = 4;
   o_groups = K / 64;
 #ifdef _OPENMP
   if (threads < 1) threads = omp_get_max_threads();
@@ -190,6 +222,7 @@ void w4o_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
 void w4o_qmm_rows(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                   const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
                   const int64_t* rows, int64_t nrows, int threads) {
+  o_bits = 4;
   o_groups = K / 64;
 #ifdef _OPENMP
   if (threads < 1) threads = omp_get_max_threads();
@@ -200,6 +233,56 @@ void w4o_qmm_rows(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
   for (int64_t m = 0; m < M; ++m)
     for (int64_t j = 0; j < nrows; ++j)
       y[m * nrows + j] = o_dot(wq, scales, biases, x + o_xrow(m, M, N, K), N, K, rows[j]);
+}
+
+/* The same three products at code width `bits` (2, 4 or 8; anything else
+   returns 1 and computes nothing). */
+int w4o_dequant_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                     int64_t N, int64_t K, int bits, float* w) {
+  if (bits != 2 && bits != 4 && bits != 8) return 1;
+  o_groups = K / 64;
+  o_bits = bits;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) w[n * K + k] = o_weight(wq, scales, biases, N, K, n, k);
+  o_bits = 4;
+  return 0;
+}
+
+int w4o_qmm_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                 const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K, int bits, int threads) {
+  if (bits != 2 && bits != 4 && bits != 8) return 1;
+  o_groups = K / 64;
+  o_bits = bits;
+#ifdef _OPENMP
+  if (threads < 1) threads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(static) num_threads(threads)
+#else
+  (void)threads;
+#endif
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n)
+      y[m * N + n] = o_dot(wq, scales, biases, x + o_xrow(m, M, N, K), N, K, n);
+  o_bits = 4;
+  return 0;
+}
+
+int w4o_qmm_rows_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                      const uint16_t* x, float* y, int64_t M, int64_t N, int64_t K,
+                      const int64_t* rows, int64_t nrows, int bits, int threads) {
+  if (bits != 2 && bits != 4 && bits != 8) return 1;
+  o_groups = K / 64;
+  o_bits = bits;
+#ifdef _OPENMP
+  if (threads < 1) threads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(static) num_threads(threads)
+#else
+  (void)threads;
+#endif
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t j = 0; j < nrows; ++j)
+      y[m * nrows + j] = o_dot(wq, scales, biases, x + o_xrow(m, M, N, K), N, K, rows[j]);
+  o_bits = 4;
+  return 0;
 }
 
 static int o_finite(float v) {

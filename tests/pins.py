@@ -15,7 +15,10 @@ What fixes the expected values (never the oracle itself, never the GPU):
   * invariants: row permutation, power-of-two scaling, negation;
   * argmax: hand-built rows for each rule and numpy's argmax (first
     occurrence) on finite rows;
-  * bf16 store: hand-worked roundings and torch's CPU bfloat16 conversion.
+  * bf16 store: hand-worked roundings and torch's CPU bfloat16 conversion;
+  * 2- and 8-bit codes: tables packed with numpy's little-endian views and bit
+    packing, read back one weight at a time, as an integer mat-vec and by exact
+    rational brute force.
 """
 import json
 import os
@@ -363,9 +366,83 @@ def pin_bf16_store(lib):
     assert bad.size == 0, [(allv[i], hex(got[i]), hex(want[i])) for i in bad[:5]]
 
 
+def pack_codes(codes, bits):
+    """[N][K] codes -> [N][K*bits/32] uint32 words, element (32/bits) i + j in bits
+    [bits j, bits j + bits) of word i, built with numpy's little-endian views and
+    bit packing rather than shifts: 8-bit codes are the bytes of little-endian
+    words; 2- and 4-bit codes are a little-endian bit stream."""
+    codes = np.ascontiguousarray(codes)
+    N, K = codes.shape
+    if bits == 8:
+        return codes.astype(np.uint8).view("<u4").reshape(N, K // 4).astype(np.uint32)
+    bitplanes = ((codes[..., None].astype(np.uint32) >> np.arange(bits, dtype=np.uint32)) & 1).astype(np.uint8)
+    packed = np.packbits(bitplanes.reshape(N, K * bits), axis=1, bitorder="little")
+    return packed.view("<u4").reshape(N, K * bits // 32).astype(np.uint32)
+
+
+def pin_bits_hand_dequant(lib):
+    """Other widths: s = 2^-6, b = -1/8, so w = q/64 - 1/8 exactly; one-hot x reads
+    single weights (every field position of a word, both sides of a group boundary)
+    and the dequantized table matches code by code."""
+    for bits in (2, 8):
+        r = np.random.default_rng(bits)
+        N, K = 3, 128
+        codes = r.integers(0, 1 << bits, size=(N, K), dtype=np.int64)
+        codes[0, :4] = [0, (1 << bits) - 1, 1, (1 << bits) // 2]
+        wq = pack_codes(codes, bits)
+        sc = np.full((N, K // 64), _bf16(2.0 ** -6), np.uint16)
+        bi = np.full((N, K // 64), _bf16(-0.125), np.uint16)
+        want = codes.astype(np.float64) / 64.0 - 0.125
+        w = oracle.dequant(wq, sc, bi, lib=lib, bits=bits)
+        assert np.array_equal(w.astype(np.float64), want), bits
+        for k in list(range(0, 32 // bits + 1)) + [63, 64, 65, K - 1]:
+            x = np.zeros((1, K), np.uint16)
+            x[0, k] = _bf16(1.0)
+            y = oracle.qmm(wq, sc, bi, x, lib=lib, bits=bits)
+            assert np.array_equal(y[0].astype(np.float64), want[:, k]), (bits, k)
+
+
+def pin_bits_integer_matvec(lib):
+    """Other widths with s = 1, b = 0 and small integer x: an integer mat-vec,
+    compared with numpy's int64 matmul (exact in fp32 at these sizes)."""
+    for bits in (2, 8):
+        r = np.random.default_rng(100 + bits)
+        N, K, M = 7, 256, 3
+        codes = r.integers(0, 1 << bits, size=(N, K), dtype=np.int64)
+        xi = r.integers(-8, 9, size=(M, K), dtype=np.int64)
+        x = np.vectorize(lambda v: _bf16(float(v)))(xi).astype(np.uint16)
+        sc = np.full((N, K // 64), _bf16(1.0), np.uint16)
+        bi = np.zeros((N, K // 64), np.uint16)
+        y = oracle.qmm(pack_codes(codes, bits), sc, bi, x, lib=lib, bits=bits)
+        assert np.array_equal(y.astype(np.int64), xi @ codes.T), bits
+
+
+def pin_bits_bruteforce(lib):
+    """Other widths: exact rational evaluation of tiny products with random bf16
+    scales, biases and activations, rounded once to fp32."""
+    for bits in (2, 8):
+        r = np.random.default_rng(200 + bits)
+        N, K, M = 2, 128, 2
+        codes = r.integers(0, 1 << bits, size=(N, K), dtype=np.int64)
+        sc = synth.f32_to_bf16_bits(r.uniform(0.002, 0.02, (N, K // 64)).astype(np.float32))
+        bi = synth.f32_to_bf16_bits(r.normal(0, 0.05, (N, K // 64)).astype(np.float32))
+        x = synth.f32_to_bf16_bits(r.normal(0, 1, (M, K)).astype(np.float32))
+        y = oracle.qmm(pack_codes(codes, bits), sc, bi, x, lib=lib, bits=bits)
+        xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+        sf = synth.bf16_bits_to_f32(sc).astype(np.float64)
+        bf = synth.bf16_bits_to_f32(bi).astype(np.float64)
+        for m in range(M):
+            for n in range(N):
+                tot = Fraction(0)
+                for k in range(K):
+                    w = Fraction(np.float32(codes[n, k] * sf[n, k // 64] + bf[n, k // 64]).item())
+                    tot += Fraction(xf[m, k].item()) * w
+                assert y[m, n] == np.float32(frac_to_f32(tot)), (bits, m, n)
+
+
 PRODUCT_PINS = [pin_hand_dequant, pin_closed_form, pin_integer_matvec, pin_scale_bias_layout,
                 pin_bruteforce, pin_numpy_dot, pin_dequant_bits, pin_invariants, pin_rows_subset,
-                pin_bf16_store]
+                pin_bf16_store, pin_bits_hand_dequant, pin_bits_integer_matvec, pin_bits_bruteforce]
 ARGMAX_PINS = [pin_argmax_rules, pin_argmax_numpy, pin_argmax_bf16_nonfinite, pin_top2_rules,
                pin_top2_lexsort]
 ALL_PINS = PRODUCT_PINS + ARGMAX_PINS

@@ -26,6 +26,8 @@ PLANTS = {
     11: "last K group dropped",
     12: "runner-up tie to the higher id",
     13: "bf16 store ties away from zero",
+    14: "high field first at other widths",
+    15: "8-bit rows at the 4-bit pitch",
 }
 
 
