@@ -108,11 +108,11 @@ def probe(kind):
 class Mat:
     """One quantized matrix resident on the GPU."""
 
-    def __init__(self, N, K, workload, matrix, layer, dev):
+    def __init__(self, N, K, workload, matrix, layer, dev, bits=4):
         from w4_gemv_greedy_amd import synth
         import torch
-        wq, sc, bi = synth.weights(N, K, workload=workload, matrix=matrix, layer=layer)
-        self.N, self.K = N, K
+        wq, sc, bi = synth.weights(N, K, workload=workload, matrix=matrix, layer=layer, bits=bits)
+        self.N, self.K, self.bits = N, K, bits
         self.wq = torch.from_numpy(wq.view(np.int32)).to(dev)
         self.sc = torch.from_numpy(sc.view(np.int16)).to(dev).view(torch.bfloat16)
         self.bi = torch.from_numpy(bi.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -389,6 +389,35 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args):
                                                       "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
     log("per-product: " + ", ".join(f"{k} {v['us']}us {v['GBps']}GB/s" for k, v in ex.items()
                                     if k.startswith("gemv_")))
+
+    # other code widths (B = 1): the 8-bit LM head with the greedy argmax, and the
+    # gate-up product at 8 and 2 bits, cycling over enough copies that none is
+    # served from the 256 MB cache
+    head8 = Mat(VOCAB, HIDDEN, 5, synth.LM_HEAD, 0, dev, bits=8)
+
+    def head8_step():
+        w4g.qmm_gemv(head8.wq, head8.sc, head8.bi, xh, logits, bits=8)
+        w4g.vocab_argmax(logits, ids, ws)
+    ms, _ = timed(head8_step, 10, 2, True, reps=4)
+    ex["w8_lm_head_argmax_us_per_token"] = round(ms * 1e3, 2)
+    ex["w8_lm_head_argmax_GBps"] = round((1.0625 * VOCAB * HIDDEN + 2 * HIDDEN + 8 * VOCAB) / (ms * 1e-3) / 1e9, 1)
+    del head8
+    xg1 = make_x(1, HIDDEN, 5, synth.GATE_UP, 0, dev)
+    yg1 = torch.empty((1, 2 * INTER), dtype=torch.float32, device=dev)
+    for bits, copies in ((8, 4), (2, 6)):
+        mats = [Mat(2 * INTER, HIDDEN, 5, synth.GATE_UP, l, dev, bits=bits) for l in range(copies)]
+
+        def run_bits(mats=mats, bits=bits):
+            for m in mats:
+                w4g.qmm_gemv(m.wq, m.sc, m.bi, xg1, yg1, bits=bits)
+        ms, _ = timed(run_bits, 10, 2, True)
+        us = ms * 1e3 / copies
+        nb = (bits / 8 + 0.0625) * 2 * INTER * HIDDEN + 2 * HIDDEN + 4 * 2 * INTER
+        ex[f"w{bits}_gate_up_b1"] = {"us": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
+        del mats
+    log(f"other widths: w8 lm_head+argmax {ex['w8_lm_head_argmax_us_per_token']} us/token "
+        f"({ex['w8_lm_head_argmax_GBps']} GB/s), w8 gate_up {ex['w8_gate_up_b1']}, w2 gate_up {ex['w2_gate_up_b1']}")
+    torch.cuda.empty_cache()
 
     # prompt products: the 512-row pass, the 128-row round and short prompts of 64
     # and 16 rows (where the weight stream, not the matrix cores, sets the time).

@@ -110,6 +110,30 @@ int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
              const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode product with codes of another width.  Same arguments, layout and
+ * result as qmm_gemv, plus `bits` in {2, 4, 8} (else W4G_EDTYPE): wq is
+ * [N][K*bits/32] uint32, element (32/bits) i + j of a row in bits
+ * [bits j, bits j + bits) of word i (low field first), an unsigned code
+ * 0 .. 2^bits - 1, with the same bf16 scale and bias per (row, 64-group):
+ * w = q*s + b.  bits = 4 is exactly qmm_gemv.  The pages' kernel takes widths
+ * other than 4 bits in its simd_qmm_bits variant (TensorFold PR #1433, review
+ * of step 2) and the B70 page serves an INT8 LM head with bf16 scales
+ * (b70-optimization-lab, "Reproduce Qwen3.6 27B AutoRound Bring-Up", current
+ * best profile); reading: the same affine group-64 format at those widths.
+ * Widths 2 and 8 run on the vector ALUs with x staged in LDS, so they need
+ * B * 2.125 * K bytes <= 152 KiB (else W4G_ESHAPE).  Order per row, K only:
+ * as qmm_gemv's, with each lane's 32-element segment taken as its code words
+ * in order; 2-bit: within a word fields (j, j + 8) form one bf16 pair
+ * (128 + q), j ascending; 8-bit: a code is its two nibbles, Dl over the low
+ * and Dh over the high nibbles (each 128 + nibble, pairs (q0, q2), (q1, q3)
+ * per word), the segment's term is fma(16, Dh, Dl), and the constant part
+ * folds into b - 2176 s.
+ */
+int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                  const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K, int bits,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* kernel families for qmm_gemv_ex */
 #define W4G_GEMV_AUTO 0   /* the library's choice by B and shape (what qmm_gemv uses) */
 #define W4G_GEMV_VALU 1   /* vector-ALU dot2 kernel (the order documented for qmm_gemv) */

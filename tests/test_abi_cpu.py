@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert set(names) >= {"qmm_gemv", "qmm_gemv_ex", "qmm_gemm", "qmm_gemm_ex", "qmm_gemv_argmax", "vocab_argmax",
+    assert set(names) >= {"qmm_gemv", "qmm_gemv_ex", "qmm_gemv_bits", "qmm_gemm", "qmm_gemm_ex", "qmm_gemv_argmax", "vocab_argmax",
                           "vocab_argmax_top2",
                           "qmm_workspace_bytes", "w4g_status_string", "w4g_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -96,6 +96,25 @@ def test_gemv_rejects(lib):
     assert gemv(lib, y=SC) == _lib.EALIAS
     assert gemv(lib, kernel=7) == _lib.EDTYPE
     assert gemv(lib, kernel=-1) == _lib.EDTYPE
+
+
+def test_gemv_bits_rejects(lib):
+    call = lambda **k: lib.qmm_gemv_bits(k.get("wq", WQ), SC, BI, X, k.get("y", Y), k.get("B", 1),
+                                         k.get("N", 64), k.get("K", 128), k.get("bits", 8), None, 0, None)
+    assert call(bits=3) == _lib.EDTYPE
+    assert call(bits=16) == _lib.EDTYPE
+    assert call(wq=None) == _lib.EINVAL_PTR
+    assert call(B=0) == _lib.ESHAPE
+    assert call(B=9) == _lib.ESHAPE
+    assert call(K=96) == _lib.ESHAPE
+    assert call(wq=WQ + 4) == _lib.EALIGN
+    assert call(y=X) == _lib.EALIAS
+    # an 8-bit table is twice a 4-bit one: y just past the 4-bit extent still overlaps it
+    assert call(y=WQ + 64 * (128 // 8) * 4) == _lib.EALIAS
+    assert call(bits=2, y=WQ + 64 * (128 // 16) * 4 - 16) == _lib.EALIAS
+    # x must fit in LDS at widths other than 4: B * 2.125 * K bytes <= 152 KiB
+    assert call(B=8, K=17408) == _lib.ESHAPE
+    assert call(bits=2, B=5, K=17408) == _lib.ESHAPE
 
 
 def test_gemm_rejects(lib):

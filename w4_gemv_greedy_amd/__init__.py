@@ -48,14 +48,16 @@ def _need(t, name, dtypes, ndim, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _check_qmm(wq, scales, biases, x):
+def _check_qmm(wq, scales, biases, x, bits=4):
     torch = _torch()
     _need(wq, "wq", (torch.int32, torch.uint32), 2, None)
     dev = wq.device
     _need(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), 2, dev)
     _need(biases, "biases", (torch.bfloat16, torch.int16, torch.uint16), 2, dev)
     _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2, dev)
-    N, K = wq.shape[0], wq.shape[1] * 8
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
+    N, K = wq.shape[0], wq.shape[1] * 32 // bits
     if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
         raise ValueError("scales and biases must be [N][K/64]")
     if x.shape[1] != K:
@@ -101,14 +103,31 @@ def _call_qmm(fn, op, wq, scales, biases, x, y, workspace, extra=(), y_dtypes=No
     return y
 
 
-def qmm_gemv(wq, scales, biases, x, y=None, workspace=None, kernel=GEMV_AUTO):
+def qmm_gemv(wq, scales, biases, x, y=None, workspace=None, kernel=GEMV_AUTO, bits=4):
     """Decode product for 1 <= B <= 8 rows of x; returns y [B][N] fp32.
 
     kernel: GEMV_AUTO (the library's choice), GEMV_VALU, GEMV_MFMA, or
     GEMV_VALU_REGS (the register-staged variant of the vector-ALU family).
+    bits: code width, 4 (the default) or 2 or 8 (wq [N][K*bits/32], low field
+    first; the library's choice of kernel only).
     """
     if x.dim() == 2 and not 1 <= x.shape[0] <= MAX_GEMV_BATCH:
         raise ValueError(f"qmm_gemv takes 1..{MAX_GEMV_BATCH} rows")
+    if bits != 4:
+        if kernel != GEMV_AUTO:
+            raise ValueError("other code widths take the library's kernel choice only")
+        torch = _torch()
+        N, K = _check_qmm(wq, scales, biases, x, bits)
+        rows = x.shape[0]
+        if y is None:
+            y = torch.empty((rows, N), dtype=torch.float32, device=wq.device)
+        _need(y, "y", (torch.float32,), 2, wq.device)
+        if tuple(y.shape) != (rows, N):
+            raise ValueError(f"y must be [{rows}][{N}]")
+        status = _lib.load().qmm_gemv_bits(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
+                                           y.data_ptr(), rows, N, K, int(bits), None, 0, _stream(wq))
+        _lib.check("qmm_gemv_bits", status)
+        return y
     if kernel == GEMV_AUTO:
         return _call_qmm("qmm_gemv", OP_GEMV, wq, scales, biases, x, y, workspace)
     return _call_qmm("qmm_gemv_ex", OP_GEMV, wq, scales, biases, x, y, workspace, (int(kernel),))

@@ -15,7 +15,7 @@ ABI_VERSION = 1
 
 GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_VALU_REGS = 0, 1, 2, 3
 
-EXPORTS = ["qmm_gemv", "qmm_gemv_ex", "qmm_gemm", "qmm_gemm_ex", "qmm_gemv_argmax", "vocab_argmax",
+EXPORTS = ["qmm_gemv", "qmm_gemv_ex", "qmm_gemv_bits", "qmm_gemm", "qmm_gemm_ex", "qmm_gemv_argmax", "vocab_argmax",
            "vocab_argmax_top2", "qmm_workspace_bytes", "w4g_status_string", "w4g_abi_version"]
 
 _lib = None
@@ -41,6 +41,8 @@ def load(path=None):
     lib.qmm_gemv.restype = I
     lib.qmm_gemv_ex.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P, I]
     lib.qmm_gemv_ex.restype = I
+    lib.qmm_gemv_bits.argtypes = [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]
+    lib.qmm_gemv_bits.restype = I
     lib.qmm_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.qmm_gemm.restype = I
     lib.qmm_gemm_ex.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P, I]

@@ -23,7 +23,8 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;  // rows, columns and batch below 
 
 int check_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
               const uint16_t* x, const void* y, int64_t rows, int64_t N, int64_t K,
-              const void* workspace, size_t workspace_bytes, size_t need, size_t ysize = 4) {
+              const void* workspace, size_t workspace_bytes, size_t need, size_t ysize = 4,
+              int bits = 4) {
   if (!wq || !scales || !biases || !x || !y) return W4G_EINVAL_PTR;
   if (rows < 1 || rows >= kMaxDim || N < 1 || N >= kMaxDim || K < 64 || K >= kMaxDim || K % 64)
     return W4G_ESHAPE;
@@ -32,7 +33,7 @@ int check_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases
   if (need > 0 && (!workspace || workspace_bytes < need)) return W4G_EWORKSPACE;
   if (need > 0 && !aligned16(workspace)) return W4G_EALIGN;
   const size_t ybytes = (size_t)rows * (size_t)N * ysize;
-  const size_t wbytes = (size_t)N * (size_t)(K / 8) * sizeof(uint32_t);
+  const size_t wbytes = (size_t)N * (size_t)(K * bits / 32) * sizeof(uint32_t);
   const size_t gbytes = (size_t)N * (size_t)(K / 64) * sizeof(uint16_t);
   const size_t xbytes = (size_t)rows * (size_t)K * sizeof(uint16_t);
   if (overlap(y, ybytes, wq, wbytes) || overlap(y, ybytes, scales, gbytes) ||
@@ -115,6 +116,22 @@ int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* bias
     return from_hip(w4g::launch_gemv_mfma(wq, scales, biases, x, y, (int)B, N, K, s));
   return from_hip(w4g::launch_gemv(wq, scales, biases, x, y, (int)B, N, K,
                                    kernel == W4G_GEMV_VALU_REGS, s));
+}
+
+int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                  const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K, int bits,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (bits != 2 && bits != 4 && bits != 8) return W4G_EDTYPE;
+  if (bits == 4)
+    return qmm_gemv_ex(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, stream,
+                       W4G_GEMV_AUTO);
+  if (B < 1 || B > W4G_MAX_GEMV_BATCH)
+    return (!wq || !scales || !biases || !x || !y) ? W4G_EINVAL_PTR : W4G_ESHAPE;
+  const int rc = check_qmm(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, 0, 4, bits);
+  if (rc) return rc;
+  if (!w4g::gemv_bits_fits((int)B, K)) return W4G_ESHAPE;
+  return from_hip(w4g::launch_gemv_bits(wq, scales, biases, x, y, (int)B, N, K, bits,
+                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
 int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,

@@ -106,9 +106,70 @@ __device__ __forceinline__ float half_wave_sum(float v) {
   return v;
 }
 
-template <int R>
+// Other code widths (2 and 8 bits: 32/bits codes per uint32, low field first).
+// 2-bit: word t of a lane's 32 elements covers elements 16t .. 16t + 15; field j
+// and field j + 8 go to one bf16 pair (128 + q[j], 128 + q[j + 8]) with one
+// v_and_or_b32, against the x pair (x[j], x[j + 8]).
+__device__ __forceinline__ float dot_word2(uint32_t w, uint4 xa, uint4 xb, float d, uint32_t g) {
+  const uint32_t m2 = 0x00030003u;
+  d = dot2(and_or(w, m2, g), xa.x, d);
+  d = dot2(and_or(w >> 2, m2, g), xa.y, d);
+  d = dot2(and_or(w >> 4, m2, g), xa.z, d);
+  d = dot2(and_or(w >> 6, m2, g), xa.w, d);
+  d = dot2(and_or(w >> 8, m2, g), xb.x, d);
+  d = dot2(and_or(w >> 10, m2, g), xb.y, d);
+  d = dot2(and_or(w >> 12, m2, g), xb.z, d);
+  d = dot2(and_or(w >> 14, m2, g), xb.w, d);
+  return d;
+}
+// 8-bit: a code q = 16 h + l is taken as its two nibbles; word t covers
+// elements 4t .. 4t + 3; pairs (l[0], l[2]), (l[1], l[3]) against (x0, x2),
+// (x1, x3) accumulate Dl, the high nibbles likewise Dh (each 128 + nibble).
+__device__ __forceinline__ void dot_word8(uint32_t w, uint32_t p0, uint32_t p1, float& dl, float& dh,
+                                          uint32_t m, uint32_t g) {
+  dl = dot2(and_or(w, m, g), p0, dl);
+  dl = dot2(and_or(w >> 8, m, g), p1, dl);
+  dh = dot2(and_or(w >> 4, m, g), p0, dh);
+  dh = dot2(and_or(w >> 12, m, g), p1, dh);
+}
+// x pairs for those orders, from natural pairs: 2-bit, a 16-element block
+// (a, b) -> (x[j], x[j + 8]) for j = 0..3 and 4..7; 8-bit, each 4-element
+// block -> (x0, x2), (x1, x3).
+__device__ __forceinline__ void pair_x2(uint4 a, uint4 b, uint4& lo, uint4& hi) {
+  lo.x = __builtin_amdgcn_perm(b.x, a.x, 0x05040100u);
+  lo.y = __builtin_amdgcn_perm(b.x, a.x, 0x07060302u);
+  lo.z = __builtin_amdgcn_perm(b.y, a.y, 0x05040100u);
+  lo.w = __builtin_amdgcn_perm(b.y, a.y, 0x07060302u);
+  hi.x = __builtin_amdgcn_perm(b.z, a.z, 0x05040100u);
+  hi.y = __builtin_amdgcn_perm(b.z, a.z, 0x07060302u);
+  hi.z = __builtin_amdgcn_perm(b.w, a.w, 0x05040100u);
+  hi.w = __builtin_amdgcn_perm(b.w, a.w, 0x07060302u);
+}
+__device__ __forceinline__ uint4 pair_x8(uint4 v) {
+  uint4 p;
+  p.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (x0, x2)
+  p.y = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (x1, x3)
+  p.z = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (x4, x6)
+  p.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (x5, x7)
+  return p;
+}
+
+// One lane's codes of one row and chunk: 32 codes = 4 BITS bytes, loaded as
+// VPL vectors of type V.
+template <int BITS>
+struct CodeVec {
+  typedef uint4 V;
+  static constexpr int VPL = BITS / 4;
+};
+template <>
+struct CodeVec<2> {
+  typedef uint2 V;
+  static constexpr int VPL = 1;
+};
+
+template <int R, int BITS = 4>
 struct Item {
-  uint4 w[R];
+  typename CodeVec<BITS>::V w[R][CodeVec<BITS>::VPL];
   uint16_t s[R], b[R];  // kept 16-bit so no widening copy waits on the loads
 };
 
@@ -127,7 +188,7 @@ struct Item {
 // after the stream one thread per batch row writes the record of the best
 // (value, lowest row), or the non-finite flag, to rec[bb][blockIdx.x]; y may
 // then be null.
-template <int B, int R, int P, bool RAGGED, bool AM, int MAXT = kThreads>
+template <int B, int R, int P, bool RAGGED, bool AM, int MAXT = kThreads, int BITS = 4>
 __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restrict__ wq,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint16_t* __restrict__ biases,
@@ -136,7 +197,9 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
                                                          int64_t K, int64_t rpw,
                                                          uint2* __restrict__ rec) {
   extern __shared__ uint4 s_mem[];
-  const int64_t K8 = K >> 3, K32 = K >> 5, G = K >> 6;
+  typedef typename CodeVec<BITS>::V V;
+  constexpr int VPL = CodeVec<BITS>::VPL;
+  const int64_t KW = K * BITS / 32, K32 = K >> 5, G = K >> 6;  // KW: code words per row
   const int C = (int)((K + kChunk - 1) / kChunk);
   uint4* s_xp = s_mem;                                                   // [B][C][4][32]
   float* s_xh = reinterpret_cast<float*>(s_mem + (int64_t)B * C * 128);  // [B][C][32]
@@ -157,7 +220,7 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
 
   // this lane's position in the rows of the group being loaded (set once per
   // group); an item adds the chunk's offset to each
-  const uint4* pw[R];
+  const V* pw[R];
   const uint16_t* ps[R];
   const uint16_t* pb[R];
   int64_t prow = row_begin;
@@ -165,7 +228,7 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t row = prow + r < wg_end ? prow + r : wg_end - 1;
-      pw[r] = reinterpret_cast<const uint4*>(wq + row * K8) + lane;
+      pw[r] = reinterpret_cast<const V*>(wq + row * KW) + VPL * lane;
       ps[r] = scales + row * G + (lane >> 1);
       pb[r] = biases + row * G + (lane >> 1);
     }
@@ -175,15 +238,16 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
   // Loads the next item.  The stream below never asks for an item past the
   // last one, except in the prologue when a half wave has fewer than P items;
   // those loads read clamped, valid rows and are never consumed.
-  auto issue = [&](Item<R>& it) {
-    int vo = pc * 32, go = pc * 16;  // vector and group offsets of the chunk
+  auto issue = [&](Item<R, BITS>& it) {
+    int vo = pc * 32 * VPL, go = pc * 16;  // vector and group offsets of the chunk
     if (RAGGED && pc == C - 1 && lane >= last_lanes) {  // past the end: lane 0's data
-      vo = -lane;
+      vo = -VPL * lane;
       go = -(lane >> 1);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      it.w[r] = pw[r][vo];
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) it.w[r][v] = pw[r][vo + v];
       it.s[r] = ps[r][go];
       it.b[r] = pb[r][go];
     }
@@ -203,9 +267,14 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
     const int64_t sg = seg % K32;
     const int64_t c = sg >> 5, l = sg & 31;
     float h = 0.0f;
+    uint4 pr[4];
+    if constexpr (BITS == 2) {
+      pair_x2(raw[0], raw[1], pr[0], pr[1]);
+      pair_x2(raw[2], raw[3], pr[2], pr[3]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 p = pair_x(raw[i]);
+      const uint4 p = BITS == 4 ? pair_x(raw[i]) : BITS == 8 ? pair_x8(raw[i]) : pr[i];
       s_xp[((int64_t)bb * C + c) * 128 + i * 32 + l] = p;
       h = dot2(p.x, kOnes, h);
       h = dot2(p.y, kOnes, h);
@@ -228,7 +297,7 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
     if (seg < nseg) load_seg(seg, pre[q]);
   }
 
-  Item<R> ring[P];
+  Item<R, BITS> ring[P];
 #pragma unroll
   for (int sl = 0; sl < P; ++sl) issue(ring[sl]);
 
@@ -258,7 +327,7 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
 
   const uint4* xlane = s_xp + lane;
   const float* hlane = s_xh + lane;
-  auto consume = [&](const Item<R>& it, int64_t item) {
+  auto consume = [&](const Item<R, BITS>& it, int64_t item) {
     if (item < n_items) {
       // a lane past the end of a short last chunk reads lane 0 of chunk 0
       // (always staged, so finite) and scales it by exact zeros
@@ -273,7 +342,9 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         sc[r] = bf16_to_f32(it.s[r]);
-        cb[r] = __builtin_fmaf(-128.0f, sc[r], bf16_to_f32(it.b[r]));
+        // the constant part of the expanded codes: 128 per code, 128 + 16 * 128
+        // per 8-bit code (two nibbles)
+        cb[r] = __builtin_fmaf(BITS == 8 ? -2176.0f : -128.0f, sc[r], bf16_to_f32(it.b[r]));
         if (RAGGED && !active) sc[r] = cb[r] = 0.0f;
       }
 #pragma unroll
@@ -284,10 +355,26 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           float d = 0.0f;
-          d = dot_word(it.w[r].x, x0, d, m, g);
-          d = dot_word(it.w[r].y, x1, d, m, g);
-          d = dot_word(it.w[r].z, x2, d, m, g);
-          d = dot_word(it.w[r].w, x3, d, m, g);
+          if constexpr (BITS == 4) {
+            d = dot_word(it.w[r][0].x, x0, d, m, g);
+            d = dot_word(it.w[r][0].y, x1, d, m, g);
+            d = dot_word(it.w[r][0].z, x2, d, m, g);
+            d = dot_word(it.w[r][0].w, x3, d, m, g);
+          } else if constexpr (BITS == 2) {
+            d = dot_word2(it.w[r][0].x, x0, x1, d, g);
+            d = dot_word2(it.w[r][0].y, x2, x3, d, g);
+          } else {
+            float dl = 0.0f, dh = 0.0f;
+            dot_word8(it.w[r][0].x, x0.x, x0.y, dl, dh, m, g);
+            dot_word8(it.w[r][0].y, x0.z, x0.w, dl, dh, m, g);
+            dot_word8(it.w[r][0].z, x1.x, x1.y, dl, dh, m, g);
+            dot_word8(it.w[r][0].w, x1.z, x1.w, dl, dh, m, g);
+            dot_word8(it.w[r][1].x, x2.x, x2.y, dl, dh, m, g);
+            dot_word8(it.w[r][1].y, x2.z, x2.w, dl, dh, m, g);
+            dot_word8(it.w[r][1].z, x3.x, x3.y, dl, dh, m, g);
+            dot_word8(it.w[r][1].w, x3.z, x3.w, dl, dh, m, g);
+            d = __builtin_fmaf(16.0f, dh, dl);  // sum x q = Dl + 16 Dh - 2176 X
+          }
           acc[r][bb] = __builtin_fmaf(sc[r], d, acc[r][bb]);
           acc[r][bb] = __builtin_fmaf(cb[r], xh, acc[r][bb]);
         }
@@ -464,15 +551,15 @@ int lds_rows_per_item(int B, int64_t N) { return B == 1 ? (few_rows(N) ? 1 : 2) 
 int regs_rows(int B) { return B <= 2 ? 4 : 2; }
 bool use_regs(int B, int64_t K, bool force_regs) { return force_regs || lds_bytes(B, K) > kMaxLds; }
 
-template <int B, int R, int P, bool AM, int MAXT = kThreads>
+template <int B, int R, int P, bool AM, int MAXT = kThreads, int BITS = 4>
 hipError_t launch_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                       const uint16_t* x, float* y, uint2* rec, int64_t N, int64_t K, int64_t rpw,
                       int threads, hipStream_t stream) {
   const bool ragged = (K % kChunk) != 0;
   const int64_t blocks = (N + rpw - 1) / rpw;
   const size_t lds = lds_bytes(B, K);
-  const void* fn = ragged ? reinterpret_cast<const void*>(&gemv_valu_kernel<B, R, P, true, AM, MAXT>)
-                          : reinterpret_cast<const void*>(&gemv_valu_kernel<B, R, P, false, AM, MAXT>);
+  const void* fn = ragged ? reinterpret_cast<const void*>(&gemv_valu_kernel<B, R, P, true, AM, MAXT, BITS>)
+                          : reinterpret_cast<const void*>(&gemv_valu_kernel<B, R, P, false, AM, MAXT, BITS>);
   if (lds > kDefaultLds) {
     // a host-side attribute of the kernel, set before each such launch (not a
     // stream operation, so it is also fine while a graph is being captured)
@@ -480,10 +567,10 @@ hipError_t launch_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t
     if (e != hipSuccess) return e;
   }
   if (ragged)
-    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, true, AM, MAXT>), dim3((unsigned)blocks), dim3(threads), lds,
-                       stream, wq, scales, biases, x, y, N, K, rpw, rec);
+    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, true, AM, MAXT, BITS>), dim3((unsigned)blocks), dim3(threads),
+                       lds, stream, wq, scales, biases, x, y, N, K, rpw, rec);
   else
-    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, false, AM, MAXT>), dim3((unsigned)blocks), dim3(threads),
+    hipLaunchKernelGGL((gemv_valu_kernel<B, R, P, false, AM, MAXT, BITS>), dim3((unsigned)blocks), dim3(threads),
                        lds, stream, wq, scales, biases, x, y, N, K, rpw, rec);
   return hipGetLastError();
 }
@@ -491,24 +578,25 @@ hipError_t launch_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t
 // 256 threads, one group of R rows per half wave: many short workgroups, which
 // the dispatcher spreads over the CUs as they free up (the fused head's layout:
 // one record per workgroup)
-template <int B, int R, int P, bool AM>
+template <int B, int R, int P, bool AM, int BITS = 4>
 hipError_t launch_short(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                         const uint16_t* x, float* y, uint2* rec, int64_t N, int64_t K,
                         hipStream_t stream) {
-  return launch_lds<B, R, P, AM>(wq, scales, biases, x, y, rec, N, K, (int64_t)kHalfWaves * R, kThreads,
-                                 stream);
+  return launch_lds<B, R, P, AM, kThreads, BITS>(wq, scales, biases, x, y, rec, N, K,
+                                                 (int64_t)kHalfWaves * R, kThreads, stream);
 }
 
 // One workgroup per CU, each with an equal share of the rows (so every CU
 // streams the same number of bytes and no second round of workgroups
 // trails; x is staged once per CU): up to 32 rows per CU one row per half
 // wave, else 16 half waves striding through the share, R rows per item.
-template <int R, int P>
+template <int R, int P, int BITS = 4>
 hipError_t launch_per_cu(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                          const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t rpw = (N + kCUs - 1) / kCUs;
   const int threads = rpw <= 32 ? 64 * (int)((rpw + 1) / 2) : 512;
-  return launch_lds<1, R, P, false, 1024>(wq, scales, biases, x, y, nullptr, N, K, rpw, threads, stream);
+  return launch_lds<1, R, P, false, 1024, BITS>(wq, scales, biases, x, y, nullptr, N, K, rpw, threads,
+                                                stream);
 }
 
 template <int B, int R, bool AM>
@@ -578,7 +666,42 @@ hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
   }
 }
 
+// 2- and 8-bit codes: the shared-memory variant only (the caller checks that x
+// fits), with the 4-bit layouts.
+template <int BITS>
+hipError_t dispatch_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                         const uint16_t* x, float* y, int B, int64_t N, int64_t K, hipStream_t stream) {
+  if (use_regs(B, K, false)) return hipErrorInvalidValue;
+  if (B == 1) {
+    if ((N + kCUs - 1) / kCUs < 2 * 16 * 16)
+      return launch_per_cu<1, 4, BITS>(wq, scales, biases, x, y, N, K, stream);
+    return launch_short<1, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+  }
+  switch (B) {
+    case 2: return launch_short<2, BITS == 8 ? 2 : 4, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+    case 3: return launch_short<3, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+    case 4: return launch_short<4, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+    case 5: return launch_short<5, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+    case 6: return launch_short<6, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+    case 7: return launch_short<7, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+    case 8: return launch_short<8, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+bool gemv_bits_fits(int B, int64_t K) { return !use_regs(B, K, false); }
+
+hipError_t launch_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                            const uint16_t* x, float* y, int B, int64_t N, int64_t K, int bits,
+                            hipStream_t stream) {
+  switch (bits) {
+    case 2: return dispatch_bits<2>(wq, scales, biases, x, y, B, N, K, stream);
+    case 8: return dispatch_bits<8>(wq, scales, biases, x, y, B, N, K, stream);
+    default: return launch_gemv(wq, scales, biases, x, y, B, N, K, false, stream);
+  }
+}
 
 hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                        const uint16_t* x, float* y, int B, int64_t N, int64_t K, bool force_regs,

@@ -22,6 +22,13 @@ hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const ui
 hipError_t launch_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                        const uint16_t* x, void* y, bool y_bf16, int64_t M, int64_t N, int64_t K,
                        void* workspace, hipStream_t stream);
+// Decode product with 2-, 4- or 8-bit codes (32/bits per uint32, low field
+// first); widths other than 4 run the vector-ALU shared-memory variant only,
+// which needs gemv_bits_fits(B, K).
+hipError_t launch_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                            const uint16_t* x, float* y, int B, int64_t N, int64_t K, int bits,
+                            hipStream_t stream);
+bool gemv_bits_fits(int B, int64_t K);
 // Kernel family qmm_gemv runs for a shape (1 = vector ALU, 2 = matrix cores);
 // a function of (B, N, K) only.
 int gemv_auto_family(int B, int64_t N, int64_t K);

@@ -51,20 +51,29 @@ def bf16_bits_to_f32(h):
     return (np.ascontiguousarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def weights(N, K, workload=0, matrix=GENERIC, layer=0):
-    """(codes [N][K/8] uint32, scales [N][K/64] bf16 bits, biases [N][K/64] bf16 bits)."""
+def weights(N, K, workload=0, matrix=GENERIC, layer=0, bits=4):
+    """(codes [N][K*bits/32] uint32, scales [N][K/64] bf16 bits, biases [N][K/64] bf16 bits).
+
+    Other code widths (2 or 8 bits, 32/bits codes per word): the same recipe with
+    the scale magnitude multiplied by 16 / 2^bits and the bias centred at
+    -2^(bits-1) * scale, so the dequantized weights span the 4-bit workload's range.
+    """
     if K % 64:
         raise ValueError("K must be a multiple of 64")
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
     G = K // 64
     codes = rng(workload, matrix, T_CODES, layer).integers(
-        0, 1 << 32, size=(N, K // 8), dtype=np.uint32, endpoint=False)
+        0, 1 << 32, size=(N, K * bits // 32), dtype=np.uint32, endpoint=False)
     mag = rng(workload, matrix, T_SCALE_MAG, layer).random((N, G), dtype=np.float32)
     mag = np.float32(0.002) + np.float32(0.018) * mag
+    if bits != 4:
+        mag = (mag * np.float32(16.0 / (1 << bits))).astype(np.float32)
     sign = rng(workload, matrix, T_SCALE_SIGN, layer).integers(0, 2, size=(N, G), dtype=np.int8)
     s = np.where(sign == 1, mag, -mag).astype(np.float32)
     scales = f32_to_bf16_bits(s)
     eps = rng(workload, matrix, T_BIAS_EPS, layer).normal(0.0, 1e-3, size=(N, G)).astype(np.float32)
-    b = (np.float32(-8.0) * bf16_bits_to_f32(scales) + eps).astype(np.float32)
+    b = (np.float32(-(1 << (bits - 1))) * bf16_bits_to_f32(scales) + eps).astype(np.float32)
     biases = f32_to_bf16_bits(b)
     return codes, scales, biases
 
