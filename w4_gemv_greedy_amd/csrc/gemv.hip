@@ -590,13 +590,16 @@ hipError_t launch_short(const uint32_t* wq, const uint16_t* scales, const uint16
 // streams the same number of bytes and no second round of workgroups
 // trails; x is staged once per CU): up to 32 rows per CU one row per half
 // wave, else 16 half waves striding through the share, R rows per item.
-template <int R, int P, int BITS = 4>
+// (Launch bounds: 640 threads for shares of at most 20 groups of R rows, one
+// group per half wave; else 512 threads, 16 half waves striding.)
+template <int R, int P, int BITS = 4, int B = 1>
 hipError_t launch_per_cu(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                          const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t rpw = (N + kCUs - 1) / kCUs;
-  const int threads = rpw <= 32 ? 64 * (int)((rpw + 1) / 2) : 512;
-  return launch_lds<1, R, P, false, 1024, BITS>(wq, scales, biases, x, y, nullptr, N, K, rpw, threads,
-                                                stream);
+  if (rpw <= 20 * R)
+    return launch_lds<B, R, P, false, 640, BITS>(wq, scales, biases, x, y, nullptr, N, K, rpw,
+                                                 64 * (int)((rpw + 2 * R - 1) / (2 * R)), stream);
+  return launch_lds<B, R, P, false, 512, BITS>(wq, scales, biases, x, y, nullptr, N, K, rpw, 512, stream);
 }
 
 template <int B, int R, bool AM>
@@ -651,6 +654,21 @@ hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
     // measured in the decode sweep: the per-CU layout for the layer widths; the
     // vocabulary-wide head keeps the short workgroups
     if (rpw < 2 * 16 * 16) return launch_per_cu<1, 4>(wq, scales, biases, x, y, N, K, stream);
+  }
+  // B >= 2: the per-CU layout too, also for the head (measured: down at B = 4
+  // 36 -> 22 us, gate-up at B = 8 90 -> 47 us, lm_head at B = 8 581 -> 322 us),
+  // two rows per item when a CU's share exceeds 40 rows
+  if (!AM && B >= 2) {
+    const bool two = (N + kCUs - 1) / kCUs > 40;  // (R = 2 then always strides: 512 threads)
+    switch (B) {
+#define W4G_PER_CU(BB)                                                                      \
+      case BB:                                                                              \
+        return two ? launch_per_cu<2, 2, 4, BB>(wq, scales, biases, x, y, N, K, stream)     \
+                   : launch_per_cu<1, 2, 4, BB>(wq, scales, biases, x, y, N, K, stream);
+      W4G_PER_CU(2) W4G_PER_CU(3) W4G_PER_CU(4) W4G_PER_CU(5) W4G_PER_CU(6) W4G_PER_CU(7) W4G_PER_CU(8)
+#undef W4G_PER_CU
+      default: return hipErrorInvalidValue;
+    }
   }
   switch (B) {
     case 1: return few_rows(N) ? launch_short<1, 1, 4, AM>(wq, scales, biases, x, y, rec, N, K, stream)
@@ -724,14 +742,15 @@ hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const 
   return dispatch<true>(wq, scales, biases, x, y, rec, B, N, K, false, stream);
 }
 
-// Measured: the vector ALUs keep up to B = 4 on every decode shape, and to
-// B = 6 while x fits in LDS; past that (x staged in registers, or B >= 7) the
-// matrix cores are faster.
+// Measured with the per-CU layouts: the vector ALUs are faster whenever x fits
+// in LDS (gate-up at B = 8: 47 against 50 us; o_proj at every B), except on
+// vocabulary-wide products from B = 7 (lm_head at B = 8: 322 against 282 us);
+// where x is staged in registers the matrix cores win from B = 3 (down at B = 4:
+// 46 against 39 us, at B = 8: 76 against 42 us).
 int gemv_auto_family(int B, int64_t N, int64_t K) {
-  (void)N;
-  if (B <= 4) return 1;
-  if (B <= 6 && !use_regs(B, K, false)) return 1;
-  return 2;
+  if (use_regs(B, K, false)) return B <= 2 ? 1 : 2;
+  if (B >= 7 && (N + kCUs - 1) / kCUs >= 2 * 16 * 16) return 2;
+  return 1;
 }
 
 }  // namespace w4g
