@@ -471,6 +471,21 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args):
         ex["sweep_b8"] = {"us_per_step": round(ms * 1e3, 1), "us_per_token": round(ms * 1e3 / 8, 2),
                           "GBps": round(step_bytes(8) / (ms * 1e-3) / 1e9, 1)}
         log(f"sweep B=8: {ex['sweep_b8']}")
+
+        # the head alone at B = 8: product + two-pass argmax, and fused
+        ws8f = torch.empty(w4g.workspace_bytes(w4g.OP_GEMV_ARGMAX, 8, VOCAB, HIDDEN), dtype=torch.uint8,
+                           device=dev)
+
+        def head8():
+            w4g.qmm_gemv(head.wq, head.sc, head.bi, xh8, lg)
+            w4g.vocab_argmax(lg, ids8, ws8)
+
+        def head8_fused():
+            w4g.qmm_gemv_argmax(head.wq, head.sc, head.bi, xh8, None, ids8, ws8f, want_logits=False)
+        ms, _ = timed(head8, 10, 2, True, reps=2)
+        ms_f, _ = timed(head8_fused, 10, 2, True, reps=2)
+        ex["lm_head_argmax_b8"] = {"us_per_call": round(ms * 1e3, 1), "fused_ids_only_us_per_call": round(ms_f * 1e3, 1)}
+        log(f"lm_head+argmax B=8: {ex['lm_head_argmax_b8']}")
     return ex
 
 

@@ -218,14 +218,15 @@ int vocab_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int
  *   wq, scales, biases, x, B, N, K: as qmm_gemv (N is the vocabulary size,
  *   N < 2^31).
  *   logits [B][N] fp32, or NULL: when given, receives exactly the bits
- *   qmm_gemv_ex(..., W4G_GEMV_VALU) writes.
+ *   qmm_gemv writes for the same (B, N, K) (the same kernel family, chosen
+ *   the same way).
  *   ids [B] uint32: per batch row the id of the largest logit, the lowest id
  *   among equal values (-0.0 ties +0.0), or W4G_SENTINEL if any logit of the
  *   row is NaN or +-Inf; always equal to vocab_argmax over those logits.
  *   workspace: at least qmm_workspace_bytes(W4G_OP_GEMV_ARGMAX, B, N, K)
  *   bytes, 8-byte aligned: one (value, id | flag) record per workgroup of the
  *   product and batch row.
- * Order of the logits: that of the vector-ALU family (see qmm_gemv).
+ * Order of the logits: that of the family qmm_gemv picks (see qmm_gemv).
  */
 int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                     const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N,

@@ -1,5 +1,6 @@
 """The decode product with the argmax's first pass fused into its epilogue
-(qmm_gemv_argmax): the logits are bitwise those of the vector-ALU product, the
+(qmm_gemv_argmax): the logits are bitwise those of qmm_gemv (the same kernel
+family, vector-ALU or matrix-core, chosen by shape the same way), the
 ids are bitwise those of the two-pass argmax over those logits and of the
 oracle's argmax, at small ragged shapes, at the full lm_head shape, and on
 planted rows (ties across workgroups, a tie to a lower id, non-finite rows)."""
@@ -26,7 +27,7 @@ def _run(wq, sc, bi, x, want_logits=True):
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
     X = up_bf16(x)
     ids, logits = w4g.qmm_gemv_argmax(*W, X, want_logits=want_logits)
-    ref_logits = w4g.qmm_gemv(*W, X, kernel=w4g.GEMV_VALU)
+    ref_logits = w4g.qmm_gemv(*W, X)
     two_pass = w4g.vocab_argmax(ref_logits)
     out = (ids_down(ids), down(logits) if logits is not None else None, down(ref_logits),
            ids_down(two_pass))
@@ -56,12 +57,13 @@ def _copy_row(wq, sc, bi, src, dst):
     wq[dst], sc[dst], bi[dst] = wq[src], sc[src], bi[src]
 
 
-@pytest.mark.parametrize("B", [1, 3])
-def test_fused_planted_rows(B):
+@pytest.mark.parametrize("B,K", [(1, 1024), (3, 1024), (8, 10240)])
+def test_fused_planted_rows(B, K):
     """Equal rows give equal logits bit for bit (each row's arithmetic is its own),
     so copying a batch row's winner to a lower id must move the answer there, a
-    copy to a higher id must not, and an infinite scale makes the row fail."""
-    N, K = 9000, 1024
+    copy to a higher id must not, and an infinite scale makes the row fail.
+    (B = 8 at K = 10240 runs the matrix-core family: x would not fit in LDS.)"""
+    N = 9000
     wq, sc, bi, x = _case(N, K, B, 11)
     ids0, _, ref0, _ = _run(wq, sc, bi, x)
     win = int(ids0[0])

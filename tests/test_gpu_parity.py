@@ -87,7 +87,7 @@ def test_gemv_per_cu_layout(N, K):
     """B = 1 with one workgroup per CU (an equal share of rows each, half waves
     striding through it; ragged shares and a last workgroup with an odd row
     count) against the oracle, and bitwise equal to the same rows computed by
-    the short-workgroup layout of B = 2 and by the register-staged variant."""
+    the layout of B = 2 and by the register-staged variant."""
     wq, sc, bi, x = _case(N, K, 2, N % 97)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
     y1 = down(w4g.qmm_gemv(*W, up_bf16(x[:1]), kernel=1))
@@ -96,6 +96,26 @@ def test_gemv_per_cu_layout(N, K):
     assert np.array_equal(y1[0].view(np.uint32), y2[0].view(np.uint32))
     assert np.array_equal(y1.view(np.uint32), yr.view(np.uint32))
     assert_close(y1, oracle.qmm(wq, sc, bi, x[:1]), f"gemv per-CU N={N} K={K}")
+
+
+def test_gemv_short_layout_ragged():
+    """B = 1 over more than 511 rows per CU takes the short workgroups (32 rows
+    each, two groups of two rows per half wave): a row count that leaves the
+    last workgroup ragged (29 rows) and a ragged last chunk of K, on sampled
+    rows against the oracle, bitwise equal to the per-CU layout of B = 2 and
+    to the fused head's logits, whose id matches the two-pass argmax."""
+    N, K = 131101, 1088
+    wq, sc, bi, x = _case(N, K, 2, 3)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y1 = down(w4g.qmm_gemv(*W, up_bf16(x[:1])))
+    y2 = down(w4g.qmm_gemv(*W, up_bf16(x)))
+    assert np.array_equal(y1[0].view(np.uint32), y2[0].view(np.uint32))
+    ids, lg = w4g.qmm_gemv_argmax(*W, up_bf16(x[:1]))
+    assert np.array_equal(down(lg).view(np.uint32), y1.view(np.uint32))
+    assert ids_down(ids)[0] == oracle.argmax(y1)[0]
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(N - 70, N),
+                                     np.random.default_rng(4).choice(N, 200, replace=False)]))
+    assert_close(y1[:, rows], oracle.qmm_rows(wq, sc, bi, x[:1], rows), f"gemv short N={N} K={K}")
 
 
 def test_gemv_families_agree():

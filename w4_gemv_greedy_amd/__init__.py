@@ -152,7 +152,8 @@ def qmm_gemm(wq, scales, biases, x, y=None, workspace=None, out_dtype=None):
 
 def qmm_gemv_argmax(wq, scales, biases, x, logits=None, ids=None, workspace=None, want_logits=True):
     """Decode product and greedy argmax per batch row, the argmax's first pass
-    fused into the product; returns (ids, logits).
+    fused into the product; returns (ids, logits).  The logits are bitwise
+    those of qmm_gemv (the same kernel family).
 
     ids: int32 tensor [B] holding uint32 bits (0xFFFFFFFF = a non-finite logit
     in the row).  logits: [B][N] fp32, allocated when not given and

@@ -183,11 +183,11 @@ struct Item {
 // end of a short last chunk reads lane 0 of chunk 0 (always staged, so finite)
 // and adds exact zeros.
 //
-// AM adds the argmax's pass 1 as an epilogue (launched with 256 threads and
-// rpw = 8 R, one group per half wave): the workgroup's values go to LDS, and
-// after the stream one thread per batch row writes the record of the best
-// (value, lowest row), or the non-finite flag, to rec[bb][blockIdx.x]; y may
-// then be null.
+// AM adds the argmax's pass 1 as an epilogue, in any layout: as each group of
+// rows finishes, its candidates (value, lowest row) go into the workgroup's
+// per-batch-row maximum in LDS (an atomic max), and the last half wave to
+// finish writes the workgroup's record, or the non-finite flag, to
+// rec[bb][blockIdx.x]; y may then be null.
 template <int B, int R, int P, bool RAGGED, bool AM, int MAXT = kThreads, int BITS = 4>
 __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restrict__ wq,
                                                          const uint16_t* __restrict__ scales,
@@ -301,8 +301,17 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
 #pragma unroll
   for (int sl = 0; sl < P; ++sl) issue(ring[sl]);
 
-  // argmax epilogue: the workgroup's values (one group of R rows per half wave)
-  __shared__ float s_vals[AM ? kHalfWaves * R : 1][AM ? B : 1];
+  // argmax epilogue: the workgroup's best candidate so far per batch row, a bit
+  // per batch row for a non-finite value, and the count of half waves done
+  // (cleared before the barrier that ends the staging of x)
+  __shared__ uint64_t s_best[AM ? B : 1];
+  __shared__ uint32_t s_bad, s_done;
+  if (AM && tid == 0) {
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) s_best[bb] = 0;
+    s_bad = 0;
+    s_done = 0;
+  }
 
 #pragma unroll
   for (int q = 0; q < XPRE; ++q) {
@@ -386,7 +395,16 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
           for (int bb = 0; bb < B; ++bb) {
             const float v = half_wave_sum(acc[r][bb]);
             if (lane == 0 && crow + r < wg_end && (!AM || y != nullptr)) y[(int64_t)bb * N + crow + r] = v;
-            if (AM && lane == 0) s_vals[hwi * R + r][bb] = v;
+            if constexpr (AM) {
+              if (lane == 0 && crow + r < wg_end) {
+                const uint32_t u = __float_as_uint(v);
+                if (!finite_bits(u))
+                  __hip_atomic_fetch_or(&s_bad, 1u << bb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                else
+                  __hip_atomic_fetch_max(&s_best[bb], cand(u, (uint32_t)(crow + r)), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+              }
+            }
             acc[r][bb] = 0.0f;
           }
         }
@@ -415,22 +433,20 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
   for (int sl = 0; sl < P; ++sl) consume(ring[sl], it + P + sl);
 
   if constexpr (AM) {
-    // the best (value, lowest row) per batch row, or the non-finite flag
-    // (launched with one group of R rows per half wave)
-    __syncthreads();
-    if (tid < B) {
-      const int64_t first = wg_begin;
-      uint64_t best = 0;
-      bool bad = false;
+    // The last half wave to finish writes the workgroup's record per batch row:
+    // the best (value, lowest row), or the non-finite flag.  A maximum, so it
+    // does not depend on which half wave took which rows or finished first; no
+    // barrier, so finished waves leave at once as in the plain product.  (The
+    // count's release orders each half wave's maxima before it; the last one's
+    // acquire sees them all.)
+    if (lane == 0 &&
+        __hip_atomic_fetch_add(&s_done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == (uint32_t)H - 1) {
+      const uint32_t bad = __hip_atomic_load(&s_bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-      for (int i = 0; i < kHalfWaves * R; ++i) {
-        if (first + i < wg_end) {
-          const uint32_t u = __float_as_uint(s_vals[i][tid]);
-          if (!finite_bits(u)) bad = true;
-          else best = umax64(best, cand(u, (uint32_t)(first + i)));
-        }
-      }
-      rec[(int64_t)tid * gridDim.x + blockIdx.x] = make_record(best, bad, (uint32_t)first);
+      for (int bb = 0; bb < B; ++bb)
+        rec[(int64_t)bb * gridDim.x + blockIdx.x] =
+            make_record(__hip_atomic_load(&s_best[bb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP),
+                        ((bad >> bb) & 1u) != 0, (uint32_t)wg_begin);
     }
   }
 }
@@ -544,10 +560,9 @@ size_t lds_bytes(int B, int64_t K) {
   return (size_t)B * (size_t)C * (128 * 16 + 32 * 4);
 }
 
-// Rows per item for the shared-memory variant, by batch (measured); few rows
-// (N below 16 per-item groups of 1024) take one row per item and a deeper ring.
+// Few rows (N below 16 per-item groups of 1024) take one row per item and a
+// deeper ring in the short layout.
 bool few_rows(int64_t N) { return N < (int64_t)kHalfWaves * 2 * 1024; }
-int lds_rows_per_item(int B, int64_t N) { return B == 1 ? (few_rows(N) ? 1 : 2) : B == 2 ? 4 : 2; }
 int regs_rows(int B) { return B <= 2 ? 4 : 2; }
 bool use_regs(int B, int64_t K, bool force_regs) { return force_regs || lds_bytes(B, K) > kMaxLds; }
 
@@ -575,15 +590,25 @@ hipError_t launch_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t
   return hipGetLastError();
 }
 
-// 256 threads, one group of R rows per half wave: many short workgroups, which
-// the dispatcher spreads over the CUs as they free up (the fused head's layout:
-// one record per workgroup)
+// 256 threads, short_groups() groups of R rows per half wave: many short
+// workgroups, which the dispatcher spreads over the CUs as they free up
+// Groups of R rows per half wave in the short layout: two (32-row workgroups
+// for R = 2; measured on the vocabulary-wide head at B = 1 on three GPUs: as
+// fast as one group or up to 5% faster, and half the fused head's records).
+int short_groups() {
+#ifdef W4G_TUNING
+  const char* k = getenv("W4G_SM");
+  if (k && atoi(k) > 0) return atoi(k);
+#endif
+  return 2;
+}
+
 template <int B, int R, int P, bool AM, int BITS = 4>
 hipError_t launch_short(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                         const uint16_t* x, float* y, uint2* rec, int64_t N, int64_t K,
                         hipStream_t stream) {
   return launch_lds<B, R, P, AM, kThreads, BITS>(wq, scales, biases, x, y, rec, N, K,
-                                                 (int64_t)kHalfWaves * R, kThreads, stream);
+                                                 (int64_t)kHalfWaves * R * short_groups(), kThreads, stream);
 }
 
 // One workgroup per CU, each with an equal share of the rows (so every CU
@@ -592,15 +617,27 @@ hipError_t launch_short(const uint32_t* wq, const uint16_t* scales, const uint16
 // wave, else 16 half waves striding through the share, R rows per item.
 // (Launch bounds: 640 threads for shares of at most 20 groups of R rows, one
 // group per half wave; else 512 threads, 16 half waves striding.)
-template <int R, int P, int BITS = 4, int B = 1>
+int64_t per_cu_rows(int64_t N) { return (N + kCUs - 1) / kCUs; }
+
+template <int R, int P, int BITS = 4, int B = 1, bool AM = false>
 hipError_t launch_per_cu(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                         const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream) {
-  const int64_t rpw = (N + kCUs - 1) / kCUs;
-  if (rpw <= 20 * R)
-    return launch_lds<B, R, P, false, 640, BITS>(wq, scales, biases, x, y, nullptr, N, K, rpw,
-                                                 64 * (int)((rpw + 2 * R - 1) / (2 * R)), stream);
-  return launch_lds<B, R, P, false, 512, BITS>(wq, scales, biases, x, y, nullptr, N, K, rpw, 512, stream);
+                         const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream,
+                         uint2* rec = nullptr) {
+  const int64_t rpw = per_cu_rows(N);
+  // (R = 2 at B >= 2 runs only for shares above 40 rows, so that pairing never
+  // takes the 640-thread variant, which is not built for it; nor are 8-bit
+  // codes at B >= 7, whose registers exceed the 640-thread budget)
+  if constexpr (!(R == 2 && B >= 2) && !(BITS == 8 && B >= 7)) {
+    if (rpw <= 20 * R)
+      return launch_lds<B, R, P, AM, 640, BITS>(wq, scales, biases, x, y, rec, N, K, rpw,
+                                                64 * (int)((rpw + 2 * R - 1) / (2 * R)), stream);
+  }
+  return launch_lds<B, R, P, AM, 512, BITS>(wq, scales, biases, x, y, rec, N, K, rpw, 512, stream);
 }
+
+// The layer widths (a CU's share below 512 rows) take the per-CU layout at
+// B = 1; the vocabulary-wide head keeps the short workgroups there.
+bool b1_per_cu(int64_t N) { return per_cu_rows(N) < 2 * 16 * 16; }
 
 template <int B, int R, bool AM>
 hipError_t launch_regs(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
@@ -631,10 +668,9 @@ hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
       default: return hipErrorInvalidValue;
     }
   }
-  if (!AM && B == 1) {
-    const int64_t rpw = (N + kCUs - 1) / kCUs;
+  if (B == 1) {
 #ifdef W4G_TUNING
-    const char* knob = getenv(rpw >= 2 * 16 * 16 ? "W4G_CUH" : "W4G_CU");
+    const char* knob = AM ? nullptr : getenv(per_cu_rows(N) >= 2 * 16 * 16 ? "W4G_CUH" : "W4G_CU");
     if (knob) {
       switch (atoi(knob)) {
         case 0: break;  // the short-workgroup layout below
@@ -651,58 +687,44 @@ hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
                            : launch_short<1, 2, 2, false>(wq, scales, biases, x, y, rec, N, K, stream);
     }
 #endif
-    // measured in the decode sweep: the per-CU layout for the layer widths; the
-    // vocabulary-wide head keeps the short workgroups
-    if (rpw < 2 * 16 * 16) return launch_per_cu<1, 4>(wq, scales, biases, x, y, N, K, stream);
+    // measured in the decode sweep
+    if (b1_per_cu(N)) return launch_per_cu<1, 4, 4, 1, AM>(wq, scales, biases, x, y, N, K, stream, rec);
+    return few_rows(N) ? launch_short<1, 1, 4, AM>(wq, scales, biases, x, y, rec, N, K, stream)
+                       : launch_short<1, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
   }
   // B >= 2: the per-CU layout too, also for the head (measured: down at B = 4
   // 36 -> 22 us, gate-up at B = 8 90 -> 47 us, lm_head at B = 8 581 -> 322 us),
   // two rows per item when a CU's share exceeds 40 rows
-  if (!AM && B >= 2) {
-    const bool two = (N + kCUs - 1) / kCUs > 40;  // (R = 2 then always strides: 512 threads)
-    switch (B) {
-#define W4G_PER_CU(BB)                                                                      \
-      case BB:                                                                              \
-        return two ? launch_per_cu<2, 2, 4, BB>(wq, scales, biases, x, y, N, K, stream)     \
-                   : launch_per_cu<1, 2, 4, BB>(wq, scales, biases, x, y, N, K, stream);
-      W4G_PER_CU(2) W4G_PER_CU(3) W4G_PER_CU(4) W4G_PER_CU(5) W4G_PER_CU(6) W4G_PER_CU(7) W4G_PER_CU(8)
-#undef W4G_PER_CU
-      default: return hipErrorInvalidValue;
-    }
-  }
+  const bool two = per_cu_rows(N) > 40;  // (R = 2 then always strides: 512 threads)
   switch (B) {
-    case 1: return few_rows(N) ? launch_short<1, 1, 4, AM>(wq, scales, biases, x, y, rec, N, K, stream)
-                               : launch_short<1, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
-    case 2: return launch_short<2, 4, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
-    case 3: return launch_short<3, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
-    case 4: return launch_short<4, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
-    case 5: return launch_short<5, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
-    case 6: return launch_short<6, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
-    case 7: return launch_short<7, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
-    case 8: return launch_short<8, 2, 2, AM>(wq, scales, biases, x, y, rec, N, K, stream);
+#define W4G_PER_CU(BB)                                                                               \
+    case BB:                                                                                         \
+      return two ? launch_per_cu<2, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec)       \
+                 : launch_per_cu<1, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec);
+    W4G_PER_CU(2) W4G_PER_CU(3) W4G_PER_CU(4) W4G_PER_CU(5) W4G_PER_CU(6) W4G_PER_CU(7) W4G_PER_CU(8)
+#undef W4G_PER_CU
     default: return hipErrorInvalidValue;
   }
 }
 
 // 2- and 8-bit codes: the shared-memory variant only (the caller checks that x
-// fits), with the 4-bit layouts.
+// fits), with the 4-bit layouts (per CU, short workgroups for the B = 1 head).
 template <int BITS>
 hipError_t dispatch_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                          const uint16_t* x, float* y, int B, int64_t N, int64_t K, hipStream_t stream) {
   if (use_regs(B, K, false)) return hipErrorInvalidValue;
   if (B == 1) {
-    if ((N + kCUs - 1) / kCUs < 2 * 16 * 16)
-      return launch_per_cu<1, 4, BITS>(wq, scales, biases, x, y, N, K, stream);
+    if (b1_per_cu(N)) return launch_per_cu<1, 4, BITS>(wq, scales, biases, x, y, N, K, stream);
     return launch_short<1, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
   }
+  const bool two = per_cu_rows(N) > 40;
   switch (B) {
-    case 2: return launch_short<2, BITS == 8 ? 2 : 4, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
-    case 3: return launch_short<3, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
-    case 4: return launch_short<4, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
-    case 5: return launch_short<5, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
-    case 6: return launch_short<6, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
-    case 7: return launch_short<7, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
-    case 8: return launch_short<8, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+#define W4G_PER_CU(BB)                                                                            \
+    case BB:                                                                                      \
+      return two ? launch_per_cu<2, 2, BITS, BB>(wq, scales, biases, x, y, N, K, stream)          \
+                 : launch_per_cu<1, 2, BITS, BB>(wq, scales, biases, x, y, N, K, stream);
+    W4G_PER_CU(2) W4G_PER_CU(3) W4G_PER_CU(4) W4G_PER_CU(5) W4G_PER_CU(6) W4G_PER_CU(7) W4G_PER_CU(8)
+#undef W4G_PER_CU
     default: return hipErrorInvalidValue;
   }
 }
@@ -728,17 +750,22 @@ hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_
 }
 
 int64_t gemv_argmax_records(int B, int64_t N, int64_t K) {
+  if (gemv_auto_family(B, N, K) == 2) return gemv_mfma_argmax_records(N);
   if (use_regs(B, K, false)) {
     const int R = regs_rows(B);
     return (N + 2 * R - 1) / (2 * R);
   }
-  const int64_t rows_per_block = (int64_t)kHalfWaves * lds_rows_per_item(B, N);
-  return (N + rows_per_block - 1) / rows_per_block;
+  // the workgroups of the layout dispatch() launches, one record each
+  const int64_t rpw = (B >= 2 || b1_per_cu(N)) ? per_cu_rows(N)
+                                               : (int64_t)kHalfWaves * (few_rows(N) ? 1 : 2) * short_groups();
+  return (N + rpw - 1) / rpw;
 }
 
 hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                               const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                               hipStream_t stream) {
+  if (gemv_auto_family(B, N, K) == 2)
+    return launch_gemv_mfma_argmax(wq, scales, biases, x, y, rec, B, N, K, stream);
   return dispatch<true>(wq, scales, biases, x, y, rec, B, N, K, false, stream);
 }
 
@@ -749,7 +776,7 @@ hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const 
 // 46 against 39 us, at B = 8: 76 against 42 us).
 int gemv_auto_family(int B, int64_t N, int64_t K) {
   if (use_regs(B, K, false)) return B <= 2 ? 1 : 2;
-  if (B >= 7 && (N + kCUs - 1) / kCUs >= 2 * 16 * 16) return 2;
+  if (B >= 7 && per_cu_rows(N) >= 2 * 16 * 16) return 2;
   return 1;
 }
 

@@ -55,6 +55,27 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t g) {
   return d;
 }
 
+// The largest 64-bit word over the 32 lanes of each half wave, in every lane
+// of that half: partners across the two 16-lane rows, then within a row by
+// mirrors and quad swaps (each step pairs every lane with one whose set of
+// covered lanes is disjoint from its own, so the last step covers all 32).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max64(uint64_t c) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)c, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(c >> 32), CTRL, 0xF, 0xF, false);
+  return umax64(c, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint64_t half_wave_max64(uint64_t c) {
+  const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)c, (uint32_t)c, false, false);
+  const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(c >> 32), (uint32_t)(c >> 32), false, false);
+  c = umax64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
+  c = dpp_max64<0x140>(c);  // row_mirror
+  c = dpp_max64<0x141>(c);  // row_half_mirror
+  c = dpp_max64<0x4E>(c);   // quad_perm [2,3,0,1]
+  c = dpp_max64<0xB1>(c);   // quad_perm [1,0,3,2]
+  return c;
+}
+
 // 8 codes -> bf16 values 128 + q in the order q0,q4,q1,q5,q2,q6,q3,q7
 __device__ __forceinline__ bf16x8_t expand128(uint32_t w, uint32_t m, uint32_t g) {
   uint4 p;
@@ -88,13 +109,17 @@ __device__ __forceinline__ uint32_t bf16_at(const uint4& v, int i) {
 // The workgroup's four waves split the K groups round robin; each stage of 16
 // groups gives every wave GPS = 16 / W of them.  The activations of a stage are
 // staged in one of two LDS buffers while the other feeds the matrix cores.
-template <int W, bool VEC>
+//
+// AM adds the argmax's pass 1 as an epilogue: per batch row, the best (value,
+// lowest row) of the workgroup's 32 rows, or the non-finite flag, goes to
+// rec[b][blockIdx.x] (one record per 32 rows); y may then be null.
+template <int W, bool VEC, bool AM>
 __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __restrict__ wq,
                                                            const uint16_t* __restrict__ scales,
                                                            const uint16_t* __restrict__ biases,
                                                            const uint16_t* __restrict__ x,
                                                            float* __restrict__ y, int B, int64_t N,
-                                                           int64_t K) {
+                                                           int64_t K, uint2* __restrict__ rec) {
   constexpr int GPS = kStageGroups / W;
   // [buf][8-element block][slot]: slots 0..7 hold the batch rows (row r of
   // block k at slot r ^ ((k >> 3) & 7), so the staging writes of different
@@ -246,16 +271,44 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
 #pragma unroll
   for (int v = 0; v < 4; ++v) s_red[wave][v][lane] = tot[v];
   __syncthreads();
-  if (wave == 0) {
+  {
+    // wave v finishes column v of every lane: batch row b = 4 h + v, weight row
+    // n0 + l32 (the wave sums added in ascending wave order)
+    static_assert(W == 4, "one output column per wave");
+    const int v = wave;
+    float acc = s_red[0][v][lane];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float acc = s_red[0][v][lane];
-#pragma unroll
-      for (int w = 1; w < W; ++w) acc += s_red[w][v][lane];
-      const int b = 4 * h + v;
-      if (b < B && n0 + l32 < N) y[(int64_t)b * N + n0 + l32] = acc;
+    for (int w = 1; w < W; ++w) acc += s_red[w][v][lane];
+    const int b = 4 * h + v;
+    const bool valid = n0 + l32 < N;
+    if (b < B && valid && (!AM || y != nullptr)) y[(int64_t)b * N + n0 + l32] = acc;
+    if constexpr (AM) {
+      // the best candidate over the 32 rows of this half wave's batch row
+      const uint32_t u = __float_as_uint(acc);
+      const bool bad = valid && !finite_bits(u);
+      const uint64_t c = half_wave_max64((valid && !bad) ? cand(u, (uint32_t)(n0 + l32)) : 0);
+      const uint64_t badm = __ballot(bad);
+      const bool half_bad = ((badm >> (32 * h)) & 0xFFFFFFFFull) != 0;
+      if (l32 == 0 && b < B)
+        rec[(int64_t)b * gridDim.x + blockIdx.x] = make_record(c, half_bad, (uint32_t)n0);
     }
   }
+}
+
+template <bool AM>
+hipError_t launch(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                  const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                  hipStream_t stream) {
+  const int64_t blocks = (N + 31) / 32;
+  const bool vec = ((K >> 6) % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
+                                             reinterpret_cast<uintptr_t>(biases)) & 15u) == 0;
+  if (vec)
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, true, AM>), dim3((unsigned)blocks), dim3(256), 0, stream, wq,
+                       scales, biases, x, y, B, N, K, rec);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<4, false, AM>), dim3((unsigned)blocks), dim3(256), 0, stream, wq,
+                       scales, biases, x, y, B, N, K, rec);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -263,16 +316,15 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
 hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                             const uint16_t* x, float* y, int B, int64_t N, int64_t K,
                             hipStream_t stream) {
-  const int64_t blocks = (N + 31) / 32;
-  const bool vec = ((K >> 6) % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
-                                             reinterpret_cast<uintptr_t>(biases)) & 15u) == 0;
-  if (vec)
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, true>), dim3((unsigned)blocks), dim3(256), 0, stream, wq,
-                       scales, biases, x, y, B, N, K);
-  else
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, false>), dim3((unsigned)blocks), dim3(256), 0, stream, wq,
-                       scales, biases, x, y, B, N, K);
-  return hipGetLastError();
+  return launch<false>(wq, scales, biases, x, y, nullptr, B, N, K, stream);
+}
+
+int64_t gemv_mfma_argmax_records(int64_t N) { return (N + 31) / 32; }
+
+hipError_t launch_gemv_mfma_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                                   const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                                   hipStream_t stream) {
+  return launch<true>(wq, scales, biases, x, y, rec, B, N, K, stream);
 }
 
 }  // namespace w4g

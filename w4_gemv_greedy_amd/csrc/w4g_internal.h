@@ -43,14 +43,19 @@ size_t argmax_top2_workspace_bytes(int64_t rows, int64_t vocab);
 // Pass 2 alone: combines `nrec` (value, id | flag) records per row into ids.
 hipError_t launch_argmax_combine(const uint2* rec, int64_t rows, int64_t nrec, uint32_t* ids,
                                  hipStream_t stream);
-// Decode product on the vector ALUs with the argmax's pass 1 as its epilogue:
-// each workgroup writes one record per batch row (`nrec` per row, see
-// gemv_argmax_records) instead of needing the logits read back; `y` may be
-// null.  The logits' bits are those of launch_gemv.
+// Decode product with the argmax's pass 1 as its epilogue, in the family
+// gemv_auto_family picks: each workgroup writes one record per batch row
+// (`nrec` per row, see gemv_argmax_records) instead of needing the logits read
+// back; `y` may be null.  The logits' bits are those of that family's product.
 hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                               const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                               hipStream_t stream);
 int64_t gemv_argmax_records(int B, int64_t N, int64_t K);
+// The matrix-core family's epilogue variant: one record per 32 rows.
+hipError_t launch_gemv_mfma_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                                   const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                                   hipStream_t stream);
+int64_t gemv_mfma_argmax_records(int64_t N);
 
 constexpr int kArgmaxBlock = 1024;  // ids per pass-1 record
 constexpr uint32_t kArgmaxFlag = 0x80000000u;  // non-finite bit of a record's id word
