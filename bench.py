@@ -13,7 +13,11 @@ Printed: one JSON line.  `value` is the algorithmic bytes of a step
 measured step time, in GB/s.  The line also carries the roofline of the
 dominant kernel (the gate-up product), the oracle timed on the host cores, and
 secondary figures: lm_head+argmax microseconds per token, the prompt products
-at 512, 128, 64 and 16 rows (fp32 and, at 128, bf16 store), and the batch-8 sweep.
+at 512, 128, 64 and 16 rows (fp32 and, at 128, bf16 store), the batch-8 sweep,
+the sweep as eager launches, per-call eager percentiles of the batch-1
+products, and the measured ceilings the products are read against (a
+read-only HBM stream of each product's bytes, a matrix-core loop with no
+memory traffic, and torch's bf16 matmul on dequantized weights).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--batch 1]
 """
@@ -289,7 +293,7 @@ def main():
 
     extras = {}
     if not args.skip_extras:
-        extras = secondary(torch, w4g, synth, layers, head, dev, timed, args)
+        extras = secondary(torch, w4g, synth, layers, head, dev, timed, args, make_step)
 
     cpu = None
     if not args.skip_cpu:
@@ -308,8 +312,119 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def secondary(torch, w4g, synth, layers, head, dev, timed, args):
+def ceilings(torch, layers, dev, timed):
+    """Measured ceilings: a read-only HBM stream of each product's bytes (graph of
+    16 launches cycling over enough copies to defeat the 256 MB cache; the best of
+    three launch shapes), a matrix-core loop with no memory traffic, and torch's
+    bf16 matmul (hipBLASLt) on weights dequantized to bf16 (2 bytes per weight
+    against 0.5625), for the 512-row prompt shapes."""
+    import ctypes
+    from w4_gemv_greedy_amd import build as hip_build
+    if not os.path.exists(hip_build.CEILING_LIB):
+        log("ceilings skipped: libw4g_ceiling.so not built")
+        return None
+    lib = ctypes.CDLL(hip_build.CEILING_LIB)
+    P, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.w4g_ceiling_read.argtypes = [P, SZ, I, I, I, P, P]
+    lib.w4g_ceiling_read.restype = I
+    lib.w4g_ceiling_mfma.argtypes = [I, I, P, P]
+    lib.w4g_ceiling_mfma.restype = I
+    out = {"hbm_read": {}}
+    sink = torch.zeros(1 << 20, dtype=torch.float32, device=dev)
+
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    for name, nbytes, copies in (("o_proj", gemv_bytes(HIDDEN, HIDDEN, 1), 40),
+                                 ("down", gemv_bytes(HIDDEN, INTER, 1), 12),
+                                 ("gate_up", gemv_bytes(2 * INTER, HIDDEN, 1), 6),
+                                 ("lm_head", gemv_bytes(VOCAB, HIDDEN, 1), 2)):
+        nb = nbytes // 16 * 16
+        bufs = [torch.full((nb,), c, dtype=torch.uint8, device=dev) for c in range(copies)]
+        best = None
+        for blocks, threads, u in ((256, 1024, 4), (2048, 256, 4), (4096, 256, 2)):
+            def run(blocks=blocks, threads=threads, u=u):
+                for i in range(16):
+                    st = lib.w4g_ceiling_read(bufs[i % copies].data_ptr(), nb, blocks, threads, u,
+                                              sink.data_ptr(), stream())
+                    if st != 0:
+                        raise RuntimeError(f"w4g_ceiling_read: hip error {st}")
+            ms, _ = timed(run, 10, 2, True)
+            us = ms * 1e3 / 16
+            if best is None or us < best[0]:
+                best = (us, f"{blocks}x{threads}, {u} loads in flight")
+        out["hbm_read"][name] = {"bytes": nb, "us": round(best[0], 2),
+                                 "GBps": round(nb / (best[0] * 1e-6) / 1e9, 1), "launch": best[1]}
+        del bufs
+    torch.cuda.empty_cache()
+
+    blocks, iters = 1024, 400
+    flop = blocks * 4 * iters * 8 * 32768
+
+    def mf():
+        st = lib.w4g_ceiling_mfma(blocks, iters, sink.data_ptr(), stream())
+        if st != 0:
+            raise RuntimeError(f"w4g_ceiling_mfma: hip error {st}")
+    ms, _ = timed(mf, 10, 2, True)
+    out["mfma_bf16_loop_TFLOPS"] = round(flop / (ms * 1e-3) / 1e12, 1)
+
+    # torch bf16 matmul on dequantized weights (w = q*s + b, rounded to bf16)
+    shifts = torch.arange(0, 32, 4, dtype=torch.int32, device=dev)
+    tm = {}
+    for name, idx, N, K in (("o_proj", 0, HIDDEN, HIDDEN), ("gate_up", 1, 2 * INTER, HIDDEN),
+                            ("down", 2, HIDDEN, INTER)):
+        m = layers[0][idx]
+        q = ((m.wq.unsqueeze(-1) >> shifts) & 15).reshape(N, K).float()
+        w = (q.view(N, K // 64, 64) * m.sc.float().unsqueeze(-1) + m.bi.float().unsqueeze(-1))
+        w = w.reshape(N, K).to(torch.bfloat16).contiguous()
+        del q
+        x = torch.randn((512, K), device=dev).to(torch.bfloat16)
+        y = torch.empty((512, N), dtype=torch.bfloat16, device=dev)
+
+        def mm(x=x, w=w, y=y):
+            torch.mm(x, w.t(), out=y)
+        ms, _ = timed(mm, 10, 3, True, reps=4)
+        tm[name] = round(2.0 * 512 * N * K / (ms * 1e-3) / 1e12, 1)
+        del w
+    out["torch_bf16_matmul_m512_TFLOPS"] = tm
+    torch.cuda.empty_cache()
+    return out
+
+
+def eager_percentiles(torch, w4g, layers, dev, calls=160):
+    """Per-call times of the batch-1 products as eager launches (HIP events around
+    each call, cycling over the 16 layers' weights): median, p10 and p90 in us."""
+    res = {}
+    from w4_gemv_greedy_amd import synth
+    for name, idx, N, K in (("o_proj", 0, HIDDEN, HIDDEN), ("gate_up", 1, 2 * INTER, HIDDEN),
+                            ("down", 2, HIDDEN, INTER)):
+        x = make_x(1, K, 5, synth.GENERIC, 98, dev)
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        for l in range(LAYERS):
+            m = layers[l][idx]
+            w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        torch.cuda.synchronize()
+        for i in range(calls):
+            m = layers[i % LAYERS][idx]
+            ev[i][0].record()
+            w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        res[name] = {"median_us": round(float(np.median(t)), 2), "p10_us": round(float(np.percentile(t, 10)), 2),
+                     "p90_us": round(float(np.percentile(t, 90)), 2), "calls": calls}
+    return res
+
+
+def secondary(torch, w4g, synth, layers, head, dev, timed, args, make_step):
     ex = {}
+    # the sweep as eager launches (no graph)
+    step_e, _, _ = make_step(1)
+    ms_e, _ = timed(step_e, 10, 3, False)
+    ex["sweep_b1_eager_us"] = round(ms_e * 1e3, 1)
+    ex["b1_eager_per_call"] = eager_percentiles(torch, w4g, layers, dev)
+    log(f"sweep B=1 eager {ex['sweep_b1_eager_us']} us/step; per call {ex['b1_eager_per_call']}")
     # the 16 gate-up launches of a step alone, back to back in a graph
     xg_in = [make_x(1, HIDDEN, 5, synth.GATE_UP, l, dev) for l in range(LAYERS)]
     yg_out = torch.empty((1, 2 * INTER), dtype=torch.float32, device=dev)
@@ -486,6 +601,9 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args):
         ms_f, _ = timed(head8_fused, 10, 2, True, reps=2)
         ex["lm_head_argmax_b8"] = {"us_per_call": round(ms * 1e3, 1), "fused_ids_only_us_per_call": round(ms_f * 1e3, 1)}
         log(f"lm_head+argmax B=8: {ex['lm_head_argmax_b8']}")
+
+    ex["ceilings"] = ceilings(torch, layers, dev, timed)
+    log(f"ceilings: {ex['ceilings']}")
     return ex
 
 

@@ -11,6 +11,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4g.so")
 SOURCES = ["gemv.hip", "gemv_mfma.hip", "gemm.hip", "argmax.hip", "abi.hip"]
+# measurement kernels (HBM read and matrix-core ceilings), a library of their own
+# that only the benchmark loads
+CEILING_LIB = os.path.join(HERE, "libw4g_ceiling.so")
+CEILING_SOURCE = "ceiling.hip"
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -35,7 +39,7 @@ def build(quiet=False):
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     jobs = []
-    for src in SOURCES:
+    for src in SOURCES + [CEILING_SOURCE]:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         jobs.append((obj, [hipcc] + FLAGS + EXTRA.get(src, []) +
                      ["-c", os.path.join(CSRC, src), "-o", obj]))
@@ -47,12 +51,12 @@ def build(quiet=False):
             raise RuntimeError(f"hipcc failed ({rc}) on {os.path.basename(obj)}:\n{msgs}")
         if msgs.strip():
             out.append(msgs)
-    tmp = LIB + ".tmp"
-    rc, msgs = _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + [j[0] for j in jobs] +
-                    ["-o", tmp])
-    if rc != 0:
-        raise RuntimeError(f"link failed ({rc}):\n{msgs}")
-    os.replace(tmp, LIB)
+    for lib, objs in ((LIB, [j[0] for j in jobs[:len(SOURCES)]]), (CEILING_LIB, [jobs[-1][0]])):
+        tmp = lib + ".tmp"
+        rc, msgs = _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + objs + ["-o", tmp])
+        if rc != 0:
+            raise RuntimeError(f"link of {os.path.basename(lib)} failed ({rc}):\n{msgs}")
+        os.replace(tmp, lib)
     if out and not quiet:
         print("\n".join(out), file=sys.stderr)
     return LIB

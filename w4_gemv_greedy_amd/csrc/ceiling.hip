@@ -1,0 +1,99 @@
+// Measurement kernels: the ceilings the products are read against, not part of
+// the products or of their C ABI (built into libw4g_ceiling.so, loaded by the
+// benchmark only).
+//
+// w4g_ceiling_read: a read-only stream of `bytes` (a multiple of 16) with
+// 16-byte vector loads; workgroup b reads the contiguous slice
+// [b * per, (b + 1) * per), its threads striding through it with U loads in
+// flight each.  Nothing is written unless the XOR of everything read equals a
+// fixed constant (never, for the benchmark's buffers), so the loads cannot be
+// dropped.
+//
+// w4g_ceiling_mfma: every wave issues `iters` rounds of eight independent
+// v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 each, 32,768 FLOP), with no memory
+// traffic, and stores only if a result equals a fixed constant.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+typedef __bf16 bf16x8_c __attribute__((ext_vector_type(8)));
+typedef float f32x16_c __attribute__((ext_vector_type(16)));
+
+namespace {
+
+template <int U>
+__global__ __launch_bounds__(1024) void read_kernel(const uint4* __restrict__ p, int64_t n16, int64_t per16,
+                                                    uint32_t* __restrict__ sink) {
+  const int64_t beg = (int64_t)blockIdx.x * per16;
+  const int64_t end = beg + per16 < n16 ? beg + per16 : n16;
+  uint32_t acc = 0;
+  for (int64_t i = beg + threadIdx.x; i < end; i += (int64_t)blockDim.x * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = i + (int64_t)u * blockDim.x;
+      v[u] = j < end ? p[j] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+__global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  uint4 ra, rb;
+  ra.x = 0x3F803F80u ^ (uint32_t)lane;  // bf16 values near 1.0, lane dependent
+  ra.y = ra.z = ra.w = ra.x;
+  rb.x = 0x3F803F80u ^ (uint32_t)(lane >> 1);
+  rb.y = rb.z = rb.w = rb.x;
+  const bf16x8_c a = __builtin_bit_cast(bf16x8_c, ra);
+  const bf16x8_c b = __builtin_bit_cast(bf16x8_c, rb);
+  f32x16_c acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][15];
+  if (s == 1234.5f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Returns a hipError_t value (0 on success); 1 (hipErrorInvalidValue) for a
+// bad size or launch shape.
+int w4g_ceiling_read(const void* p, size_t bytes, int blocks, int threads, int loads_in_flight,
+                     uint32_t* sink, void* stream) {
+  if (!p || !sink || bytes % 16 || blocks < 1 || threads < 64 || threads > 1024 || threads % 64)
+    return (int)hipErrorInvalidValue;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t per16 = (n16 + blocks - 1) / blocks;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  switch (loads_in_flight) {
+    case 2: hipLaunchKernelGGL(read_kernel<2>, dim3(blocks), dim3(threads), 0, s, q, n16, per16, sink); break;
+    case 4: hipLaunchKernelGGL(read_kernel<4>, dim3(blocks), dim3(threads), 0, s, q, n16, per16, sink); break;
+    case 8: hipLaunchKernelGGL(read_kernel<8>, dim3(blocks), dim3(threads), 0, s, q, n16, per16, sink); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+// FLOP per launch: blocks * 4 waves * iters * 8 * 32,768.  `sink` holds
+// blocks * 256 floats.
+int w4g_ceiling_mfma(int blocks, int iters, float* sink, void* stream) {
+  if (!sink || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), iters, sink);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"
