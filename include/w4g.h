@@ -146,11 +146,17 @@ int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
  * family stages x in LDS when B * 2.125 * K bytes fit in 152 KiB and in
  * registers otherwise; W4G_GEMV_VALU_REGS forces the register variant (for
  * checking that both variants give the same bits).
- * The matrix-core family (W4G_GEMV_MFMA) feeds the codes to
- * v_mfma_f32_32x32x16_bf16 as exact bf16 values 128 + q; per 64-group it adds
- * s*P_g and (b - 128 s)*X_g in fp32 (P_g the matrix-core group product, X_g
- * the fp32 group sum of x), wave w of four taking the groups g = w (mod 4) in
- * ascending order, and the four wave sums are added in ascending order.
+ * The matrix-core family (W4G_GEMV_MFMA) feeds the codes to the matrix cores
+ * as exact bf16 values 128 + q; per 64-group it adds s*P_g and
+ * (b - 128 s)*X_g in fp32 (P_g the matrix-core group product from zero, X_g
+ * the fp32 group sum of x).  Where eight rows of x fit in LDS (K up to about
+ * 9,000; a function of N and K only) it runs one workgroup per CU on
+ * v_mfma_f32_16x16x32_bf16 (two instructions per group): W = min(8, NI) waves,
+ * NI = ceil(K / 128) items of two groups, wave w summing items
+ * [w NI / W, (w + 1) NI / W) in ascending order, the W wave sums added in
+ * ascending order.  Otherwise v_mfma_f32_32x32x16_bf16 (four per group), wave
+ * w of four taking the groups g = w (mod 4) in ascending order, the four wave
+ * sums added in ascending order.
  * Within one family, row m of a B-row call is bitwise equal to the same row
  * computed alone; the two families agree within fp32 rounding, not bitwise.
  */

@@ -57,13 +57,13 @@ def _copy_row(wq, sc, bi, src, dst):
     wq[dst], sc[dst], bi[dst] = wq[src], sc[src], bi[src]
 
 
-@pytest.mark.parametrize("B,K", [(1, 1024), (3, 1024), (8, 10240)])
-def test_fused_planted_rows(B, K):
+@pytest.mark.parametrize("B,K,N", [(1, 1024, 9000), (3, 1024, 9000), (8, 10240, 9000), (4, 1024, 12000)])
+def test_fused_planted_rows(B, K, N):
     """Equal rows give equal logits bit for bit (each row's arithmetic is its own),
     so copying a batch row's winner to a lower id must move the answer there, a
     copy to a higher id must not, and an infinite scale makes the row fail.
-    (B = 8 at K = 10240 runs the matrix-core family: x would not fit in LDS.)"""
-    N = 9000
+    (B = 8 at K = 10240 runs the matrix-core family with the activations staged
+    in stages, B = 4 over 12000 rows its one-workgroup-per-CU kernel.)"""
     wq, sc, bi, x = _case(N, K, B, 11)
     ids0, _, ref0, _ = _run(wq, sc, bi, x)
     win = int(ids0[0])

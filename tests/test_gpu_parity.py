@@ -118,6 +118,22 @@ def test_gemv_short_layout_ragged():
     assert_close(y1[:, rows], oracle.qmm_rows(wq, sc, bi, x[:1], rows), f"gemv short N={N} K={K}")
 
 
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_gemv_mfma_staged_fallback(B):
+    """K = 73,728: one row of activations does not fit the per-CU matrix-core
+    kernel's LDS, so the family stages them per 1024-element stage instead;
+    against the oracle, and the fused head over the same product."""
+    N, K = 300, 73728
+    wq, sc, bi, x = _case(N, K, B, 21)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y = down(w4g.qmm_gemv(*W, up_bf16(x), kernel=2))
+    assert_close(y, oracle.qmm(wq, sc, bi, x), f"gemv[mfma staged] B={B}")
+    if B >= 3:  # the automatic family is the matrix cores here (x is staged in registers otherwise)
+        ids, lg = w4g.qmm_gemv_argmax(*W, up_bf16(x))
+        assert np.array_equal(down(lg).view(np.uint32), y.view(np.uint32))
+        assert np.array_equal(ids_down(ids), oracle.argmax(y))
+
+
 def test_gemv_families_agree():
     wq, sc, bi, x = _case(256, 5120, 4, 12)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x))

@@ -750,7 +750,7 @@ hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_
 }
 
 int64_t gemv_argmax_records(int B, int64_t N, int64_t K) {
-  if (gemv_auto_family(B, N, K) == 2) return gemv_mfma_argmax_records(N);
+  if (gemv_auto_family(B, N, K) == 2) return gemv_mfma_argmax_records(B, N, K);
   if (use_regs(B, K, false)) {
     const int R = regs_rows(B);
     return (N + 2 * R - 1) / (2 * R);
@@ -769,14 +769,16 @@ hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const 
   return dispatch<true>(wq, scales, biases, x, y, rec, B, N, K, false, stream);
 }
 
-// Measured with the per-CU layouts: the vector ALUs are faster whenever x fits
-// in LDS (gate-up at B = 8: 47 against 50 us; o_proj at every B), except on
-// vocabulary-wide products from B = 7 (lm_head at B = 8: 322 against 282 us);
-// where x is staged in registers the matrix cores win from B = 3 (down at B = 4:
-// 46 against 39 us, at B = 8: 76 against 42 us).
+// Measured with the per-CU layouts of both families (graph-timed, B = 1..8):
+// the vector ALUs are faster at small B, the matrix cores from B = 4 where a
+// CU holds more than 40 rows (gate-up at B = 4: 31.7 against 33.8 us, at B = 8:
+// 34.2 against 50.2; lm_head at B = 4: 195 against 207, at B = 8: 192 against
+// 306), from B = 7 for the layer widths (o_proj at B = 8: 11.5 against 12.8),
+// and where x is staged in registers from B = 3 (down at B = 5: 42 against 55,
+// at B = 8: 43 against 75).
 int gemv_auto_family(int B, int64_t N, int64_t K) {
   if (use_regs(B, K, false)) return B <= 2 ? 1 : 2;
-  if (B >= 7 && per_cu_rows(N) >= 2 * 16 * 16) return 2;
+  if (B >= 7 || (B >= 4 && per_cu_rows(N) > 40)) return 2;
   return 1;
 }
 

@@ -295,10 +295,312 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
   }
 }
 
+// ---- One workgroup per CU (the per-CU matrix-core layout) ----
+//
+// Workgroup b owns rows [b * rpw, (b + 1) * rpw) (rpw = ceil(N / 256)) as tiles
+// of 16 rows, and stages the activations of its batch rows once, whole, in LDS
+// (used where eight rows' activations fit, whatever B is).  Its W
+// waves (W = min(8, NI), NI = ceil(G / 2) items of two consecutive groups
+// (2i, 2i + 1)) split the items of every tile into contiguous ranges: wave w
+// takes items [w NI / W, (w + 1) NI / W) of each tile in ascending order, the
+// tiles one after the other, through a ring of P items in flight.
+//
+// v_mfma_f32_16x16x32_bf16: A = activations (batch row m = lane & 15, rows
+// m >= B zero), B = codes of the tile's 16 rows expanded to 128 + q (row
+// lane & 15); the K quarter q = lane >> 4 of an instruction is one code word.
+// Lane l loads 16 bytes of row l / 4 (part p = l % 4: for p < 2 words 4p ..
+// 4p + 3 of group 2i, for p >= 2 the same words of group 2i + 1), so four
+// adjacent lanes read one row's 64 contiguous bytes and the L1 sees one access
+// per row; a ds_bpermute moves them to lane (n = row, q = p) of the
+// instruction's layout, and one v_permlane32_swap per word pair then gives
+// every quarter two words of each group (quarter 0: words 0,1; 1: words 4,5;
+// 2: words 2,3; 3: words 6,7), the first for the group's first instruction and
+// the second for its second.  The activations are staged in that order.  The
+// scale and bias pairs come the same way (each lane loads those of the row it
+// loads codes of; four adjacent lanes share the address).
+//
+// Arithmetic per (row n, batch row b): for each group g the matrix core forms
+// P_g = sum_{k in g} x*(128 + q) from zero over two instructions; the wave
+// then adds s*P_g and (b_g - 128 s)*X_g in fp32 (X_g as in the kernel above).
+// Wave w's sum covers its range of groups in ascending order; the W wave sums
+// are added in ascending wave order.  The order depends on K alone (W and the
+// ranges are functions of K), and each batch row is its own.  Activation rows
+// past the batch read row B - 1: they only reach result rows that are never
+// read.
+//
+// Tiles run in batches of TB (as many as LDS holds partial sums for): each
+// wave writes its partial sums of a tile to LDS when it finishes its share,
+// and after the batch, at one barrier, the wave sums are added; so no barrier
+// and no global store sits among the code loads in flight.  The results stay
+// in LDS until the end, then are written out; AM folds them into the
+// workgroup's argmax record per batch row instead of or beside the store.
+
+constexpr int kCuRows = 16;      // rows per tile
+constexpr int kCuMaxWaves = 8;   // waves per workgroup
+
+__device__ __forceinline__ bf16x8_t zero_bf16x8() { return __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u)); }
+
+// LDS barrier for data exchanged through LDS only: the loads in flight are not
+// waited for
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+template <bool EVENG>
+struct CuItem {
+  uint4 c;  // 16 bytes of codes, as loaded (see above)
+  // EVENG: the scale pair and the bias pair (bf16 x 2) of the item's groups for
+  // the row this lane loaded codes of; else this lane's row's one by one
+  uint32_t s[EVENG ? 1 : 2], b[EVENG ? 1 : 2];
+};
+
+template <bool EVENG, bool AM, int P>
+__global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
+    const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const uint16_t* __restrict__ x, float* __restrict__ y, int B, int64_t N, int64_t K, int64_t rpw,
+    int TB, uint2* __restrict__ rec) {
+  extern __shared__ uint4 s_mem[];
+  __shared__ uint64_t s_best[AM ? 8 : 1];
+  __shared__ uint32_t s_bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = (int)(blockDim.x >> 6);
+  const int n16 = lane & 15, q = lane >> 4;
+  const int G = (int)(K >> 6), NI = (G + 1) >> 1;
+  const int64_t KW = K >> 3;
+  const int64_t r0 = (int64_t)blockIdx.x * rpw;
+  const int64_t r1 = N - r0 < rpw ? N : r0 + rpw;
+  const int nrows = (int)(r1 - r0);
+  const int T = (nrows + kCuRows - 1) / kCuRows;
+  // this wave's items of every tile: [ist, iend) (contiguous, >= 1 since W <= NI)
+  const int ist = (int)((int64_t)wave * NI / W), iend = (int)((int64_t)(wave + 1) * NI / W);
+  const int cnt = iend - ist;
+  const int n_items = T * cnt;
+
+  const int XS = B > 4 ? 8 : 4;                                      // batch slots per group sum
+  uint4* s_x = s_mem;                                                // [G][2][4][B]
+  float* s_X = reinterpret_cast<float*>(s_mem + (int64_t)G * 8 * B);  // [G][XS]
+  float* s_red = s_X + (int64_t)G * XS;                              // [TB][W][32][4]
+  float* s_y = s_red + TB * W * 128;                                 // [B][rpw]
+
+  // Per-lane LDS offsets.  Lanes whose activation row m = n16 is past the batch
+  // read row B - 1: they only feed result rows m >= B, which are never used.
+  const int lane_a = q * B + (n16 < B ? n16 : B - 1);  // uint4, within a (group, half) block
+  const int stride_g = 8 * B;                           // uint4 per group
+  const int xq = XS == 8 ? 4 * (q & 1) : 0;             // first batch row of this lane's results
+
+  // ---- item issue.  Codes: lane l reads 16 bytes of row l / 4 of the tile
+  // (four adjacent lanes read one row's 64 bytes, so the L1 sees one access per
+  // row, not one per lane); part p = l % 4 is words 4 (p % 2) .. + 3 of group
+  // g0 + p / 2.  The consumer moves each lane's 16 bytes to lane
+  // (row, quarter p), the matrix-core layout, through the LDS crossbar.
+  const int pc = lane & 3;
+  int it_t = 0, it_i = ist;
+  const uint32_t* cptr;
+  const uint16_t *sptr, *bptr;
+  auto set_tile = [&]() {
+    const int64_t rt = r0 + (int64_t)it_t * kCuRows;
+    int64_t rc = rt + (lane >> 2);
+    rc = rc < r1 ? rc : r1 - 1;
+    cptr = wq + rc * KW + (pc & 1) * 4 + (pc >> 1) * 8;
+    if constexpr (EVENG) {
+      sptr = scales + rc * G;
+      bptr = biases + rc * G;
+    } else {
+      int64_t rn = rt + n16;
+      rn = rn < r1 ? rn : r1 - 1;
+      sptr = scales + rn * G;
+      bptr = biases + rn * G;
+    }
+  };
+  set_tile();
+  auto issue = [&](CuItem<EVENG>& it) {
+    const int g0 = 2 * it_i;
+    int off = g0 * 8;
+    if (!EVENG && g0 + 1 >= G && pc >= 2) off -= 8;  // an odd last group: parts 2, 3 reread it (unused)
+    it.c = *reinterpret_cast<const uint4*>(cptr + off);
+    if constexpr (EVENG) {
+      it.s[0] = *reinterpret_cast<const uint32_t*>(sptr + g0);
+      it.b[0] = *reinterpret_cast<const uint32_t*>(bptr + g0);
+    } else {
+      const int g1 = g0 + 1 < G ? g0 + 1 : g0;
+      it.s[0] = sptr[g0];
+      it.s[1] = sptr[g1];
+      it.b[0] = bptr[g0];
+      it.b[1] = bptr[g1];
+    }
+    if (++it_i == iend) {
+      it_i = ist;
+      ++it_t;
+      set_tile();
+    }
+  };
+
+  // ---- stage x: segment (b, g) = 64 activations -> 8 blocks in the quarter
+  // order above, and the group sum X_g (two 32-element halves over natural pairs)
+  const int nseg = B * G;
+  auto load_seg = [&](int seg, uint4 (&v)[8]) {
+    const int g = seg / B, bb = seg - g * B;  // batch row fastest: conflict-free LDS writes
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)bb * K + (int64_t)g * 64);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[j];
+  };
+  auto put_seg = [&](int seg, const uint4 (&v)[8]) {
+    const int g = seg / B, bb = seg - g * B;
+    float h0 = 0.0f, h1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int qq = ((j >> 1) & 1) * 2 + (j >> 2), hh = j & 1;
+      s_x[g * stride_g + hh * 4 * B + qq * B + bb] = permute_block(v[j]);
+      float& h = j < 4 ? h0 : h1;
+      h = dot2(v[j].x, kOnes, h);
+      h = dot2(v[j].y, kOnes, h);
+      h = dot2(v[j].z, kOnes, h);
+      h = dot2(v[j].w, kOnes, h);
+    }
+    s_X[g * XS + bb] = h0 + h1;
+  };
+  uint4 pre[8];
+  const bool has_pre = tid < nseg;
+  if (has_pre) load_seg(tid, pre);
+
+  CuItem<EVENG> ring[P];
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl) issue(ring[sl]);
+
+  if (has_pre) put_seg(tid, pre);
+  for (int seg = tid + (int)blockDim.x; seg < nseg; seg += (int)blockDim.x) {
+    uint4 v[8];
+    load_seg(seg, v);
+    put_seg(seg, v);
+  }
+  for (int i = tid; i < XS * G; i += (int)blockDim.x)  // the unused batch slots of the group sums
+    if ((i & (XS - 1)) >= B) s_X[i] = 0.0f;
+  if (AM && tid < 8) s_best[tid] = 0;
+  if (AM && tid == 0) s_bad = 0;
+  __syncthreads();
+
+  // ---- stream, TB tiles at a time: each wave writes its partial sums of a
+  // tile to LDS as it finishes its share (from a register that holds the
+  // address, so nothing on that path waits for the loads in flight), and when
+  // a batch of tiles is done the wave sums are added, at two barriers
+  const uint32_t m = 0x000F000Fu, gm = kMagic128;
+  f32x4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
+  int ci = ist, bt = 0, tb0 = 0;
+  float* const red_base = s_red + (wave * 32 + lane) * 4;
+  float* red_ptr = red_base;
+  auto group = [&](int g, uint32_t w0, uint32_t w1, uint32_t sb, uint32_t bb) {
+    const int ab = lane_a + g * stride_g;
+    const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, s_x[ab]);
+    const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, s_x[ab + 4 * B]);
+    const float4 xs = *reinterpret_cast<const float4*>(s_X + g * XS + xq);
+    f32x4_t pg = {0.0f, 0.0f, 0.0f, 0.0f};
+    pg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, expand128(w0, m, gm), pg, 0, 0, 0);
+    pg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, expand128(w1, m, gm), pg, 0, 0, 0);
+    const float sc = bf16_to_f32(sb);
+    const float cb = __builtin_fmaf(-128.0f, sc, bf16_to_f32(bb));
+    tot[0] = __builtin_fmaf(cb, xs.x, __builtin_fmaf(sc, pg[0], tot[0]));
+    tot[1] = __builtin_fmaf(cb, xs.y, __builtin_fmaf(sc, pg[1], tot[1]));
+    tot[2] = __builtin_fmaf(cb, xs.z, __builtin_fmaf(sc, pg[2], tot[2]));
+    tot[3] = __builtin_fmaf(cb, xs.w, __builtin_fmaf(sc, pg[3], tot[3]));
+  };
+  auto reduce_batch = [&]() {
+    // add the wave sums of the batch's bt tiles in ascending wave order
+    lds_barrier();
+    const int nout = bt * kCuRows * B;
+    for (int o = tid; o < nout; o += (int)blockDim.x) {
+      const int tb = o / (kCuRows * B), rem = o - tb * (kCuRows * B);
+      const int n = rem / B, bq = rem - n * B;
+      const int row = (tb0 + tb) * kCuRows + n;
+      if (row < nrows) {
+        const float* pr = s_red + (tb * W * 32 + n + 16 * (bq >> 2)) * 4 + (bq & 3);
+        float acc = pr[0];
+        for (int w = 1; w < W; ++w) acc += pr[w * 128];
+        s_y[bq * (int)rpw + row] = acc;
+      }
+    }
+    lds_barrier();
+  };
+  const int src_lane = ((n16 << 2) | q) << 2;  // byte address of lane 4 n + q
+  auto consume = [&](const CuItem<EVENG>& it) {
+    // lane (n, q) takes the 16 bytes lane 4 n + q loaded
+    const uint32_t c0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.x);
+    const uint32_t c1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.y);
+    const uint32_t c2 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.z);
+    const uint32_t c3 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.w);
+    // quarters 0,1 hold group 2i's words, 2,3 group 2i + 1's: swap word pairs across
+    const auto sx = __builtin_amdgcn_permlane32_swap(c0, c2, false, false);
+    const auto sy = __builtin_amdgcn_permlane32_swap(c1, c3, false, false);
+    const int g0 = 2 * ci;
+    if constexpr (EVENG) {
+      // the scale and bias pairs of row n, from the same lane as the codes
+      const uint32_t sp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.s[0]);
+      const uint32_t bp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.b[0]);
+      group(g0, sx[0], sy[0], sp & 0xFFFFu, bp & 0xFFFFu);
+      group(g0 + 1, sx[1], sy[1], sp >> 16, bp >> 16);
+    } else {
+      group(g0, sx[0], sy[0], it.s[0], it.b[0]);
+      if (g0 + 1 < G) group(g0 + 1, sx[1], sy[1], it.s[1], it.b[1]);
+    }
+    if (++ci == iend) {  // this wave's share of a tile is done: its partial sums to LDS
+      ci = ist;
+      if (lane < 32) *reinterpret_cast<f32x4_t*>(red_ptr) = tot;
+      red_ptr += W * 32 * 4;
+      tot = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if (++bt == TB || tb0 + bt == T) {
+        reduce_batch();
+        tb0 += bt;
+        bt = 0;
+        red_ptr = red_base;
+      }
+    }
+  };
+  // steady state (every issued item exists), then the last items
+  int j = 0;
+  for (; j + 2 * P - 1 < n_items; j += P) {
+#pragma unroll
+    for (int sl = 0; sl < P; ++sl) {
+      consume(ring[sl]);
+      issue(ring[sl]);
+    }
+  }
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl) {
+    if (j + sl < n_items) consume(ring[sl]);
+    if (j + sl + P < n_items) issue(ring[sl]);
+  }
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl)
+    if (j + P + sl < n_items) consume(ring[sl]);
+
+  // ---- results (the last reduction ended with a barrier)
+  const int nout = B * nrows;
+  if (!AM || y != nullptr) {
+    for (int o = tid; o < nout; o += (int)blockDim.x) {
+      const int bq = o / nrows, row = o - bq * nrows;
+      y[(int64_t)bq * N + r0 + row] = s_y[bq * (int)rpw + row];
+    }
+  }
+  if constexpr (AM) {
+    for (int o = tid; o < nout; o += (int)blockDim.x) {
+      const int bq = o / nrows, row = o - bq * nrows;
+      const uint32_t u = __float_as_uint(s_y[bq * (int)rpw + row]);
+      if (!finite_bits(u))
+        __hip_atomic_fetch_or(&s_bad, 1u << bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      else
+        __hip_atomic_fetch_max(&s_best[bq], cand(u, (uint32_t)(r0 + row)), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    if (tid < B)
+      rec[(int64_t)tid * gridDim.x + blockIdx.x] = make_record(s_best[tid], ((s_bad >> tid) & 1u) != 0, (uint32_t)r0);
+  }
+}
+
 template <bool AM>
-hipError_t launch(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                  const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
-                  hipStream_t stream) {
+hipError_t launch_stage(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                        const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                        hipStream_t stream) {
   const int64_t blocks = (N + 31) / 32;
   const bool vec = ((K >> 6) % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
                                              reinterpret_cast<uintptr_t>(biases)) & 15u) == 0;
@@ -311,6 +613,66 @@ hipError_t launch(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
   return hipGetLastError();
 }
 
+constexpr int kCUs = 256;                  // compute units of the MI355X
+constexpr int kMaxBatch = 8;               // decode batch rows at most
+constexpr size_t kCuMaxLds = 152 * 1024;   // dynamic LDS asked for (of 160 KiB per CU)
+
+int64_t cu_rows(int64_t N) { return (N + kCUs - 1) / kCUs; }
+int cu_waves(int64_t K) {
+  const int64_t NI = ((K >> 6) + 1) >> 1;
+  return NI < kCuMaxWaves ? (int)NI : kCuMaxWaves;
+}
+int cu_tiles(int64_t N) { return (int)((cu_rows(N) + kCuRows - 1) / kCuRows); }
+size_t cu_lds_fixed(int Bc, int64_t N, int64_t K) {
+  const int64_t G = K >> 6;
+  return (size_t)(G * 8 * Bc) * 16 + (size_t)G * (Bc > 4 ? 8 : 4) * 4 + (size_t)Bc * cu_rows(N) * 4;
+}
+size_t cu_tile_bytes(int64_t K) { return (size_t)cu_waves(K) * 32 * 4 * 4; }
+// tiles per batch: as many as the LDS left holds partial sums for (0: none fits)
+int cu_batch_tiles(int Bc, int64_t N, int64_t K) {
+  const size_t fixed = cu_lds_fixed(Bc, N, K);
+  if (fixed + cu_tile_bytes(K) > kCuMaxLds) return 0;
+  const int64_t t = (int64_t)((kCuMaxLds - fixed) / cu_tile_bytes(K));
+  return t < cu_tiles(N) ? (int)t : cu_tiles(N);
+}
+size_t cu_lds_bytes(int Bc, int64_t N, int64_t K) {
+  return cu_lds_fixed(Bc, N, K) + (size_t)cu_batch_tiles(Bc, N, K) * cu_tile_bytes(K);
+}
+// The per-CU kernel runs where the activations of the largest batch (8 rows)
+// fit in its LDS, so one pass serves any B; else (K above about 9,000: the
+// down projection) the staged kernel above does.  A function of (N, K) only,
+// so a batch row's arithmetic does not depend on B.
+bool use_cu(int64_t N, int64_t K) { return cu_batch_tiles(kMaxBatch, N, K) > 0; }
+
+template <bool EVENG, bool AM>
+hipError_t launch_cu_pass(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                          const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                          hipStream_t stream) {
+  const int64_t rpw = cu_rows(N);
+  const int64_t blocks = (N + rpw - 1) / rpw;
+  const size_t lds = cu_lds_bytes(B, N, K);
+  const void* fn = reinterpret_cast<const void*>(&gemv_mfma_cu_kernel<EVENG, AM, 4>);
+  if (lds > 64 * 1024) {
+    // a host-side attribute of the kernel (not a stream operation)
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kCuMaxLds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((gemv_mfma_cu_kernel<EVENG, AM, 4>), dim3((unsigned)blocks), dim3(64 * cu_waves(K)), lds,
+                     stream, wq, scales, biases, x, y, B, N, K, rpw, cu_batch_tiles(B, N, K), rec);
+  return hipGetLastError();
+}
+
+template <bool AM>
+hipError_t launch(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                  const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                  hipStream_t stream) {
+  if (!use_cu(N, K)) return launch_stage<AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
+  const bool eveng = ((K >> 6) % 2) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
+                                               reinterpret_cast<uintptr_t>(biases)) & 3u) == 0;
+  return eveng ? launch_cu_pass<true, AM>(wq, scales, biases, x, y, rec, B, N, K, stream)
+               : launch_cu_pass<false, AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
@@ -319,7 +681,11 @@ hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const ui
   return launch<false>(wq, scales, biases, x, y, nullptr, B, N, K, stream);
 }
 
-int64_t gemv_mfma_argmax_records(int64_t N) { return (N + 31) / 32; }
+int64_t gemv_mfma_argmax_records(int B, int64_t N, int64_t K) {
+  (void)B;
+  if (!use_cu(N, K)) return (N + 31) / 32;
+  return (N + cu_rows(N) - 1) / cu_rows(N);
+}
 
 hipError_t launch_gemv_mfma_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                                    const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,

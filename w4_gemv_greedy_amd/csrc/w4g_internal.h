@@ -51,11 +51,12 @@ hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const 
                               const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                               hipStream_t stream);
 int64_t gemv_argmax_records(int B, int64_t N, int64_t K);
-// The matrix-core family's epilogue variant: one record per 32 rows.
+// The matrix-core family's epilogue variant: one record per workgroup (per CU,
+// or per 32 rows where the activations are staged in stages).
 hipError_t launch_gemv_mfma_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                                    const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                                    hipStream_t stream);
-int64_t gemv_mfma_argmax_records(int64_t N);
+int64_t gemv_mfma_argmax_records(int B, int64_t N, int64_t K);
 
 constexpr int kArgmaxBlock = 1024;  // ids per pass-1 record
 constexpr uint32_t kArgmaxFlag = 0x80000000u;  // non-finite bit of a record's id word
