@@ -289,8 +289,8 @@ __device__ __forceinline__ void bias_and_store_any(f32x16_t (&tot)[TI][TJ], cons
 // Workgroup tile 128 x 128 of Y, four waves in a 2 x 2 grid, each owning 64 x 64
 // (2 x 2 matrix-core tiles).  Per 64-group one stage holds in LDS
 //   A: 128 rows x 64 permuted activations (16-byte chunk c of row r stored at
-//      chunk c ^ (r & 7), so a wave's reads of one chunk column spread over
-//      the banks),
+//      chunk c ^ ((r >> 1) & 7): sixteen consecutive rows' chunk c, which one
+//      16-lane LDS pass reads, land in sixteen distinct 16-byte bank slots),
 //   B: the 128 columns' code halves, [half][column] x 16 bytes,
 //   S: the 128 columns' scales.
 // Global loads run two groups ahead in registers, and LDS is double-buffered,
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   const int wb_off = (int)(bcol * K8 * 4) + bh * 16;
   const int scol = tid & (kTN - 1);
   const int ws_off = (int)(scol * G * 2);
-  const int a_w = srow * 128 + ((sch ^ (srow & 7)) << 4);  // + 32 i * 128
+  const int a_w = srow * 128 + ((sch ^ ((srow >> 1) & 7)) << 4);  // + 32 i * 128
   const int b_w = kAStage + bh * (kTN * 16) + bcol * 16;
   const int s_w = kAStage + kBStage + scol * 2;
 
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      a_r[i][t] = (wm * 64 + i * 32 + l32) * 128 + ((((t + 4 * h) ^ (l32 & 7))) << 4);
+      a_r[i][t] = (wm * 64 + i * 32 + l32) * 128 + ((((t + 4 * h) ^ ((l32 >> 1) & 7))) << 4);
   int b_r[2], s_r[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
