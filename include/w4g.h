@@ -154,9 +154,12 @@ int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
  * v_mfma_f32_16x16x32_bf16 (two instructions per group): W = min(8, NI) waves,
  * NI = ceil(K / 128) items of two groups, wave w summing items
  * [w NI / W, (w + 1) NI / W) in ascending order, the W wave sums added in
- * ascending order.  Otherwise v_mfma_f32_32x32x16_bf16 (four per group), wave
- * w of four taking the groups g = w (mod 4) in ascending order, the four wave
- * sums added in ascending order.
+ * ascending order.  Where x does not fit but a CU holds at most 32 rows
+ * (N <= 8,192) the same kernel shape and order runs with x staged in LDS one
+ * step of items at a time (so the same bits as the whole-x kernel).
+ * Otherwise v_mfma_f32_32x32x16_bf16 (four per group), wave w of four taking
+ * the groups g = w (mod 4) in ascending order, the four wave sums added in
+ * ascending order.
  * Within one family, row m of a B-row call is bitwise equal to the same row
  * computed alone; the two families agree within fp32 rounding, not bitwise.
  */

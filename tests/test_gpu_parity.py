@@ -118,20 +118,28 @@ def test_gemv_short_layout_ragged():
     assert_close(y1[:, rows], oracle.qmm_rows(wq, sc, bi, x[:1], rows), f"gemv short N={N} K={K}")
 
 
+@pytest.mark.parametrize("N,K", [(300, 73728), (6999, 12288), (33, 9920), (9000, 10240)])
 @pytest.mark.parametrize("B", [1, 3, 8])
-def test_gemv_mfma_staged_fallback(B):
-    """K = 73,728: one row of activations does not fit the per-CU matrix-core
-    kernel's LDS, so the family stages them per 1024-element stage instead;
-    against the oracle, and the fused head over the same product."""
-    N, K = 300, 73728
+def test_gemv_mfma_large_k(N, K, B):
+    """K too large for eight rows of activations in the per-CU kernel's LDS: a CU
+    holding one or two 16-row tiles stages them step by step (N = 300: one tile;
+    6999: two, the last workgroup ragged; K = 9920: an odd group count), more
+    tiles per CU take the 32-row staged kernel (N = 9000); against the oracle.
+    The fused head over the same shape is checked against the plain product of
+    the family the automatic choice takes (the matrix cores or the vector
+    path, depending on the shape)."""
+    if N * K * B > 250_000_000 and B != 3:
+        pytest.skip("large shape: B = 3 only")
     wq, sc, bi, x = _case(N, K, B, 21)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
     y = down(w4g.qmm_gemv(*W, up_bf16(x), kernel=2))
-    assert_close(y, oracle.qmm(wq, sc, bi, x), f"gemv[mfma staged] B={B}")
-    if B >= 3:  # the automatic family is the matrix cores here (x is staged in registers otherwise)
-        ids, lg = w4g.qmm_gemv_argmax(*W, up_bf16(x))
-        assert np.array_equal(down(lg).view(np.uint32), y.view(np.uint32))
-        assert np.array_equal(ids_down(ids), oracle.argmax(y))
+    y_ref = oracle.qmm(wq, sc, bi, x)
+    assert_close(y, y_ref, f"gemv[mfma] N={N} K={K} B={B}")
+    ya = down(w4g.qmm_gemv(*W, up_bf16(x)))
+    assert_close(ya, y_ref, f"gemv[auto] N={N} K={K} B={B}")
+    ids, lg = w4g.qmm_gemv_argmax(*W, up_bf16(x))
+    assert np.array_equal(down(lg).view(np.uint32), ya.view(np.uint32))
+    assert np.array_equal(ids_down(ids), oracle.argmax(ya))
 
 
 def test_gemv_families_agree():

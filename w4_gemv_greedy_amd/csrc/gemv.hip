@@ -771,11 +771,13 @@ hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const 
 
 // Measured with the per-CU layouts of both families (graph-timed, B = 1..8):
 // the vector ALUs are faster at small B, the matrix cores from B = 4 where a
-// CU holds more than 40 rows (gate-up at B = 4: 31.7 against 33.8 us, at B = 8:
-// 34.2 against 50.2; lm_head at B = 4: 195 against 207, at B = 8: 192 against
+// CU holds more than 40 rows (gate-up at B = 4: 31.6 against 33.2 us, at B = 8:
+// 34.0 against 50.2; lm_head at B = 4: 195 against 207, at B = 8: 192 against
 // 306), from B = 7 for the layer widths (o_proj at B = 8: 11.5 against 12.8),
-// and where x is staged in registers from B = 3 (down at B = 5: 42 against 55,
-// at B = 8: 43 against 75).
+// and where x is staged in registers from B = 3 (down, K = 17408, leaves the
+// vector-ALU kernel's LDS from B = 5: 27.6 against 55.2 at B = 5, 29.1 against
+// 75 at B = 8; at B = 3 and 4 it stays in LDS, 19.8 and 23.3 against 26.8 and
+// 26.9).
 int gemv_auto_family(int B, int64_t N, int64_t K) {
   if (use_regs(B, K, false)) return B <= 2 ? 1 : 2;
   if (B >= 7 || (B >= 4 && per_cu_rows(N) > 40)) return 2;

@@ -597,6 +597,247 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   }
 }
 
+// ---- The per-CU layout where x does not fit in LDS (the down projection) ----
+//
+// Same rows, tiles, waves, items and arithmetic as gemv_mfma_cu_kernel (so the
+// same bits), for a CU holding one or two tiles: instead of staging all of x,
+// the waves advance through their item ranges in lockstep, one item per tile
+// per step, and step s's activations (each wave's two groups, all batch rows)
+// sit in one of two LDS buffers.  Threads load the activations of step s + SPB
+// as the step starts (SPB steps ahead, as the codes are) and store them into
+// the free buffer when the next step's turn comes, then all meet at one
+// barrier per step.  Each wave keeps one running sum per tile; the wave sums
+// are added once, at the end.
+template <bool EVENG, bool AM, int TT>
+__global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cuk_kernel(
+    const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
+    const uint16_t* __restrict__ x, float* __restrict__ y, int B, int64_t N, int64_t K, int64_t rpw,
+    uint2* __restrict__ rec) {
+  static_assert(TT == 1 || TT == 2, "one or two tiles per CU (activations loaded two or more steps ahead)");
+  constexpr int SPB = 4 / TT;  // steps per unrolled body (code items in flight: P = TT * SPB = 4)
+  constexpr int P = TT * SPB;
+  extern __shared__ uint4 s_mem[];
+  __shared__ uint64_t s_best[AM ? 8 : 1];
+  __shared__ uint32_t s_bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = (int)(blockDim.x >> 6);
+  const int n16 = lane & 15, q = lane >> 4;
+  const int G = (int)(K >> 6), NI = (G + 1) >> 1;
+  const int64_t KW = K >> 3;
+  const int64_t r0 = (int64_t)blockIdx.x * rpw;
+  const int64_t r1 = N - r0 < rpw ? N : r0 + rpw;
+  const int nrows = (int)(r1 - r0);
+  const int ist = (int)((int64_t)wave * NI / W), iend = (int)((int64_t)(wave + 1) * NI / W);
+  const int cnt = iend - ist;
+  const int S = (NI + W - 1) / W;  // steps: the most items any wave has per tile
+
+  const int XS = B > 4 ? 8 : 4;
+  uint4* s_xs = s_mem;                                                     // [2][W][2][2][4][B]
+  float* s_Xs = reinterpret_cast<float*>(s_mem + 2 * W * 16 * B);          // [2][W][2][XS]
+  float* s_red = s_Xs + 2 * W * 2 * XS;                                    // [TT][W][32][4]
+  float* s_y = s_red + TT * W * 128;                                       // [B][rpw]
+  const int stride_buf = W * 16 * B;  // uint4 per buffer
+
+  // ---- codes: as in gemv_mfma_cu_kernel, tile t's pointers fixed
+  const int pc = lane & 3;
+  const uint32_t* cptr[TT];
+  const uint16_t* sptr[TT];
+  const uint16_t* bptr[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const int64_t rt = r0 + (int64_t)t * kCuRows;
+    int64_t rc = rt + (lane >> 2);
+    rc = rc < r1 ? rc : r1 - 1;
+    cptr[t] = wq + rc * KW + (pc & 1) * 4 + (pc >> 1) * 8;
+    if constexpr (EVENG) {
+      sptr[t] = scales + rc * G;
+      bptr[t] = biases + rc * G;
+    } else {
+      int64_t rn = rt + n16;
+      rn = rn < r1 ? rn : r1 - 1;
+      sptr[t] = scales + rn * G;
+      bptr[t] = biases + rn * G;
+    }
+  }
+  // item (step s, tile t): item index ist + s, clamped to the wave's last (loads
+  // stay unconditional so the waits count exactly; a clamped item is not consumed)
+  auto issue = [&](CuItem<EVENG>& it, int s, int t) {
+    const int i = ist + (s < cnt ? s : cnt - 1);
+    const int g0 = 2 * i;
+    int off = g0 * 8;
+    if (!EVENG && g0 + 1 >= G && pc >= 2) off -= 8;
+    it.c = *reinterpret_cast<const uint4*>(cptr[t] + off);
+    if constexpr (EVENG) {
+      it.s[0] = *reinterpret_cast<const uint32_t*>(sptr[t] + g0);
+      it.b[0] = *reinterpret_cast<const uint32_t*>(bptr[t] + g0);
+    } else {
+      const int g1 = g0 + 1 < G ? g0 + 1 : g0;
+      it.s[0] = sptr[t][g0];
+      it.s[1] = sptr[t][g1];
+      it.b[0] = bptr[t][g0];
+      it.b[1] = bptr[t][g1];
+    }
+  };
+
+  // ---- activations of a step: half-segment h = (wave w, group gg, row bb,
+  // half) of 32 elements per staging thread (the two halves of a group in
+  // adjacent lanes, whose sums meet over a lane swap)
+  const int H = W * 2 * B * 2;
+  const int xhalf = tid & 1, xrest = tid >> 1;
+  const int xbb = xrest % B, xgg = (xrest / B) & 1, xw = xrest / (2 * B);
+  const int xist = (int)((int64_t)xw * NI / W), xcnt = (int)((int64_t)(xw + 1) * NI / W) - xist;
+  auto x_load = [&](int s, uint4 (&v)[4]) {
+    const int g = 2 * (xist + s) + xgg;
+    const bool ok = tid < H && s < xcnt && g < G;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (ok ? (int64_t)xbb * K + (int64_t)g * 64 + xhalf * 32 : 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ok ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto x_store = [&](const uint4 (&v)[4], int buf) {
+    float h = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h = dot2(v[i].x, kOnes, h);
+      h = dot2(v[i].y, kOnes, h);
+      h = dot2(v[i].z, kOnes, h);
+      h = dot2(v[i].w, kOnes, h);
+    }
+    const float other = __shfl_xor(h, 1);
+    if (tid < H) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = xhalf * 4 + i;  // block of the group
+        const int qq = ((j >> 1) & 1) * 2 + (j >> 2), hh = j & 1;
+        s_xs[buf * stride_buf + (((xw * 2 + xgg) * 2 + hh) * 4 + qq) * B + xbb] = permute_block(v[i]);
+      }
+      if (xhalf == 0) s_Xs[((buf * W + xw) * 2 + xgg) * XS + xbb] = h + other;  // first half + second
+    }
+  };
+
+  // ---- per-lane LDS offsets (as in gemv_mfma_cu_kernel)
+  const int lane_a = q * B + (n16 < B ? n16 : B - 1);
+  const int xq = XS == 8 ? 4 * (q & 1) : 0;
+  const int src_lane = ((n16 << 2) | q) << 2;
+  const uint32_t m = 0x000F000Fu, gm = kMagic128;
+  f32x4_t tot[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) tot[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto group = [&](f32x4_t& acc, int buf, int gg, int g, uint32_t w0, uint32_t w1, uint32_t sb, uint32_t bb) {
+    const int ab = buf * stride_buf + ((wave * 2 + gg) * 2) * 4 * B + lane_a;
+    const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, s_xs[ab]);
+    const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, s_xs[ab + 4 * B]);
+    const float4 xs = *reinterpret_cast<const float4*>(s_Xs + ((buf * W + wave) * 2 + gg) * XS + xq);
+    f32x4_t pg = {0.0f, 0.0f, 0.0f, 0.0f};
+    pg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, expand128(w0, m, gm), pg, 0, 0, 0);
+    pg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, expand128(w1, m, gm), pg, 0, 0, 0);
+    const float sc = bf16_to_f32(sb);
+    const float cb = __builtin_fmaf(-128.0f, sc, bf16_to_f32(bb));
+    acc[0] = __builtin_fmaf(cb, xs.x, __builtin_fmaf(sc, pg[0], acc[0]));
+    acc[1] = __builtin_fmaf(cb, xs.y, __builtin_fmaf(sc, pg[1], acc[1]));
+    acc[2] = __builtin_fmaf(cb, xs.z, __builtin_fmaf(sc, pg[2], acc[2]));
+    acc[3] = __builtin_fmaf(cb, xs.w, __builtin_fmaf(sc, pg[3], acc[3]));
+    (void)g;
+  };
+  auto consume = [&](const CuItem<EVENG>& it, f32x4_t& acc, int s, int buf) {
+    const uint32_t c0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.x);
+    const uint32_t c1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.y);
+    const uint32_t c2 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.z);
+    const uint32_t c3 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.w);
+    const auto sx = __builtin_amdgcn_permlane32_swap(c0, c2, false, false);
+    const auto sy = __builtin_amdgcn_permlane32_swap(c1, c3, false, false);
+    const int g0 = 2 * (ist + s);
+    if constexpr (EVENG) {
+      const uint32_t sp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.s[0]);
+      const uint32_t bp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.b[0]);
+      group(acc, buf, 0, g0, sx[0], sy[0], sp & 0xFFFFu, bp & 0xFFFFu);
+      group(acc, buf, 1, g0 + 1, sx[1], sy[1], sp >> 16, bp >> 16);
+    } else {
+      group(acc, buf, 0, g0, sx[0], sy[0], it.s[0], it.b[0]);
+      if (g0 + 1 < G) group(acc, buf, 1, g0 + 1, sx[1], sy[1], it.s[1], it.b[1]);
+    }
+  };
+
+  // ---- prologue: the first SPB steps' activations, the first P code items
+  uint4 xr[SPB][4];
+#pragma unroll
+  for (int u = 0; u < SPB; ++u) x_load(u, xr[u]);
+  CuItem<EVENG> ring[P];
+#pragma unroll
+  for (int u = 0; u < SPB; ++u)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) issue(ring[u * TT + t], u, t);
+  x_store(xr[0], 0);
+  if (AM && tid < 8) s_best[tid] = 0;
+  if (AM && tid == 0) s_bad = 0;
+  __syncthreads();
+
+  // ---- steps, SPB per unrolled body: step s consumes buffer s % 2; the
+  // activations of step s + 1 (loaded SPB - 1 steps earlier) go into the other
+  // buffer before the step's barrier, and those of step s + SPB are loaded
+  for (int s0 = 0; s0 < S; s0 += SPB) {
+#pragma unroll
+    for (int u = 0; u < SPB; ++u) {
+      const int s = s0 + u;
+      if (s < S) {
+        const int buf = s & 1;
+        if (s < cnt) {
+#pragma unroll
+          for (int t = 0; t < TT; ++t) {
+            consume(ring[u * TT + t], tot[t], s, buf);
+            issue(ring[u * TT + t], s + SPB, t);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < TT; ++t) issue(ring[u * TT + t], s + SPB, t);
+        }
+        if (s + 1 < S) x_store(xr[(u + 1) % SPB], buf ^ 1);
+        x_load(s + SPB, xr[u]);
+        lds_barrier();
+      }
+    }
+  }
+
+  // ---- the wave sums, in ascending wave order, then the results
+  if (lane < 32) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t) *reinterpret_cast<f32x4_t*>(s_red + ((t * W + wave) * 32 + lane) * 4) = tot[t];
+  }
+  __syncthreads();
+  for (int o = tid; o < TT * kCuRows * B; o += (int)blockDim.x) {
+    const int tb = o / (kCuRows * B), rem = o - tb * (kCuRows * B);
+    const int n = rem / B, bq = rem - n * B;
+    const int row = tb * kCuRows + n;
+    if (row < nrows) {
+      const float* pr = s_red + (tb * W * 32 + n + 16 * (bq >> 2)) * 4 + (bq & 3);
+      float acc = pr[0];
+      for (int w = 1; w < W; ++w) acc += pr[w * 128];
+      s_y[bq * (int)rpw + row] = acc;
+    }
+  }
+  __syncthreads();
+  const int nout = B * nrows;
+  if (!AM || y != nullptr) {
+    for (int o = tid; o < nout; o += (int)blockDim.x) {
+      const int bq = o / nrows, row = o - bq * nrows;
+      y[(int64_t)bq * N + r0 + row] = s_y[bq * (int)rpw + row];
+    }
+  }
+  if constexpr (AM) {
+    for (int o = tid; o < nout; o += (int)blockDim.x) {
+      const int bq = o / nrows, row = o - bq * nrows;
+      const uint32_t u = __float_as_uint(s_y[bq * (int)rpw + row]);
+      if (!finite_bits(u))
+        __hip_atomic_fetch_or(&s_bad, 1u << bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      else
+        __hip_atomic_fetch_max(&s_best[bq], cand(u, (uint32_t)(r0 + row)), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    if (tid < B)
+      rec[(int64_t)tid * gridDim.x + blockIdx.x] = make_record(s_best[tid], ((s_bad >> tid) & 1u) != 0, (uint32_t)r0);
+  }
+}
+
 template <bool AM>
 hipError_t launch_stage(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                         const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
@@ -639,10 +880,35 @@ size_t cu_lds_bytes(int Bc, int64_t N, int64_t K) {
   return cu_lds_fixed(Bc, N, K) + (size_t)cu_batch_tiles(Bc, N, K) * cu_tile_bytes(K);
 }
 // The per-CU kernel runs where the activations of the largest batch (8 rows)
-// fit in its LDS, so one pass serves any B; else (K above about 9,000: the
-// down projection) the staged kernel above does.  A function of (N, K) only,
-// so a batch row's arithmetic does not depend on B.
+// fit in its LDS, so one pass serves any B (K above about 9,000, as in the
+// down projection, does not).  A function of (N, K) only, so a batch row's
+// arithmetic does not depend on B.
 bool use_cu(int64_t N, int64_t K) { return cu_batch_tiles(kMaxBatch, N, K) > 0; }
+// Otherwise, where a CU holds one or two tiles (N <= 8,192), the per-CU kernel
+// that stages the activations step by step; else the staged kernel above.
+bool use_cuk(int64_t N, int64_t K) { return !use_cu(N, K) && cu_tiles(N) <= 2 && (K >> 6) >= 2; }
+size_t cuk_lds_bytes(int B, int64_t N, int64_t K) {
+  const int W = cu_waves(K), XS = B > 4 ? 8 : 4;
+  return (size_t)2 * W * 16 * B * 16 + (size_t)2 * W * 2 * XS * 4 + (size_t)cu_tiles(N) * W * 128 * 4 +
+         (size_t)B * cu_rows(N) * 4;
+}
+
+template <bool EVENG, bool AM>
+hipError_t launch_cuk(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                      const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                      hipStream_t stream) {
+  const int64_t rpw = cu_rows(N);
+  const int64_t blocks = (N + rpw - 1) / rpw;
+  const size_t lds = cuk_lds_bytes(B, N, K);
+  if (cu_tiles(N) == 1) {
+    hipLaunchKernelGGL((gemv_mfma_cuk_kernel<EVENG, AM, 1>), dim3((unsigned)blocks), dim3(64 * cu_waves(K)), lds,
+                       stream, wq, scales, biases, x, y, B, N, K, rpw, rec);
+  } else {
+    hipLaunchKernelGGL((gemv_mfma_cuk_kernel<EVENG, AM, 2>), dim3((unsigned)blocks), dim3(64 * cu_waves(K)), lds,
+                       stream, wq, scales, biases, x, y, B, N, K, rpw, rec);
+  }
+  return hipGetLastError();
+}
 
 template <bool EVENG, bool AM>
 hipError_t launch_cu_pass(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
@@ -666,11 +932,15 @@ template <bool AM>
 hipError_t launch(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                   const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                   hipStream_t stream) {
-  if (!use_cu(N, K)) return launch_stage<AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
   const bool eveng = ((K >> 6) % 2) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
                                                reinterpret_cast<uintptr_t>(biases)) & 3u) == 0;
-  return eveng ? launch_cu_pass<true, AM>(wq, scales, biases, x, y, rec, B, N, K, stream)
-               : launch_cu_pass<false, AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
+  if (use_cu(N, K))
+    return eveng ? launch_cu_pass<true, AM>(wq, scales, biases, x, y, rec, B, N, K, stream)
+                 : launch_cu_pass<false, AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
+  if (use_cuk(N, K))
+    return eveng ? launch_cuk<true, AM>(wq, scales, biases, x, y, rec, B, N, K, stream)
+                 : launch_cuk<false, AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
+  return launch_stage<AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
 }
 
 }  // namespace
@@ -683,7 +953,7 @@ hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const ui
 
 int64_t gemv_mfma_argmax_records(int B, int64_t N, int64_t K) {
   (void)B;
-  if (!use_cu(N, K)) return (N + 31) / 32;
+  if (!use_cu(N, K) && !use_cuk(N, K)) return (N + 31) / 32;
   return (N + cu_rows(N) - 1) / cu_rows(N);
 }
 
