@@ -11,10 +11,13 @@
  *       Receipt.
  *     - fp32 accumulation and an fp32 store: the same PR, commit "Add the
  *       pair seam and register its kernels with the kernel contract".
- *     - The K reduction order is a function of the matrix width K alone,
- *       never of N, the batch, the grid or timing: TensorFold PR #1433,
- *       step-2 description (a rank's K tree is its own full matrix's; the
- *       split is keyed on the whole matrix, not on a slice).
+ *     - Within a kernel family (qmm_gemv_ex) the K reduction order is a
+ *       function of the matrix width K alone, never of N, the batch, the
+ *       grid or timing: TensorFold PR #1433, step-2 description (a rank's K
+ *       tree is its own full matrix's; the split is keyed on the whole
+ *       matrix, not on a slice).  qmm_gemv picks the family by B and shape
+ *       (see there), so its bits are a function of (B, N, K); a caller that
+ *       needs a row to keep its bits at every batch size names the family.
  *     qmm_gemv is the decode path (1 <= B <= 8 activation rows); qmm_gemm is
  *     the prompt path (any M >= 1, matrix cores).
  *
@@ -139,6 +142,7 @@ int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
 #define W4G_GEMV_VALU 1   /* vector-ALU dot2 kernel (the order documented for qmm_gemv) */
 #define W4G_GEMV_MFMA 2   /* matrix-core kernel (order documented below) */
 #define W4G_GEMV_VALU_REGS 3  /* vector-ALU family, register-staged variant (same bits as 1) */
+#define W4G_GEMV_MFMA_STEP 4  /* matrix-core family, step-staged variant (same bits as 2) */
 
 /*
  * qmm_gemv with an explicit kernel family.  Same arguments and results as
@@ -149,17 +153,14 @@ int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
  * The matrix-core family (W4G_GEMV_MFMA) feeds the codes to the matrix cores
  * as exact bf16 values 128 + q; per 64-group it adds s*P_g and
  * (b - 128 s)*X_g in fp32 (P_g the matrix-core group product from zero, X_g
- * the fp32 group sum of x).  Where eight rows of x fit in LDS (K up to about
- * 9,000; a function of N and K only) it runs one workgroup per CU on
- * v_mfma_f32_16x16x32_bf16 (two instructions per group): W = min(8, NI) waves,
- * NI = ceil(K / 128) items of two groups, wave w summing items
+ * the fp32 group sum of x).  One workgroup per CU on v_mfma_f32_16x16x32_bf16
+ * (two instructions per group), the CU's rows in 16-row tiles: W = min(8, NI)
+ * waves, NI = ceil(K / 128) items of two groups, wave w summing items
  * [w NI / W, (w + 1) NI / W) in ascending order, the W wave sums added in
- * ascending order.  Where x does not fit but a CU holds at most 32 rows
- * (N <= 8,192) the same kernel shape and order runs with x staged in LDS one
- * step of items at a time (so the same bits as the whole-x kernel).
- * Otherwise v_mfma_f32_32x32x16_bf16 (four per group), wave w of four taking
- * the groups g = w (mod 4) in ascending order, the four wave sums added in
- * ascending order.
+ * ascending order.  x is held whole in LDS where eight rows of it fit (K up
+ * to about 9,000) and staged one step of items at a time otherwise
+ * (W4G_GEMV_MFMA_STEP forces the latter, for checking that both give the
+ * same bits); the choice depends on K alone.
  * Within one family, row m of a B-row call is bitwise equal to the same row
  * computed alone; the two families agree within fp32 rounding, not bitwise.
  */

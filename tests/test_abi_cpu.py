@@ -94,6 +94,7 @@ def test_gemv_rejects(lib):
     assert gemv(lib, y=X) == _lib.EALIAS
     assert gemv(lib, y=WQ + 64) == _lib.EALIAS
     assert gemv(lib, y=SC) == _lib.EALIAS
+    assert gemv(lib, kernel=5) == _lib.EDTYPE
     assert gemv(lib, kernel=7) == _lib.EDTYPE
     assert gemv(lib, kernel=-1) == _lib.EDTYPE
 
@@ -215,10 +216,8 @@ def test_workspace_sizes(lib):
     # of qmm_gemv's own choice for the shape: 32 rows per workgroup for the
     # vocabulary-wide head at B = 1, else one workgroup per CU, in both families
     # (the matrix cores run B = 8 over the vocabulary and B >= 3 where x leaves
-    # the vector-ALU kernel's LDS: down at B = 5, not at B = 4), and one per 32
-    # rows where the matrix cores stage the activations per 1024-element stage
-    # (eight rows' activations do not fit in LDS and a CU holds more than two
-    # 16-row tiles: 9000 x 10240)
+    # the vector-ALU kernel's LDS: down at B = 5, not at B = 4; their per-CU
+    # kernels serve any N and K, 9000 x 10240 included)
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 248320, 5120) == 7760 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 5120, 5120) == 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 4, 248320, 5120) == 4 * 256 * 8
@@ -228,7 +227,7 @@ def test_workspace_sizes(lib):
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 3, 300, 73728) == 3 * 150 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 4, 5120, 17408) == 4 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 5, 5120, 17408) == 5 * 256 * 8
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 9000, 10240) == 8 * 282 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 9000, 10240) == 8 * 250 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 9, 248320, 5120) == size_max
     assert lib.qmm_workspace_bytes(7, 1, 1, 64) == size_max
 

@@ -35,13 +35,15 @@ def _run(wq, sc, bi, x, want_logits=True):
 
 
 @pytest.mark.parametrize("N,K", [(37, 64), (1000, 1024), (4099, 2048), (20000, 5120), (3000, 17408),
-                                 (6001, 12288)])
+                                 (6001, 12288), (40000, 8192)])
 @pytest.mark.parametrize("B", [1, 2, 3, 8])
 def test_fused_matches_two_pass(N, K, B):
     """Fused logits bitwise those of qmm_gemv and ids those of the two-pass
     argmax, over every family and layout qmm_gemv picks for these shapes (at
     B = 8 with K = 17408 and 12288 the matrix cores stage x per step with one
-    and two 16-row tiles per CU, the latter with a ragged last workgroup)."""
+    and two 16-row tiles per CU, the latter with a ragged last workgroup; at
+    40000 x 8192 they hold x whole and fold each batch of results into the
+    record as it is reduced)."""
     wq, sc, bi, x = _case(N, K, B, N % 97 + B)
     ids, logits, ref_logits, two_pass = _run(wq, sc, bi, x)
     assert np.array_equal(logits.view(np.uint32), ref_logits.view(np.uint32)), "logits differ"

@@ -121,10 +121,10 @@ def test_gemv_short_layout_ragged():
 @pytest.mark.parametrize("N,K", [(300, 73728), (6999, 12288), (33, 9920), (9000, 10240)])
 @pytest.mark.parametrize("B", [1, 3, 8])
 def test_gemv_mfma_large_k(N, K, B):
-    """K too large for eight rows of activations in the per-CU kernel's LDS: a CU
-    holding one or two 16-row tiles stages them step by step (N = 300: one tile;
-    6999: two, the last workgroup ragged; K = 9920: an odd group count), more
-    tiles per CU take the 32-row staged kernel (N = 9000); against the oracle.
+    """K too large for eight rows of activations in the per-CU kernel's LDS: the
+    step-staged kernel takes a CU's 16-row tiles one or two at a time (N = 300:
+    one tile; 6999: two, the last workgroup ragged; K = 9920: an odd group
+    count; N = 9000: three tiles, a pair and then a single); against the oracle.
     The fused head over the same shape is checked against the plain product of
     the family the automatic choice takes (the matrix cores or the vector
     path, depending on the shape)."""
@@ -140,6 +140,23 @@ def test_gemv_mfma_large_k(N, K, B):
     ids, lg = w4g.qmm_gemv_argmax(*W, up_bf16(x))
     assert np.array_equal(down(lg).view(np.uint32), ya.view(np.uint32))
     assert np.array_equal(ids_down(ids), oracle.argmax(ya))
+
+
+@pytest.mark.parametrize("B,N,K", [(8, 5120, 5120), (3, 300, 1024), (1, 33, 128), (5, 1000, 8256),
+                                   (8, 6001, 4096), (2, 70000, 2048), (4, 37, 8320), (8, 40000, 8192)])
+def test_gemv_mfma_step_variant_bitwise(B, N, K):
+    """The step-staged per-CU matrix-core kernel, forced where the whole-x one
+    runs, gives the same bits: one order whichever of the two K selects (an odd
+    group count, a ragged last workgroup, several tile pairs per CU; at
+    40000 x 8192 the whole-x kernel's results do not fit in its LDS beside the
+    activations and are stored batch by batch)."""
+    wq, sc, bi, x = _case(N, K, B, 31 + B)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x))
+    a = down(w4g.qmm_gemv(*W, kernel=w4g.GEMV_MFMA))
+    b = down(w4g.qmm_gemv(*W, kernel=w4g.GEMV_MFMA_STEP))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    rows = np.unique(np.concatenate([np.arange(min(N, 20)), np.arange(max(0, N - 20), N)]))
+    assert_close(a[:, rows], oracle.qmm_rows(wq, sc, bi, x, rows), f"gemv[mfma] N={N} K={K} B={B}")
 
 
 def test_gemv_families_agree():

@@ -15,7 +15,7 @@ Tensors (all on one GPU, contiguous):
 import ctypes
 
 from . import _lib
-from ._lib import (BF16, F32, GEMV_AUTO, GEMV_MFMA, GEMV_VALU, GEMV_VALU_REGS,  # noqa: F401
+from ._lib import (BF16, F32, GEMV_AUTO, GEMV_MFMA, GEMV_MFMA_STEP, GEMV_VALU, GEMV_VALU_REGS,  # noqa: F401
                    MAX_GEMV_BATCH,
                    OP_ARGMAX, OP_ARGMAX_TOP2, OP_GEMM, OP_GEMV, OP_GEMV_ARGMAX, SENTINEL,
                    W4GError)
@@ -106,8 +106,9 @@ def _call_qmm(fn, op, wq, scales, biases, x, y, workspace, extra=(), y_dtypes=No
 def qmm_gemv(wq, scales, biases, x, y=None, workspace=None, kernel=GEMV_AUTO, bits=4):
     """Decode product for 1 <= B <= 8 rows of x; returns y [B][N] fp32.
 
-    kernel: GEMV_AUTO (the library's choice), GEMV_VALU, GEMV_MFMA, or
-    GEMV_VALU_REGS (the register-staged variant of the vector-ALU family).
+    kernel: GEMV_AUTO (the library's choice), GEMV_VALU, GEMV_MFMA,
+    GEMV_VALU_REGS (the register-staged variant of the vector-ALU family) or
+    GEMV_MFMA_STEP (the step-staged variant of the matrix-core family).
     bits: code width, 4 (the default) or 2 or 8 (wq [N][K*bits/32], low field
     first; the library's choice of kernel only).
     """

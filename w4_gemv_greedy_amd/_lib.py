@@ -13,7 +13,7 @@ SENTINEL = 0xFFFFFFFF
 MAX_GEMV_BATCH = 8
 ABI_VERSION = 1
 
-GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_VALU_REGS = 0, 1, 2, 3
+GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_VALU_REGS, GEMV_MFMA_STEP = 0, 1, 2, 3, 4
 
 EXPORTS = ["qmm_gemv", "qmm_gemv_ex", "qmm_gemv_bits", "qmm_gemm", "qmm_gemm_ex", "qmm_gemv_argmax", "vocab_argmax",
            "vocab_argmax_top2", "qmm_workspace_bytes", "w4g_status_string", "w4g_abi_version"]

@@ -104,7 +104,7 @@ int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* bias
                 const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
                 size_t workspace_bytes, void* stream, int kernel) {
   if (kernel != W4G_GEMV_AUTO && kernel != W4G_GEMV_VALU && kernel != W4G_GEMV_MFMA &&
-      kernel != W4G_GEMV_VALU_REGS)
+      kernel != W4G_GEMV_VALU_REGS && kernel != W4G_GEMV_MFMA_STEP)
     return W4G_EDTYPE;
   if (B < 1 || B > W4G_MAX_GEMV_BATCH)
     return (!wq || !scales || !biases || !x || !y) ? W4G_EINVAL_PTR : W4G_ESHAPE;
@@ -112,8 +112,9 @@ int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* bias
   if (rc) return rc;
   if (kernel == W4G_GEMV_AUTO) kernel = w4g::gemv_auto_family((int)B, N, K);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (kernel == W4G_GEMV_MFMA)
-    return from_hip(w4g::launch_gemv_mfma(wq, scales, biases, x, y, (int)B, N, K, s));
+  if (kernel == W4G_GEMV_MFMA || kernel == W4G_GEMV_MFMA_STEP)
+    return from_hip(w4g::launch_gemv_mfma(wq, scales, biases, x, y, (int)B, N, K,
+                                          kernel == W4G_GEMV_MFMA_STEP, s));
   return from_hip(w4g::launch_gemv(wq, scales, biases, x, y, (int)B, N, K,
                                    kernel == W4G_GEMV_VALU_REGS, s));
 }

@@ -3,33 +3,21 @@
 // Same format and result as the vector-ALU decode kernel (4-bit affine,
 // group 64: TensorFold PR #1437, Receipt; fp32 result: same PR, commit "Add
 // the pair seam and register its kernels with the kernel contract"), for
-// batches where the vector ALUs cannot keep up with HBM: a 32 x 32 x 16 bf16
-// matrix-core instruction multiplies 16 K-elements of 32 weight rows by up to
-// 32 activation rows, so every code is expanded once whatever B is.
+// batches where the vector ALUs cannot keep up with HBM: a 16 x 16 x 32 bf16
+// matrix-core instruction multiplies 32 K-elements of 16 weight rows by up to
+// 16 activation rows, so every code is expanded once whatever B is.
 //
-// Operands: A = the activations (rows b < B, the rest zero), B = the codes of
-// 32 weight rows, expanded to the exact bf16 values 128 + q.  Lane (h, n) of
-// the wave loads 16 bytes of row n: half h of one 64-group, which feeds the
-// four instructions of that group (one 32-bit code word each).  The
-// activations are staged in LDS per 1024-element chunk, permuted once into
-// the order the expansion produces.
-//
-// Arithmetic per (row n, batch row b): for each group g the matrix core forms
-// P = sum_{k in g} x*(128 + q) from zero; the lane then adds s*P and
-// (b_g - 128 s) * X_g, X_g the fp32 sum of the group's activations, in fp32.
-// X_g is the sum of the group's two 32-element halves, each summed over its
-// natural bf16 pairs in ascending order.  Wave w of the workgroup takes the
-// groups g = w (mod W) in ascending order; the W wave sums are added in
-// ascending wave order at the end.  The order
-// depends on K alone (TensorFold PR #1433, step-2 description), and every
-// batch row is computed independently of the others.
+// Two kernels with one arithmetic and one order, so the same bits: one that
+// holds the activations of the batch whole in LDS (where eight rows of them
+// fit) and one that stages them step by step (larger K).  Which one runs is a
+// function of K alone, and neither's order depends on N, B, the grid or
+// timing (TensorFold PR #1433, step-2 description: the K reduction of a row is
+// its full matrix's, whatever slice of rows a call covers).
 #include "w4g_internal.h"
 
 namespace w4g {
 namespace {
 
-constexpr int kStageGroups = 16;  // groups per staged activation chunk (1024 elements)
-constexpr int kXRows = 10;        // LDS rows per activation block
 constexpr uint32_t kMagic128 = 0x43004300u;
 constexpr uint32_t kOnes = 0x3F803F80u;
 
@@ -55,27 +43,6 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t g) {
   return d;
 }
 
-// The largest 64-bit word over the 32 lanes of each half wave, in every lane
-// of that half: partners across the two 16-lane rows, then within a row by
-// mirrors and quad swaps (each step pairs every lane with one whose set of
-// covered lanes is disjoint from its own, so the last step covers all 32).
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max64(uint64_t c) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)c, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(c >> 32), CTRL, 0xF, 0xF, false);
-  return umax64(c, ((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ uint64_t half_wave_max64(uint64_t c) {
-  const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)c, (uint32_t)c, false, false);
-  const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(c >> 32), (uint32_t)(c >> 32), false, false);
-  c = umax64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
-  c = dpp_max64<0x140>(c);  // row_mirror
-  c = dpp_max64<0x141>(c);  // row_half_mirror
-  c = dpp_max64<0x4E>(c);   // quad_perm [2,3,0,1]
-  c = dpp_max64<0xB1>(c);   // quad_perm [1,0,3,2]
-  return c;
-}
-
 // 8 codes -> bf16 values 128 + q in the order q0,q4,q1,q5,q2,q6,q3,q7
 __device__ __forceinline__ bf16x8_t expand128(uint32_t w, uint32_t m, uint32_t g) {
   uint4 p;
@@ -84,215 +51,6 @@ __device__ __forceinline__ bf16x8_t expand128(uint32_t w, uint32_t m, uint32_t g
   p.z = and_or(w >> 8, m, g);
   p.w = and_or(w >> 12, m, g);
   return __builtin_bit_cast(bf16x8_t, p);
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& v, int t) {
-  return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
-}
-
-// Codes, scales and biases of one stage of one wave.  VEC: the scales and
-// biases come as one 16-byte vector per lane (lane (h, n): groups 8h .. 8h + 7
-// of the stage for row n; a 2-byte load per group and row would cost an L1
-// tag lookup per lane), else one 2-byte load per group.
-template <int GPS, bool VEC>
-struct Ring {
-  uint4 c[GPS];
-  uint32_t s[VEC ? 1 : GPS], b[VEC ? 1 : GPS];
-  uint4 sv, bv;
-};
-
-__device__ __forceinline__ uint32_t bf16_at(const uint4& v, int i) {
-  const uint32_t w = i >> 1 == 0 ? v.x : i >> 1 == 1 ? v.y : i >> 1 == 2 ? v.z : v.w;
-  return (w >> ((i & 1) * 16)) & 0xFFFFu;
-}
-
-// The workgroup's four waves split the K groups round robin; each stage of 16
-// groups gives every wave GPS = 16 / W of them.  The activations of a stage are
-// staged in one of two LDS buffers while the other feeds the matrix cores.
-//
-// AM adds the argmax's pass 1 as an epilogue: per batch row, the best (value,
-// lowest row) of the workgroup's 32 rows, or the non-finite flag, goes to
-// rec[b][blockIdx.x] (one record per 32 rows); y may then be null.
-template <int W, bool VEC, bool AM>
-__global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __restrict__ wq,
-                                                           const uint16_t* __restrict__ scales,
-                                                           const uint16_t* __restrict__ biases,
-                                                           const uint16_t* __restrict__ x,
-                                                           float* __restrict__ y, int B, int64_t N,
-                                                           int64_t K, uint2* __restrict__ rec) {
-  constexpr int GPS = kStageGroups / W;
-  // [buf][8-element block][slot]: slots 0..7 hold the batch rows (row r of
-  // block k at slot r ^ ((k >> 3) & 7), so the staging writes of different
-  // groups land in different banks), slot 8 zeros, slot 9 padding so the two
-  // half-group reads of a wave fall in different banks
-  __shared__ uint4 s_x[2][kStageGroups * 8][kXRows];
-  __shared__ float s_X[2][8][kStageGroups];      // [buf][b][group]: group sums
-  __shared__ float s_red[W][4][64];              // wave sums
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int arow = l32 < 8 ? l32 : 8;  // activation row this lane feeds; rows >= B are zero
-  const uint32_t m = 0x000F000Fu, g = kMagic128;
-  const int64_t n0 = (int64_t)blockIdx.x * 32;
-  const int64_t n = (n0 + l32 < N) ? n0 + l32 : N - 1;
-  const int64_t G = K >> 6;
-  const int nstage = (int)((G + kStageGroups - 1) / kStageGroups);
-  const uint32_t* wrow = wq + n * (K >> 3);
-  const uint16_t* srow = scales + n * G;
-  const uint16_t* brow = biases + n * G;
-
-  // codes of stage st for this wave (groups past the end reread the row's last
-  // group, a cache hit, so no other rows are pulled in)
-  auto issue = [&](Ring<GPS, VEC>& r, int st) {
-#pragma unroll
-    for (int j = 0; j < GPS; ++j) {
-      int64_t g = (int64_t)st * kStageGroups + wave + W * j;
-      g = g < G ? g : G - 1;
-      r.c[j] = *reinterpret_cast<const uint4*>(wrow + g * 8 + h * 4);
-      if constexpr (!VEC) {
-        r.s[j] = srow[g];
-        r.b[j] = brow[g];
-      }
-    }
-    if constexpr (VEC) {  // G % 8 == 0: clamp the block start to the row's last 8 groups
-      int64_t g8 = (int64_t)st * kStageGroups + 8 * h;
-      g8 = g8 <= G - 8 ? g8 : G - 8;
-      r.sv = *reinterpret_cast<const uint4*>(srow + g8);
-      r.bv = *reinterpret_cast<const uint4*>(brow + g8);
-    }
-  };
-
-  // activation staging: thread -> (row xb, group xg, half xh) of a stage, 32 elements
-  const int xb = tid >> 5, xg = (tid & 31) >> 1, xhalf = tid & 1;
-  const bool xload = (64 * W >= 256) && xb < B;
-  uint4 xr[4];
-  auto load_x = [&](int st) {
-    const int64_t g = (int64_t)st * kStageGroups + xg;
-    const bool ok = xload && st < nstage && g < G;
-    const uint4* src = reinterpret_cast<const uint4*>(x + (ok ? (int64_t)xb * K + g * 64 + xhalf * 32 : 0));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xr[i] = ok ? src[i] : make_uint4(0u, 0u, 0u, 0u);
-  };
-  auto store_x = [&](int buf) {
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s_x[buf][xg * 8 + xhalf * 4 + i][xb ^ (xg & 7)] = permute_block(xr[i]);
-      part = dot2(xr[i].x, kOnes, part);
-      part = dot2(xr[i].y, kOnes, part);
-      part = dot2(xr[i].z, kOnes, part);
-      part = dot2(xr[i].w, kOnes, part);
-    }
-    const float other = __shfl_xor(part, 1);
-    if (xhalf == 0) s_X[buf][xb][xg] = part + other;  // first half + second half
-  };
-
-  float tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  // The stage's GPS groups run their four-instruction matrix-core chains side
-  // by side (instruction t of every group, then t + 1), so the chains overlap;
-  // each group's partial is still its own, and the groups are added to the
-  // running sums in ascending order.
-  auto compute = [&](const Ring<GPS, VEC>& r, int st, int buf) {
-    f32x16_t p[GPS];
-    bf16x8_t bop[GPS][4];
-    uint4 av[GPS][4];
-#pragma unroll
-    for (int j = 0; j < GPS; ++j) {
-      const int gl = wave + W * j;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        av[j][t] = s_x[buf][gl * 8 + h * 4 + t][arow < 8 ? arow ^ (gl & 7) : 8];
-        bop[j][t] = expand128(word(r.c[j], t), m, g);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) p[j][v] = 0.0f;
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < GPS; ++j)
-        p[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[j][t]),
-                                                       bop[j][t], p[j], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < GPS; ++j) {
-      const int gl = wave + W * j;
-      if ((int64_t)st * kStageGroups + gl < G) {
-        uint32_t sbits, bbits;
-        if constexpr (VEC) {
-          // this lane's vector holds the group when gl / 8 == h, else its partner's does
-          const uint32_t so = bf16_at(r.sv, gl & 7), bo = bf16_at(r.bv, gl & 7);
-          const uint32_t sp = __shfl_xor(so, 32), bp = __shfl_xor(bo, 32);
-          sbits = (gl >> 3) == h ? so : sp;
-          bbits = (gl >> 3) == h ? bo : bp;
-        } else {
-          sbits = r.s[j];
-          bbits = r.b[j];
-        }
-        const float sc = bf16_to_f32(sbits);
-        const float cb = __builtin_fmaf(-128.0f, sc, bf16_to_f32(bbits));
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          tot[v] = __builtin_fmaf(sc, p[j][v], tot[v]);
-          tot[v] = __builtin_fmaf(cb, s_X[buf][4 * h + v][gl], tot[v]);
-        }
-      }
-    }
-  };
-
-  // the zero slot that lanes 8..31 read as their activation operand
-  for (int i = tid; i < 2 * kStageGroups * 8; i += 64 * W)
-    s_x[i / (kStageGroups * 8)][i % (kStageGroups * 8)][8] = make_uint4(0u, 0u, 0u, 0u);
-
-  // Per half step: activations of stage st + 2 load first, then its codes, so
-  // the wait for stage st + 1's activations (issued a half step earlier) does
-  // not also wait for codes that are only needed later.
-  Ring<GPS, VEC> ra, rb;
-  load_x(0);
-  issue(ra, 0);
-  store_x(0);
-  load_x(1);
-  issue(rb, 1);
-  __syncthreads();
-  for (int st = 0; st < nstage; st += 2) {
-    // xr holds stage st + 1
-    compute(ra, st, 0);
-    store_x(1);  // stage st + 1 (zeros past the end)
-    load_x(st + 2);
-    issue(ra, st + 2);
-    __syncthreads();
-    compute(rb, st + 1, 1);  // no-op past the last stage
-    store_x(0);  // stage st + 2
-    load_x(st + 3);
-    issue(rb, st + 3);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int v = 0; v < 4; ++v) s_red[wave][v][lane] = tot[v];
-  __syncthreads();
-  {
-    // wave v finishes column v of every lane: batch row b = 4 h + v, weight row
-    // n0 + l32 (the wave sums added in ascending wave order)
-    static_assert(W == 4, "one output column per wave");
-    const int v = wave;
-    float acc = s_red[0][v][lane];
-#pragma unroll
-    for (int w = 1; w < W; ++w) acc += s_red[w][v][lane];
-    const int b = 4 * h + v;
-    const bool valid = n0 + l32 < N;
-    if (b < B && valid && (!AM || y != nullptr)) y[(int64_t)b * N + n0 + l32] = acc;
-    if constexpr (AM) {
-      // the best candidate over the 32 rows of this half wave's batch row
-      const uint32_t u = __float_as_uint(acc);
-      const bool bad = valid && !finite_bits(u);
-      const uint64_t c = half_wave_max64((valid && !bad) ? cand(u, (uint32_t)(n0 + l32)) : 0);
-      const uint64_t badm = __ballot(bad);
-      const bool half_bad = ((badm >> (32 * h)) & 0xFFFFFFFFull) != 0;
-      if (l32 == 0 && b < B)
-        rec[(int64_t)b * gridDim.x + blockIdx.x] = make_record(c, half_bad, (uint32_t)n0);
-    }
-  }
 }
 
 // ---- One workgroup per CU (the per-CU matrix-core layout) ----
@@ -321,7 +79,9 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
 //
 // Arithmetic per (row n, batch row b): for each group g the matrix core forms
 // P_g = sum_{k in g} x*(128 + q) from zero over two instructions; the wave
-// then adds s*P_g and (b_g - 128 s)*X_g in fp32 (X_g as in the kernel above).
+// then adds s*P_g and (b_g - 128 s)*X_g in fp32 (X_g the fp32 sum of the
+// group's activations: the sum of its two 32-element halves, each summed over
+// its natural bf16 pairs in ascending order).
 // Wave w's sum covers its range of groups in ascending order; the W wave sums
 // are added in ascending wave order.  The order depends on K alone (W and the
 // ranges are functions of K), and each batch row is its own.  Activation rows
@@ -330,15 +90,18 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint32_t* __res
 //
 // Tiles run in batches of TB (as many as LDS holds partial sums for): each
 // wave writes its partial sums of a tile to LDS when it finishes its share,
-// and after the batch, at one barrier, the wave sums are added; so no barrier
-// and no global store sits among the code loads in flight.  The results stay
-// in LDS until the end, then are written out; AM folds them into the
-// workgroup's argmax record per batch row instead of or beside the store.
+// and after the batch, at one barrier, the wave sums are added.  The results
+// stay in LDS until the stream ends where they fit beside the rest (hold), so
+// no global store sits among the code loads in flight (a store there makes
+// the next waits for loads wait for it too); else each batch's are stored as
+// it is reduced.  AM folds the results into the workgroup's argmax record per
+// batch row instead of or beside the store.  The activations, their group
+// sums and one tile's partial sums must fit: a function of K alone, so
+// whether this kernel applies depends on K alone; where the results go does
+// not change them.
 
 constexpr int kCuRows = 16;      // rows per tile
 constexpr int kCuMaxWaves = 8;   // waves per workgroup
-
-__device__ __forceinline__ bf16x8_t zero_bf16x8() { return __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u)); }
 
 // LDS barrier for data exchanged through LDS only: the loads in flight are not
 // waited for
@@ -359,7 +122,7 @@ template <bool EVENG, bool AM, int P>
 __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
     const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const uint16_t* __restrict__ x, float* __restrict__ y, int B, int64_t N, int64_t K, int64_t rpw,
-    int TB, uint2* __restrict__ rec) {
+    int TB, bool hold, uint2* __restrict__ rec) {
   extern __shared__ uint4 s_mem[];
   __shared__ uint64_t s_best[AM ? 8 : 1];
   __shared__ uint32_t s_bad;
@@ -381,7 +144,7 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   uint4* s_x = s_mem;                                                // [G][2][4][B]
   float* s_X = reinterpret_cast<float*>(s_mem + (int64_t)G * 8 * B);  // [G][XS]
   float* s_red = s_X + (int64_t)G * XS;                              // [TB][W][32][4]
-  float* s_y = s_red + TB * W * 128;                                 // [B][rpw]
+  float* s_y = s_red + TB * W * 128;                                 // [B][rpw] when hold
 
   // Per-lane LDS offsets.  Lanes whose activation row m = n16 is past the batch
   // read row B - 1: they only feed result rows m >= B, which are never used.
@@ -504,19 +267,38 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
     tot[2] = __builtin_fmaf(cb, xs.z, __builtin_fmaf(sc, pg[2], tot[2]));
     tot[3] = __builtin_fmaf(cb, xs.w, __builtin_fmaf(sc, pg[3], tot[3]));
   };
+  // the result of (batch row bq, workgroup row `row`): kept in LDS until the
+  // stream ends (hold), else stored and with AM folded into the workgroup's
+  // argmax record for bq at once
+  auto put_result = [&](int bq, int row, float v) {
+    if (hold) {
+      s_y[bq * (int)rpw + row] = v;
+      return;
+    }
+    if (!AM || y != nullptr) y[(int64_t)bq * N + r0 + row] = v;
+    if constexpr (AM) {
+      const uint32_t u = __float_as_uint(v);
+      if (!finite_bits(u))
+        __hip_atomic_fetch_or(&s_bad, 1u << bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      else
+        __hip_atomic_fetch_max(&s_best[bq], cand(u, (uint32_t)(r0 + row)), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  };
   auto reduce_batch = [&]() {
-    // add the wave sums of the batch's bt tiles in ascending wave order
+    // add the wave sums of the batch's bt tiles in ascending wave order (rows
+    // fastest across threads, so the stores of a batch row are contiguous)
     lds_barrier();
     const int nout = bt * kCuRows * B;
     for (int o = tid; o < nout; o += (int)blockDim.x) {
       const int tb = o / (kCuRows * B), rem = o - tb * (kCuRows * B);
-      const int n = rem / B, bq = rem - n * B;
+      const int bq = rem / kCuRows, n = rem - bq * kCuRows;
       const int row = (tb0 + tb) * kCuRows + n;
       if (row < nrows) {
         const float* pr = s_red + (tb * W * 32 + n + 16 * (bq >> 2)) * 4 + (bq & 3);
         float acc = pr[0];
         for (int w = 1; w < W; ++w) acc += pr[w * 128];
-        s_y[bq * (int)rpw + row] = acc;
+        put_result(bq, row, acc);
       }
     }
     lds_barrier();
@@ -573,25 +355,25 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   for (int sl = 0; sl < P; ++sl)
     if (j + P + sl < n_items) consume(ring[sl]);
 
-  // ---- results (the last reduction ended with a barrier)
-  const int nout = B * nrows;
-  if (!AM || y != nullptr) {
+  // ---- held results out (the last reduction ended with a barrier), then the record
+  if (hold) {
+    const int nout = B * nrows;
     for (int o = tid; o < nout; o += (int)blockDim.x) {
       const int bq = o / nrows, row = o - bq * nrows;
-      y[(int64_t)bq * N + r0 + row] = s_y[bq * (int)rpw + row];
+      const float v = s_y[bq * (int)rpw + row];
+      if (!AM || y != nullptr) y[(int64_t)bq * N + r0 + row] = v;
+      if constexpr (AM) {
+        const uint32_t u = __float_as_uint(v);
+        if (!finite_bits(u))
+          __hip_atomic_fetch_or(&s_bad, 1u << bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        else
+          __hip_atomic_fetch_max(&s_best[bq], cand(u, (uint32_t)(r0 + row)), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
     }
+    if constexpr (AM) __syncthreads();
   }
   if constexpr (AM) {
-    for (int o = tid; o < nout; o += (int)blockDim.x) {
-      const int bq = o / nrows, row = o - bq * nrows;
-      const uint32_t u = __float_as_uint(s_y[bq * (int)rpw + row]);
-      if (!finite_bits(u))
-        __hip_atomic_fetch_or(&s_bad, 1u << bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      else
-        __hip_atomic_fetch_max(&s_best[bq], cand(u, (uint32_t)(r0 + row)), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    __syncthreads();
     if (tid < B)
       rec[(int64_t)tid * gridDim.x + blockIdx.x] = make_record(s_best[tid], ((s_bad >> tid) & 1u) != 0, (uint32_t)r0);
   }
@@ -600,20 +382,23 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
 // ---- The per-CU layout where x does not fit in LDS (the down projection) ----
 //
 // Same rows, tiles, waves, items and arithmetic as gemv_mfma_cu_kernel (so the
-// same bits), for a CU holding one or two tiles: instead of staging all of x,
+// same bits), with the activations staged step by step instead of whole: the
+// workgroup takes its tiles TT at a time (one or two), and for each such pair
 // the waves advance through their item ranges in lockstep, one item per tile
-// per step, and step s's activations (each wave's two groups, all batch rows)
-// sit in one of two LDS buffers.  Threads load the activations of step s + SPB
-// as the step starts (SPB steps ahead, as the codes are) and store them into
-// the free buffer when the next step's turn comes, then all meet at one
-// barrier per step.  Each wave keeps one running sum per tile; the wave sums
-// are added once, at the end.
+// per step, step s's activations (each wave's two groups, all batch rows)
+// sitting in one of two LDS buffers.  Threads load the activations of step
+// s + SPB as the step starts (SPB steps ahead, as the codes are) and store
+// them into the free buffer when the next step's turn comes, then all meet at
+// one barrier per step.  Each wave keeps one running sum per tile; the wave
+// sums of a pair are added when its steps are done.  A CU with more than two
+// tiles runs the pairs one after the other, staging the activations again for
+// each (they come from L2).
 template <bool EVENG, bool AM, int TT>
 __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cuk_kernel(
     const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const uint16_t* __restrict__ x, float* __restrict__ y, int B, int64_t N, int64_t K, int64_t rpw,
     uint2* __restrict__ rec) {
-  static_assert(TT == 1 || TT == 2, "one or two tiles per CU (activations loaded two or more steps ahead)");
+  static_assert(TT == 1 || TT == 2, "one or two tiles at a time (activations loaded two or more steps ahead)");
   constexpr int SPB = 4 / TT;  // steps per unrolled body (code items in flight: P = TT * SPB = 4)
   constexpr int P = TT * SPB;
   extern __shared__ uint4 s_mem[];
@@ -630,35 +415,39 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cuk_kernel(
   const int ist = (int)((int64_t)wave * NI / W), iend = (int)((int64_t)(wave + 1) * NI / W);
   const int cnt = iend - ist;
   const int S = (NI + W - 1) / W;  // steps: the most items any wave has per tile
+  const int T = (nrows + kCuRows - 1) / kCuRows;  // tiles of this workgroup
 
   const int XS = B > 4 ? 8 : 4;
   uint4* s_xs = s_mem;                                                     // [2][W][2][2][4][B]
   float* s_Xs = reinterpret_cast<float*>(s_mem + 2 * W * 16 * B);          // [2][W][2][XS]
   float* s_red = s_Xs + 2 * W * 2 * XS;                                    // [TT][W][32][4]
-  float* s_y = s_red + TT * W * 128;                                       // [B][rpw]
   const int stride_buf = W * 16 * B;  // uint4 per buffer
 
-  // ---- codes: as in gemv_mfma_cu_kernel, tile t's pointers fixed
+  // ---- codes: as in gemv_mfma_cu_kernel; tile t of the current pair is
+  // workgroup tile tp + t (a tile past the last reads the last row, and its
+  // results are not kept)
   const int pc = lane & 3;
   const uint32_t* cptr[TT];
   const uint16_t* sptr[TT];
   const uint16_t* bptr[TT];
+  auto set_tiles = [&](int tp) {
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const int64_t rt = r0 + (int64_t)t * kCuRows;
-    int64_t rc = rt + (lane >> 2);
-    rc = rc < r1 ? rc : r1 - 1;
-    cptr[t] = wq + rc * KW + (pc & 1) * 4 + (pc >> 1) * 8;
-    if constexpr (EVENG) {
-      sptr[t] = scales + rc * G;
-      bptr[t] = biases + rc * G;
-    } else {
-      int64_t rn = rt + n16;
-      rn = rn < r1 ? rn : r1 - 1;
-      sptr[t] = scales + rn * G;
-      bptr[t] = biases + rn * G;
+    for (int t = 0; t < TT; ++t) {
+      const int64_t rt = r0 + (int64_t)(tp + t) * kCuRows;
+      int64_t rc = rt + (lane >> 2);
+      rc = rc < r1 ? rc : r1 - 1;
+      cptr[t] = wq + rc * KW + (pc & 1) * 4 + (pc >> 1) * 8;
+      if constexpr (EVENG) {
+        sptr[t] = scales + rc * G;
+        bptr[t] = biases + rc * G;
+      } else {
+        int64_t rn = rt + n16;
+        rn = rn < r1 ? rn : r1 - 1;
+        sptr[t] = scales + rn * G;
+        bptr[t] = biases + rn * G;
+      }
     }
-  }
+  };
   // item (step s, tile t): item index ist + s, clamped to the wave's last (loads
   // stay unconditional so the waits count exactly; a clamped item is not consumed)
   auto issue = [&](CuItem<EVENG>& it, int s, int t) {
@@ -757,101 +546,85 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cuk_kernel(
     }
   };
 
-  // ---- prologue: the first SPB steps' activations, the first P code items
-  uint4 xr[SPB][4];
-#pragma unroll
-  for (int u = 0; u < SPB; ++u) x_load(u, xr[u]);
-  CuItem<EVENG> ring[P];
-#pragma unroll
-  for (int u = 0; u < SPB; ++u)
-#pragma unroll
-    for (int t = 0; t < TT; ++t) issue(ring[u * TT + t], u, t);
-  x_store(xr[0], 0);
   if (AM && tid < 8) s_best[tid] = 0;
   if (AM && tid == 0) s_bad = 0;
-  __syncthreads();
+  for (int tp = 0; tp < T; tp += TT) {
+    set_tiles(tp);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) tot[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // ---- steps, SPB per unrolled body: step s consumes buffer s % 2; the
-  // activations of step s + 1 (loaded SPB - 1 steps earlier) go into the other
-  // buffer before the step's barrier, and those of step s + SPB are loaded
-  for (int s0 = 0; s0 < S; s0 += SPB) {
+    // ---- prologue: the first SPB steps' activations, the first P code items
+    // (the barrier also ends the previous pair's reads of the partial sums)
+    uint4 xr[SPB][4];
 #pragma unroll
-    for (int u = 0; u < SPB; ++u) {
-      const int s = s0 + u;
-      if (s < S) {
-        const int buf = s & 1;
-        if (s < cnt) {
+    for (int u = 0; u < SPB; ++u) x_load(u, xr[u]);
+    CuItem<EVENG> ring[P];
 #pragma unroll
-          for (int t = 0; t < TT; ++t) {
-            consume(ring[u * TT + t], tot[t], s, buf);
-            issue(ring[u * TT + t], s + SPB, t);
+    for (int u = 0; u < SPB; ++u)
+#pragma unroll
+      for (int t = 0; t < TT; ++t) issue(ring[u * TT + t], u, t);
+    x_store(xr[0], 0);
+    __syncthreads();
+
+    // ---- steps, SPB per unrolled body: step s consumes buffer s % 2; the
+    // activations of step s + 1 (loaded SPB - 1 steps earlier) go into the
+    // other buffer before the step's barrier, and those of step s + SPB are
+    // loaded
+    for (int s0 = 0; s0 < S; s0 += SPB) {
+#pragma unroll
+      for (int u = 0; u < SPB; ++u) {
+        const int s = s0 + u;
+        if (s < S) {
+          const int buf = s & 1;
+          if (s < cnt) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+              consume(ring[u * TT + t], tot[t], s, buf);
+              issue(ring[u * TT + t], s + SPB, t);
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) issue(ring[u * TT + t], s + SPB, t);
           }
-        } else {
-#pragma unroll
-          for (int t = 0; t < TT; ++t) issue(ring[u * TT + t], s + SPB, t);
+          if (s + 1 < S) x_store(xr[(u + 1) % SPB], buf ^ 1);
+          x_load(s + SPB, xr[u]);
+          lds_barrier();
         }
-        if (s + 1 < S) x_store(xr[(u + 1) % SPB], buf ^ 1);
-        x_load(s + SPB, xr[u]);
-        lds_barrier();
+      }
+    }
+
+    // ---- the pair's wave sums, in ascending wave order, stored (rows fastest
+    // across threads) and with AM folded into the workgroup's record
+    if (lane < 32) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t) *reinterpret_cast<f32x4_t*>(s_red + ((t * W + wave) * 32 + lane) * 4) = tot[t];
+    }
+    __syncthreads();
+    for (int o = tid; o < TT * kCuRows * B; o += (int)blockDim.x) {
+      const int tb = o / (kCuRows * B), rem = o - tb * (kCuRows * B);
+      const int bq = rem / kCuRows, n = rem - bq * kCuRows;
+      const int row = (tp + tb) * kCuRows + n;
+      if (row < nrows) {
+        const float* pr = s_red + (tb * W * 32 + n + 16 * (bq >> 2)) * 4 + (bq & 3);
+        float acc = pr[0];
+        for (int w = 1; w < W; ++w) acc += pr[w * 128];
+        if (!AM || y != nullptr) y[(int64_t)bq * N + r0 + row] = acc;
+        if constexpr (AM) {
+          const uint32_t uv = __float_as_uint(acc);
+          if (!finite_bits(uv))
+            __hip_atomic_fetch_or(&s_bad, 1u << bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          else
+            __hip_atomic_fetch_max(&s_best[bq], cand(uv, (uint32_t)(r0 + row)), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
       }
     }
   }
-
-  // ---- the wave sums, in ascending wave order, then the results
-  if (lane < 32) {
-#pragma unroll
-    for (int t = 0; t < TT; ++t) *reinterpret_cast<f32x4_t*>(s_red + ((t * W + wave) * 32 + lane) * 4) = tot[t];
-  }
-  __syncthreads();
-  for (int o = tid; o < TT * kCuRows * B; o += (int)blockDim.x) {
-    const int tb = o / (kCuRows * B), rem = o - tb * (kCuRows * B);
-    const int n = rem / B, bq = rem - n * B;
-    const int row = tb * kCuRows + n;
-    if (row < nrows) {
-      const float* pr = s_red + (tb * W * 32 + n + 16 * (bq >> 2)) * 4 + (bq & 3);
-      float acc = pr[0];
-      for (int w = 1; w < W; ++w) acc += pr[w * 128];
-      s_y[bq * (int)rpw + row] = acc;
-    }
-  }
-  __syncthreads();
-  const int nout = B * nrows;
-  if (!AM || y != nullptr) {
-    for (int o = tid; o < nout; o += (int)blockDim.x) {
-      const int bq = o / nrows, row = o - bq * nrows;
-      y[(int64_t)bq * N + r0 + row] = s_y[bq * (int)rpw + row];
-    }
-  }
   if constexpr (AM) {
-    for (int o = tid; o < nout; o += (int)blockDim.x) {
-      const int bq = o / nrows, row = o - bq * nrows;
-      const uint32_t u = __float_as_uint(s_y[bq * (int)rpw + row]);
-      if (!finite_bits(u))
-        __hip_atomic_fetch_or(&s_bad, 1u << bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      else
-        __hip_atomic_fetch_max(&s_best[bq], cand(u, (uint32_t)(r0 + row)), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
     __syncthreads();
     if (tid < B)
       rec[(int64_t)tid * gridDim.x + blockIdx.x] = make_record(s_best[tid], ((s_bad >> tid) & 1u) != 0, (uint32_t)r0);
   }
-}
-
-template <bool AM>
-hipError_t launch_stage(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                        const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
-                        hipStream_t stream) {
-  const int64_t blocks = (N + 31) / 32;
-  const bool vec = ((K >> 6) % 8) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
-                                             reinterpret_cast<uintptr_t>(biases)) & 15u) == 0;
-  if (vec)
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, true, AM>), dim3((unsigned)blocks), dim3(256), 0, stream, wq,
-                       scales, biases, x, y, B, N, K, rec);
-  else
-    hipLaunchKernelGGL((gemv_mfma_kernel<4, false, AM>), dim3((unsigned)blocks), dim3(256), 0, stream, wq,
-                       scales, biases, x, y, B, N, K, rec);
-  return hipGetLastError();
 }
 
 constexpr int kCUs = 256;                  // compute units of the MI355X
@@ -864,33 +637,40 @@ int cu_waves(int64_t K) {
   return NI < kCuMaxWaves ? (int)NI : kCuMaxWaves;
 }
 int cu_tiles(int64_t N) { return (int)((cu_rows(N) + kCuRows - 1) / kCuRows); }
-size_t cu_lds_fixed(int Bc, int64_t N, int64_t K) {
+// LDS of the whole-x kernel: the activations and group sums of Bc batch rows,
+// then the partial sums of a batch of tiles
+size_t cu_lds_fixed(int Bc, int64_t K) {
   const int64_t G = K >> 6;
-  return (size_t)(G * 8 * Bc) * 16 + (size_t)G * (Bc > 4 ? 8 : 4) * 4 + (size_t)Bc * cu_rows(N) * 4;
+  return (size_t)(G * 8 * Bc) * 16 + (size_t)G * (Bc > 4 ? 8 : 4) * 4;
 }
 size_t cu_tile_bytes(int64_t K) { return (size_t)cu_waves(K) * 32 * 4 * 4; }
-// tiles per batch: as many as the LDS left holds partial sums for (0: none fits)
+// The whole-x kernel runs where the activations of the largest batch (8 rows)
+// and one tile's partial sums fit in its LDS (K up to about 9,000), so one
+// choice serves any B; the step-staged kernel otherwise.  A function of K
+// alone; both kernels give the same bits in any case.
+bool use_cu(int64_t K) { return cu_lds_fixed(kMaxBatch, K) + cu_tile_bytes(K) <= kCuMaxLds; }
+// whether the whole-x kernel holds its results in LDS until the end: where
+// they fit beside one tile's partial sums
+size_t cu_held_bytes(int Bc, int64_t N) { return (size_t)Bc * cu_rows(N) * 4; }
+bool cu_hold(int Bc, int64_t N, int64_t K) {
+  return cu_lds_fixed(Bc, K) + cu_held_bytes(Bc, N) + cu_tile_bytes(K) <= kCuMaxLds;
+}
+// tiles per reduction batch of the whole-x kernel: as many as the LDS left
+// holds partial sums for (at least one where use_cu holds)
 int cu_batch_tiles(int Bc, int64_t N, int64_t K) {
-  const size_t fixed = cu_lds_fixed(Bc, N, K);
-  if (fixed + cu_tile_bytes(K) > kCuMaxLds) return 0;
+  const size_t fixed = cu_lds_fixed(Bc, K) + (cu_hold(Bc, N, K) ? cu_held_bytes(Bc, N) : 0);
   const int64_t t = (int64_t)((kCuMaxLds - fixed) / cu_tile_bytes(K));
   return t < cu_tiles(N) ? (int)t : cu_tiles(N);
 }
 size_t cu_lds_bytes(int Bc, int64_t N, int64_t K) {
-  return cu_lds_fixed(Bc, N, K) + (size_t)cu_batch_tiles(Bc, N, K) * cu_tile_bytes(K);
+  return cu_lds_fixed(Bc, K) + (cu_hold(Bc, N, K) ? cu_held_bytes(Bc, N) : 0) +
+         (size_t)cu_batch_tiles(Bc, N, K) * cu_tile_bytes(K);
 }
-// The per-CU kernel runs where the activations of the largest batch (8 rows)
-// fit in its LDS, so one pass serves any B (K above about 9,000, as in the
-// down projection, does not).  A function of (N, K) only, so a batch row's
-// arithmetic does not depend on B.
-bool use_cu(int64_t N, int64_t K) { return cu_batch_tiles(kMaxBatch, N, K) > 0; }
-// Otherwise, where a CU holds one or two tiles (N <= 8,192), the per-CU kernel
-// that stages the activations step by step; else the staged kernel above.
-bool use_cuk(int64_t N, int64_t K) { return !use_cu(N, K) && cu_tiles(N) <= 2 && (K >> 6) >= 2; }
+// the step-staged kernel takes a CU's tiles two at a time (one where it has one)
+int cuk_pair(int64_t N) { return cu_tiles(N) == 1 ? 1 : 2; }
 size_t cuk_lds_bytes(int B, int64_t N, int64_t K) {
   const int W = cu_waves(K), XS = B > 4 ? 8 : 4;
-  return (size_t)2 * W * 16 * B * 16 + (size_t)2 * W * 2 * XS * 4 + (size_t)cu_tiles(N) * W * 128 * 4 +
-         (size_t)B * cu_rows(N) * 4;
+  return (size_t)2 * W * 16 * B * 16 + (size_t)2 * W * 2 * XS * 4 + (size_t)cuk_pair(N) * W * 128 * 4;
 }
 
 template <bool EVENG, bool AM>
@@ -900,7 +680,7 @@ hipError_t launch_cuk(const uint32_t* wq, const uint16_t* scales, const uint16_t
   const int64_t rpw = cu_rows(N);
   const int64_t blocks = (N + rpw - 1) / rpw;
   const size_t lds = cuk_lds_bytes(B, N, K);
-  if (cu_tiles(N) == 1) {
+  if (cuk_pair(N) == 1) {
     hipLaunchKernelGGL((gemv_mfma_cuk_kernel<EVENG, AM, 1>), dim3((unsigned)blocks), dim3(64 * cu_waves(K)), lds,
                        stream, wq, scales, biases, x, y, B, N, K, rpw, rec);
   } else {
@@ -924,43 +704,44 @@ hipError_t launch_cu_pass(const uint32_t* wq, const uint16_t* scales, const uint
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((gemv_mfma_cu_kernel<EVENG, AM, 4>), dim3((unsigned)blocks), dim3(64 * cu_waves(K)), lds,
-                     stream, wq, scales, biases, x, y, B, N, K, rpw, cu_batch_tiles(B, N, K), rec);
+                     stream, wq, scales, biases, x, y, B, N, K, rpw, cu_batch_tiles(B, N, K), cu_hold(B, N, K),
+                     rec);
   return hipGetLastError();
 }
 
+// step: the step-staged kernel whatever K is (it needs two groups or more;
+// below that the whole-x kernel runs, with the same bits)
 template <bool AM>
 hipError_t launch(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                  const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                  const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K, bool step,
                   hipStream_t stream) {
   const bool eveng = ((K >> 6) % 2) == 0 && ((reinterpret_cast<uintptr_t>(scales) |
                                                reinterpret_cast<uintptr_t>(biases)) & 3u) == 0;
-  if (use_cu(N, K))
+  if (use_cu(K) && !(step && (K >> 6) >= 2))
     return eveng ? launch_cu_pass<true, AM>(wq, scales, biases, x, y, rec, B, N, K, stream)
                  : launch_cu_pass<false, AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
-  if (use_cuk(N, K))
-    return eveng ? launch_cuk<true, AM>(wq, scales, biases, x, y, rec, B, N, K, stream)
-                 : launch_cuk<false, AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
-  return launch_stage<AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
+  return eveng ? launch_cuk<true, AM>(wq, scales, biases, x, y, rec, B, N, K, stream)
+               : launch_cuk<false, AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                            const uint16_t* x, float* y, int B, int64_t N, int64_t K,
+                            const uint16_t* x, float* y, int B, int64_t N, int64_t K, bool step,
                             hipStream_t stream) {
-  return launch<false>(wq, scales, biases, x, y, nullptr, B, N, K, stream);
+  return launch<false>(wq, scales, biases, x, y, nullptr, B, N, K, step, stream);
 }
 
 int64_t gemv_mfma_argmax_records(int B, int64_t N, int64_t K) {
   (void)B;
-  if (!use_cu(N, K) && !use_cuk(N, K)) return (N + 31) / 32;
+  (void)K;
   return (N + cu_rows(N) - 1) / cu_rows(N);
 }
 
 hipError_t launch_gemv_mfma_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                                    const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                                    hipStream_t stream) {
-  return launch<true>(wq, scales, biases, x, y, rec, B, N, K, stream);
+  return launch<true>(wq, scales, biases, x, y, rec, B, N, K, false, stream);
 }
 
 }  // namespace w4g

@@ -15,8 +15,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                        const uint16_t* x, float* y, int B, int64_t N, int64_t K, bool force_regs,
                        hipStream_t stream);
+// step: run the step-staged per-CU kernel whatever K is (same bits as the
+// whole-x kernel; for checking that)
 hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                            const uint16_t* x, float* y, int B, int64_t N, int64_t K,
+                            const uint16_t* x, float* y, int B, int64_t N, int64_t K, bool step,
                             hipStream_t stream);
 // y: fp32 [M][N], or bf16 [M][N] (nearest-even from the fp32 result) when y_bf16
 hipError_t launch_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
