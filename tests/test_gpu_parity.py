@@ -61,6 +61,52 @@ def test_gemv_batch_invariance_and_determinism(family, K):
         assert np.array_equal(yb.view(np.uint32), y8[:Bn].view(np.uint32)), f"B={Bn} differs"
 
 
+_SLICE_CASES = {}
+
+
+def _slice_case(N, K, rows):
+    key = (N, K, rows)
+    if key not in _SLICE_CASES:
+        _SLICE_CASES.clear()
+        wq, sc, bi, x = _case(N, K, rows, 61)
+        _SLICE_CASES[key] = (wq, sc, bi, x, (up_u32(wq), up_bf16(sc), up_bf16(bi)))
+    return _SLICE_CASES[key]
+
+
+@pytest.mark.parametrize("family", ["valu", "mfma"])
+@pytest.mark.parametrize("B", [1, 3, 8])
+@pytest.mark.parametrize("N,K,lo,hi", [(248320, 5120, 100003, 105123),   # vocabulary head: layouts differ
+                                       (34816, 5120, 17408, 34816),      # gate-up: the up half alone
+                                       (5120, 17408, 1000, 1777),        # down: one tile per CU alone
+                                       (40000, 8192, 777, 30777)])       # results not held in LDS
+def test_gemv_row_slice_invariance(B, family, N, K, lo, hi):
+    """A row's bits do not depend on N or on where the row sits: the rows
+    [lo, hi) of a product equal, bit for bit, a product over those rows alone
+    (a different grid, layout and tile position; the stacked gate-up's halves
+    are the member matrices).  Within a family the K reduction is a function
+    of K alone."""
+    wq, sc, bi, x, W = _slice_case(N, K, 8)
+    k = FAMILIES[family]
+    X = up_bf16(x[:B])
+    y = down(w4g.qmm_gemv(*W, X, kernel=k))
+    ys = down(w4g.qmm_gemv(up_u32(wq[lo:hi]), up_bf16(sc[lo:hi]), up_bf16(bi[lo:hi]), X, kernel=k))
+    assert np.array_equal(ys.view(np.uint32), y[:, lo:hi].view(np.uint32))
+    rows = np.array([lo, (lo + hi) // 2, hi - 1])
+    assert_close(y[:, rows], oracle.qmm_rows(wq, sc, bi, x[:B], rows), f"gemv[{family}] N={N} K={K} B={B}")
+
+
+@pytest.mark.parametrize("M,N,K,lo,hi", [(200, 5120, 5120, 1000, 3000), (64, 34816, 5120, 17408, 34816),
+                                         (33, 5120, 17408, 130, 4000)])
+def test_gemm_column_slice_invariance(M, N, K, lo, hi):
+    """The prompt product's columns [lo, hi) equal, bit for bit, a product over
+    those weight rows alone (other tiles, grid and kernel choice)."""
+    wq, sc, bi, x = _case(N, K, M, 5)
+    X = up_bf16(x)
+    y = down(w4g.qmm_gemm(up_u32(wq), up_bf16(sc), up_bf16(bi), X))
+    ys = down(w4g.qmm_gemm(up_u32(wq[lo:hi]), up_bf16(sc[lo:hi]), up_bf16(bi[lo:hi]), X))
+    assert np.array_equal(ys.view(np.uint32), y[:, lo:hi].view(np.uint32))
+
+
 @pytest.mark.parametrize("family", ["valu", "mfma"])
 def test_gemv_row_permutation_bitwise(family):
     wq, sc, bi, x = _case(96, 2048, 2, 4)
