@@ -88,10 +88,6 @@ __device__ __forceinline__ bf16x8_t expand_codes(uint32_t w, uint32_t m, uint32_
   return __builtin_bit_cast(bf16x8_t, p);
 }
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int t) {
-  return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
-}
-
 // Pre-pass, one thread per (row m, group g):
 //   xp[m][g*64 + ...] = the group's 64 activations permuted block by block;
 //   xs[m][p*G16 + g]  = part p of the group sum (zero for G <= g < G16).
