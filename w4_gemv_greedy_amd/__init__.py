@@ -24,17 +24,25 @@ __all__ = ["qmm_gemv", "qmm_gemm", "qmm_gemv_argmax", "vocab_argmax", "vocab_arg
            "workspace_bytes", "SENTINEL", "W4GError"]
 
 
+_TORCH = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH
+    if _TORCH is None:
+        import torch
+        _TORCH = torch
+    return _TORCH
 
 
 def _stream(t):
-    torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    """The current stream of t's GPU (as torch.cuda.current_stream(t.device))."""
+    return ctypes.c_void_p(_torch()._C._cuda_getCurrentRawStream(t.get_device()))
 
 
 def _need(t, name, dtypes, ndim, device):
+    """device: a GPU index (or torch.device) t must be on, or None for any GPU.
+    Every check runs on every call; they read only cheap tensor attributes."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -42,7 +50,8 @@ def _need(t, name, dtypes, ndim, device):
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
     if t.dim() != ndim:
         raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
-    if not t.is_cuda or (device is not None and t.device != device):
+    d = t.get_device()
+    if d < 0 or (device is not None and d != (device if isinstance(device, int) else device.index)):
         raise ValueError(f"{name} must be on the same GPU as the weights")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -51,7 +60,7 @@ def _need(t, name, dtypes, ndim, device):
 def _check_qmm(wq, scales, biases, x, bits=4):
     torch = _torch()
     _need(wq, "wq", (torch.int32, torch.uint32), 2, None)
-    dev = wq.device
+    dev = wq.get_device()
     _need(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), 2, dev)
     _need(biases, "biases", (torch.bfloat16, torch.int16, torch.uint16), 2, dev)
     _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2, dev)
@@ -91,10 +100,11 @@ def _call_qmm(fn, op, wq, scales, biases, x, y, workspace, extra=(), y_dtypes=No
     y_dtypes = y_dtypes or (torch.float32,)
     if y is None:
         y = torch.empty((rows, N), dtype=y_dtypes[0], device=wq.device)
-    _need(y, "y", y_dtypes, 2, wq.device)
-    if tuple(y.shape) != (rows, N):
+    _need(y, "y", y_dtypes, 2, wq.get_device())
+    if y.shape[0] != rows or y.shape[1] != N:
         raise ValueError(f"y must be [{rows}][{N}]")
-    ws, nbytes = _workspace(op, rows, N, K, wq.device, workspace)
+    # the decode products take no workspace (the library checks B itself)
+    ws, nbytes = (None, 0) if op == OP_GEMV else _workspace(op, rows, N, K, wq.device, workspace)
     lib = _lib.load()
     status = getattr(lib, fn)(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
                               y.data_ptr(), rows, N, K, ws.data_ptr() if ws is not None else None,
