@@ -61,6 +61,29 @@ def test_gemv_batch_invariance_and_determinism(family, K):
         assert np.array_equal(yb.view(np.uint32), y8[:Bn].view(np.uint32)), f"B={Bn} differs"
 
 
+@pytest.mark.parametrize("kernel", ["valu", "mfma", "mfma_step", "gemm"])
+@pytest.mark.parametrize("B", [1, 5])
+def test_power_of_two_scaling_bitwise(kernel, B):
+    """Every step is linear in x and every rounding commutes with a power-of-two
+    scale: x * 4 gives exactly 4 y in both decode families, the step-staged
+    variant and the prompt product (a dropped term, a wrong scale factor or a
+    non-linear shortcut shows here).  Negation is not checked: the hardware's
+    fused bf16 dot products (v_dot2 and the matrix cores) measured not
+    sign-symmetric bit for bit on some outputs."""
+    import torch
+    wq, sc, bi, x = _case(700, 3072, B, 41 + B)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    X = up_bf16(x)
+    if kernel == "gemm":
+        run = lambda xx: down(w4g.qmm_gemm(*W, xx))  # noqa: E731
+    else:
+        k = {"valu": w4g.GEMV_VALU, "mfma": w4g.GEMV_MFMA, "mfma_step": w4g.GEMV_MFMA_STEP}[kernel]
+        run = lambda xx: down(w4g.qmm_gemv(*W, xx, kernel=k))  # noqa: E731
+    y = run(X)
+    y4 = run((X.float() * 4).to(torch.bfloat16))
+    assert np.array_equal(y4.view(np.uint32), (y * np.float32(4)).view(np.uint32))
+
+
 _SLICE_CASES = {}
 
 
