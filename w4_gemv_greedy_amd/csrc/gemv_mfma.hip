@@ -74,8 +74,10 @@ __device__ __forceinline__ bf16x8_t expand128(uint32_t w, uint32_t m, uint32_t g
 // every quarter two words of each group (quarter 0: words 0,1; 1: words 4,5;
 // 2: words 2,3; 3: words 6,7), the first for the group's first instruction and
 // the second for its second.  The activations are staged in that order.  The
-// scale and bias pairs come the same way (each lane loads those of the row it
-// loads codes of; four adjacent lanes share the address).
+// scale and bias pairs of a row come the same way: in the step-staged kernel
+// (and with an odd group count) each lane loads those of the row it loads
+// codes of, per item; in the whole-x kernel with an even group count once per
+// four items, lane 4n + p loading row n's pairs of the p-th of them.
 //
 // Arithmetic per (row n, batch row b): for each group g the matrix core forms
 // P_g = sum_{k in g} x*(128 + q) from zero over two instructions; the wave
@@ -160,16 +162,13 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   const int pc = lane & 3;
   int it_t = 0, it_i = ist;
   const uint32_t* cptr;
-  const uint16_t *sptr, *bptr;
+  const uint16_t *sptr = scales, *bptr = biases;
   auto set_tile = [&]() {
     const int64_t rt = r0 + (int64_t)it_t * kCuRows;
     int64_t rc = rt + (lane >> 2);
     rc = rc < r1 ? rc : r1 - 1;
     cptr = wq + rc * KW + (pc & 1) * 4 + (pc >> 1) * 8;
-    if constexpr (EVENG) {
-      sptr = scales + rc * G;
-      bptr = biases + rc * G;
-    } else {
+    if constexpr (!EVENG) {  // (EVENG: the pair loads below)
       int64_t rn = rt + n16;
       rn = rn < r1 ? rn : r1 - 1;
       sptr = scales + rn * G;
@@ -182,10 +181,7 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
     int off = g0 * 8;
     if (!EVENG && g0 + 1 >= G && pc >= 2) off -= 8;  // an odd last group: parts 2, 3 reread it (unused)
     it.c = *reinterpret_cast<const uint4*>(cptr + off);
-    if constexpr (EVENG) {
-      it.s[0] = *reinterpret_cast<const uint32_t*>(sptr + g0);
-      it.b[0] = *reinterpret_cast<const uint32_t*>(bptr + g0);
-    } else {
+    if constexpr (!EVENG) {
       const int g1 = g0 + 1 < G ? g0 + 1 : g0;
       it.s[0] = sptr[g0];
       it.s[1] = sptr[g1];
@@ -197,6 +193,29 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
       ++it_t;
       set_tile();
     }
+  };
+  // EVENG: the scale and bias pairs come once per P = 4 items: for the k-th
+  // such load, lane 4n + p reads row n's pairs of item 4k + p of the wave's
+  // sequence (one load per table per four items instead of one per item:
+  // B = 8 gate-up 31 against 35 us, lm_head 172 against 188), each lane
+  // following its own item through the tiles
+  static_assert(!EVENG || P == 4, "one pair load per four items");
+  int qt = 0, qi = ist;  // this lane's item of the next pair load: tile, item within the tile
+  auto q_adv = [&](int k) {
+    qi += k;
+    while (qi >= iend) {
+      qi -= cnt;
+      ++qt;
+    }
+  };
+  if constexpr (EVENG) q_adv(pc);
+  uint32_t sqa = 0, bqa = 0, sqb = 0, bqb = 0;  // pairs of the even / odd groups of four items
+  auto issue_pairs = [&](uint32_t& sw, uint32_t& bw) {
+    int64_t row = r0 + (int64_t)qt * kCuRows + (lane >> 2);
+    row = row < r1 ? row : r1 - 1;  // past the last tile: a valid row, never used
+    sw = *reinterpret_cast<const uint32_t*>(scales + row * G + 2 * qi);
+    bw = *reinterpret_cast<const uint32_t*>(biases + row * G + 2 * qi);
+    q_adv(P);
   };
 
   // ---- stage x: segment (b, g) = 64 activations -> 8 blocks in the quarter
@@ -230,6 +249,7 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   CuItem<EVENG> ring[P];
 #pragma unroll
   for (int sl = 0; sl < P; ++sl) issue(ring[sl]);
+  if constexpr (EVENG) issue_pairs(sqa, bqa);
 
   if (has_pre) put_seg(tid, pre);
   for (int seg = tid + (int)blockDim.x; seg < nseg; seg += (int)blockDim.x) {
@@ -304,7 +324,7 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
     lds_barrier();
   };
   const int src_lane = ((n16 << 2) | q) << 2;  // byte address of lane 4 n + q
-  auto consume = [&](const CuItem<EVENG>& it) {
+  auto consume = [&](const CuItem<EVENG>& it, int sl, uint32_t sq, uint32_t bq) {
     // lane (n, q) takes the 16 bytes lane 4 n + q loaded
     const uint32_t c0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.x);
     const uint32_t c1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.y);
@@ -315,9 +335,11 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
     const auto sy = __builtin_amdgcn_permlane32_swap(c1, c3, false, false);
     const int g0 = 2 * ci;
     if constexpr (EVENG) {
-      // the scale and bias pairs of row n, from the same lane as the codes
-      const uint32_t sp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.s[0]);
-      const uint32_t bp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.b[0]);
+      // the scale and bias pairs of row n for this item (slot sl of four):
+      // lane 4n + sl loaded them
+      const int src_q = ((n16 << 2) | sl) << 2;
+      const uint32_t sp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_q, (int)sq);
+      const uint32_t bp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_q, (int)bq);
       group(g0, sx[0], sy[0], sp & 0xFFFFu, bp & 0xFFFFu);
       group(g0 + 1, sx[1], sy[1], sp >> 16, bp >> 16);
     } else {
@@ -337,23 +359,44 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
       }
     }
   };
-  // steady state (every issued item exists), then the last items
+  // steady state (every issued item exists), two groups of P items per
+  // iteration so the pairs of the even and odd groups keep registers of their
+  // own (with EVENG the next group's pairs are loaded beside the first of its
+  // codes), then the last items (fewer than 3P)
   int j = 0;
-  for (; j + 2 * P - 1 < n_items; j += P) {
+  for (; j + 3 * P - 1 < n_items; j += 2 * P) {
 #pragma unroll
     for (int sl = 0; sl < P; ++sl) {
-      consume(ring[sl]);
+      consume(ring[sl], sl, sqa, bqa);
       issue(ring[sl]);
+      if (EVENG && sl == 0) issue_pairs(sqb, bqb);
+    }
+#pragma unroll
+    for (int sl = 0; sl < P; ++sl) {
+      consume(ring[sl], sl, sqb, bqb);
+      issue(ring[sl]);
+      if (EVENG && sl == 0) issue_pairs(sqa, bqa);
     }
   }
 #pragma unroll
   for (int sl = 0; sl < P; ++sl) {
-    if (j + sl < n_items) consume(ring[sl]);
-    if (j + sl + P < n_items) issue(ring[sl]);
+    if (j + sl < n_items) consume(ring[sl], sl, sqa, bqa);
+    if (j + sl + P < n_items) {
+      issue(ring[sl]);
+      if (EVENG && sl == 0) issue_pairs(sqb, bqb);
+    }
+  }
+#pragma unroll
+  for (int sl = 0; sl < P; ++sl) {
+    if (j + P + sl < n_items) consume(ring[sl], sl, sqb, bqb);
+    if (j + 2 * P + sl < n_items) {
+      issue(ring[sl]);
+      if (EVENG && sl == 0) issue_pairs(sqa, bqa);
+    }
   }
 #pragma unroll
   for (int sl = 0; sl < P; ++sl)
-    if (j + P + sl < n_items) consume(ring[sl]);
+    if (j + 2 * P + sl < n_items) consume(ring[sl], sl, sqa, bqa);
 
   // ---- held results out (the last reduction ended with a barrier), then the record
   if (hold) {
