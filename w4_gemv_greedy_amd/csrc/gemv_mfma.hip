@@ -74,10 +74,9 @@ __device__ __forceinline__ bf16x8_t expand128(uint32_t w, uint32_t m, uint32_t g
 // every quarter two words of each group (quarter 0: words 0,1; 1: words 4,5;
 // 2: words 2,3; 3: words 6,7), the first for the group's first instruction and
 // the second for its second.  The activations are staged in that order.  The
-// scale and bias pairs of a row come the same way: in the step-staged kernel
-// (and with an odd group count) each lane loads those of the row it loads
-// codes of, per item; in the whole-x kernel with an even group count once per
-// four items, lane 4n + p loading row n's pairs of the p-th of them.
+// scale and bias pairs of a row come the same way: with an even group count
+// once per four items, lane 4n + p loading row n's pairs of the p-th of them;
+// with an odd one each lane loads those of the row it loads codes of, per item.
 //
 // Arithmetic per (row n, batch row b): for each group g the matrix core forms
 // P_g = sum_{k in g} x*(128 + q) from zero over two instructions; the wave
@@ -499,15 +498,27 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cuk_kernel(
     int off = g0 * 8;
     if (!EVENG && g0 + 1 >= G && pc >= 2) off -= 8;
     it.c = *reinterpret_cast<const uint4*>(cptr[t] + off);
-    if constexpr (EVENG) {
-      it.s[0] = *reinterpret_cast<const uint32_t*>(sptr[t] + g0);
-      it.b[0] = *reinterpret_cast<const uint32_t*>(bptr[t] + g0);
-    } else {
+    if constexpr (!EVENG) {
       const int g1 = g0 + 1 < G ? g0 + 1 : g0;
       it.s[0] = sptr[t][g0];
       it.s[1] = sptr[t][g1];
       it.b[0] = bptr[t][g0];
       it.b[1] = bptr[t][g1];
+    }
+  };
+  // EVENG: a tile's scale and bias pairs come once per four steps (a group),
+  // a group ahead: lane 4n + p reads row n's pairs of step 4k + p (clamped to
+  // the wave's last item, as the codes are); even and odd groups keep
+  // registers of their own
+  uint32_t psq[2][TT], pbq[2][TT];
+  auto issue_pairs = [&](int k, int set) {
+    int st = 4 * k + pc;
+    st = st < cnt ? st : cnt - 1;
+    const int g0 = 2 * (ist + st);
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      psq[set][t] = *reinterpret_cast<const uint32_t*>(sptr[t] + g0);
+      pbq[set][t] = *reinterpret_cast<const uint32_t*>(bptr[t] + g0);
     }
   };
 
@@ -570,7 +581,7 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cuk_kernel(
     acc[3] = __builtin_fmaf(cb, xs.w, __builtin_fmaf(sc, pg[3], acc[3]));
     (void)g;
   };
-  auto consume = [&](const CuItem<EVENG>& it, f32x4_t& acc, int s, int buf) {
+  auto consume = [&](const CuItem<EVENG>& it, f32x4_t& acc, int s, int buf, uint32_t sq, uint32_t bq) {
     const uint32_t c0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.x);
     const uint32_t c1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.y);
     const uint32_t c2 = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.c.z);
@@ -579,8 +590,10 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cuk_kernel(
     const auto sy = __builtin_amdgcn_permlane32_swap(c1, c3, false, false);
     const int g0 = 2 * (ist + s);
     if constexpr (EVENG) {
-      const uint32_t sp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.s[0]);
-      const uint32_t bp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane, (int)it.b[0]);
+      // this step's pairs of row n: lane 4n + (s % 4) loaded them
+      const int src_q = ((n16 << 2) | (s & 3)) << 2;
+      const uint32_t sp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_q, (int)sq);
+      const uint32_t bp = (uint32_t)__builtin_amdgcn_ds_bpermute(src_q, (int)bq);
       group(acc, buf, 0, g0, sx[0], sy[0], sp & 0xFFFFu, bp & 0xFFFFu);
       group(acc, buf, 1, g0 + 1, sx[1], sy[1], sp >> 16, bp >> 16);
     } else {
@@ -606,31 +619,36 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cuk_kernel(
     for (int u = 0; u < SPB; ++u)
 #pragma unroll
       for (int t = 0; t < TT; ++t) issue(ring[u * TT + t], u, t);
+    if constexpr (EVENG) issue_pairs(0, 0);
     x_store(xr[0], 0);
     __syncthreads();
 
-    // ---- steps, SPB per unrolled body: step s consumes buffer s % 2; the
-    // activations of step s + 1 (loaded SPB - 1 steps earlier) go into the
-    // other buffer before the step's barrier, and those of step s + SPB are
-    // loaded
-    for (int s0 = 0; s0 < S; s0 += SPB) {
+    // ---- steps, eight per unrolled body (two groups of four, so every ring
+    // slot, activation register and pair set is a constant): step s consumes
+    // buffer s % 2; the activations of step s + 1 (loaded SPB - 1 steps
+    // earlier) go into the other buffer before the step's barrier, and those
+    // of step s + SPB are loaded; with EVENG the first step of a group loads
+    // the next group's pairs
+    for (int s0 = 0; s0 < S; s0 += 8) {
 #pragma unroll
-      for (int u = 0; u < SPB; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int s = s0 + u;
+        const int ur = u % SPB, set = (u >> 2) & 1;
         if (s < S) {
           const int buf = s & 1;
+          if (EVENG && (u & 3) == 0) issue_pairs((s >> 2) + 1, set ^ 1);
           if (s < cnt) {
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
-              consume(ring[u * TT + t], tot[t], s, buf);
-              issue(ring[u * TT + t], s + SPB, t);
+              consume(ring[ur * TT + t], tot[t], s, buf, psq[set][t], pbq[set][t]);
+              issue(ring[ur * TT + t], s + SPB, t);
             }
           } else {
 #pragma unroll
-            for (int t = 0; t < TT; ++t) issue(ring[u * TT + t], s + SPB, t);
+            for (int t = 0; t < TT; ++t) issue(ring[ur * TT + t], s + SPB, t);
           }
-          if (s + 1 < S) x_store(xr[(u + 1) % SPB], buf ^ 1);
-          x_load(s + SPB, xr[u]);
+          if (s + 1 < S) x_store(xr[(ur + 1) % SPB], buf ^ 1);
+          x_load(s + SPB, xr[ur]);
           lds_barrier();
         }
       }
