@@ -215,12 +215,14 @@ def test_workspace_sizes(lib):
     # fused head: one record per product workgroup and batch row, in the layout
     # of qmm_gemv's own choice for the shape: 32 rows per workgroup for the
     # vocabulary-wide head at B = 1, else one workgroup per CU, in both families
-    # (the matrix cores run B = 8 over the vocabulary and B >= 3 where x leaves
+    # (the matrix cores run B >= 3 over the vocabulary and B >= 3 where x leaves
     # the vector-ALU kernel's LDS: down at B = 5, not at B = 4; their per-CU
     # kernels serve any N and K, 9000 x 10240 included)
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 248320, 5120) == 7760 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 5120, 5120) == 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 4, 248320, 5120) == 4 * 256 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 3, 248320, 5120) == 3 * 256 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 3, 34816, 5120) == 3 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 2, 5120, 17408) == 2 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 248320, 5120) == 8 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 5120, 17408) == 8 * 256 * 8

@@ -769,18 +769,20 @@ hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const 
   return dispatch<true>(wq, scales, biases, x, y, rec, B, N, K, false, stream);
 }
 
-// Measured with the per-CU layouts of both families (graph-timed, B = 1..8):
-// the vector ALUs are faster at small B, the matrix cores from B = 4 where a
-// CU holds more than 40 rows (gate-up at B = 4: 31.6 against 33.2 us, at B = 8:
-// 34.0 against 50.2; lm_head at B = 4: 195 against 207, at B = 8: 192 against
-// 306), from B = 7 for the layer widths (o_proj at B = 8: 11.5 against 12.8),
-// and where x is staged in registers from B = 3 (down, K = 17408, leaves the
-// vector-ALU kernel's LDS from B = 5: 27.6 against 55.2 at B = 5, 29.1 against
-// 75 at B = 8; at B = 3 and 4 it stays in LDS, 19.8 and 23.3 against 26.8 and
-// 26.9).
+// Measured with the per-CU layouts of both families (graph-timed, B = 1..8,
+// vector ALUs against matrix cores, us): the vector ALUs are faster at small B;
+// the matrix cores from B = 4 where a CU holds more than 40 rows (gate-up at
+// B = 4: 33.5 against 30.9, at B = 8: 50.2 against 32.2; lm_head at B = 4:
+// 208 against 179), and already at B = 3 where it holds more than 256
+// (lm_head: 183 against 176; gate-up, 136 rows: 29.6 against 29.9), from B = 7
+// for the layer widths (o_proj at B = 6: 10.6 against 11.0, at B = 8: 12.8
+// against 11.5), and where x is staged in registers from B = 3 (down, K =
+// 17408, leaves the vector-ALU kernel's LDS from B = 5: 25.5 against 55.1 at
+// B = 5, 26.6 against 75 at B = 8; at B = 3 and 4 it stays in LDS, 20.0 and
+// 23.5 against 24.9 and 25.1).
 int gemv_auto_family(int B, int64_t N, int64_t K) {
   if (use_regs(B, K, false)) return B <= 2 ? 1 : 2;
-  if (B >= 7 || (B >= 4 && per_cu_rows(N) > 40)) return 2;
+  if (B >= 7 || (B >= 4 && per_cu_rows(N) > 40) || (B == 3 && per_cu_rows(N) > 256)) return 2;
   return 1;
 }
 
