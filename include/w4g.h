@@ -15,9 +15,11 @@
  *       function of the matrix width K alone, never of N, the batch, the
  *       grid or timing: TensorFold PR #1433, step-2 description (a rank's K
  *       tree is its own full matrix's; the split is keyed on the whole
- *       matrix, not on a slice).  qmm_gemv picks the family by B and shape
- *       (see there), so its bits are a function of (B, N, K); a caller that
- *       needs a row to keep its bits at every batch size names the family.
+ *       matrix, not on a slice).  qmm_gemv's own choice of family is a
+ *       function of K and of the whole matrix's row count only, never of the
+ *       batch size, so a row has the same bits at every batch size and in
+ *       every row slice that names its whole matrix: a request served beside
+ *       others gets the bits it gets alone (TensorFold PR #1437, Checklist).
  *     qmm_gemv is the decode path (1 <= B <= 8 activation rows); qmm_gemm is
  *     the prompt path (any M >= 1, matrix cores).
  *
@@ -62,7 +64,7 @@
 extern "C" {
 #endif
 
-#define W4G_ABI_VERSION 1
+#define W4G_ABI_VERSION 2
 #define W4G_SENTINEL 0xFFFFFFFFu
 #define W4G_MAX_GEMV_BATCH 8
 
@@ -105,9 +107,9 @@ extern "C" {
  * then, within 16 lanes, lane j adds lane 15 - j (DPP row_mirror), within 8
  * lanes lane 7 - j (row_half_mirror), then lane j ^ 2 and lane j ^ 1
  * (quad_perm), leaving the sum in every lane.  That is the order of the
- * vector-ALU family; qmm_gemv may pick the matrix-core family instead (see
- * qmm_gemv_ex), by B and shape only, so a given (B, N, K) always runs the
- * same kernel and its bits never change from call to call.
+ * vector-ALU family, which qmm_gemv runs for every shape: the choice is
+ * qmm_gemv_ex's W4G_GEMV_AUTO with whole = N, a function of (K, N) only, so
+ * row m of a B-row call has the bits of that row computed alone, at every B.
  */
 int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
              const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K,
@@ -138,7 +140,7 @@ int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* kernel families for qmm_gemv_ex */
-#define W4G_GEMV_AUTO 0   /* the library's choice by B and shape (what qmm_gemv uses) */
+#define W4G_GEMV_AUTO 0   /* the library's choice, by K and the whole matrix's rows only (qmm_gemv's) */
 #define W4G_GEMV_VALU 1   /* vector-ALU dot2 kernel (the order documented for qmm_gemv) */
 #define W4G_GEMV_MFMA 2   /* matrix-core kernel (order documented below) */
 #define W4G_GEMV_VALU_REGS 3  /* vector-ALU family, register-staged variant (same bits as 1) */
@@ -146,7 +148,14 @@ int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
 
 /*
  * qmm_gemv with an explicit kernel family.  Same arguments and results as
- * qmm_gemv; `kernel` is one of W4G_GEMV_*, else W4G_EDTYPE.  The vector-ALU
+ * qmm_gemv; `kernel` is one of W4G_GEMV_*, else W4G_EDTYPE.
+ * `whole`: the row count of the whole matrix that these N rows are a slice of
+ * (0 means N; else N <= whole < 2^31, W4G_ESHAPE otherwise).  W4G_GEMV_AUTO
+ * picks the family from (K, whole) alone, so a row slice of a matrix runs the
+ * family the whole matrix runs and its rows have the whole matrix's bits, as
+ * the pages' kernel keeps the K split of the whole width for a rank holding a
+ * slice (TensorFold PR #1433, step-1 description: chunks(n, whole)).  Today
+ * that choice is the vector-ALU family for every (K, whole).  The vector-ALU
  * family stages x in LDS when B * 2.125 * K bytes fit in 152 KiB and in
  * registers otherwise; W4G_GEMV_VALU_REGS forces the register variant (for
  * checking that both variants give the same bits).
@@ -166,7 +175,8 @@ int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
  */
 int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                 const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K,
-                void* workspace, size_t workspace_bytes, void* stream, int kernel);
+                void* workspace, size_t workspace_bytes, void* stream, int kernel,
+                int64_t whole);
 
 /*
  * Prompt product on the matrix cores, any M >= 1 rows.
@@ -229,7 +239,8 @@ int vocab_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int
  *   N < 2^31).
  *   logits [B][N] fp32, or NULL: when given, receives exactly the bits
  *   qmm_gemv writes for the same (B, N, K) (the same kernel family, chosen
- *   the same way).
+ *   the same way: from (K, N) alone, so a row's logit and the ids do not
+ *   depend on the batch size).
  *   ids [B] uint32: per batch row the id of the largest logit, the lowest id
  *   among equal values (-0.0 ties +0.0), or W4G_SENTINEL if any logit of the
  *   row is NaN or +-Inf; always equal to vocab_argmax over those logits.

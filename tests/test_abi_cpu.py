@@ -71,10 +71,10 @@ A = 1 << 40
 WQ, SC, BI, X, Y, WS, LOG, IDS = (A + i * (1 << 36) for i in range(8))
 
 
-def gemv(lib, wq=WQ, sc=SC, bi=BI, x=X, y=Y, B=1, N=64, K=128, ws=None, wsb=0, kernel=None):
+def gemv(lib, wq=WQ, sc=SC, bi=BI, x=X, y=Y, B=1, N=64, K=128, ws=None, wsb=0, kernel=None, whole=0):
     if kernel is None:
         return lib.qmm_gemv(wq, sc, bi, x, y, B, N, K, ws, wsb, None)
-    return lib.qmm_gemv_ex(wq, sc, bi, x, y, B, N, K, ws, wsb, None, kernel)
+    return lib.qmm_gemv_ex(wq, sc, bi, x, y, B, N, K, ws, wsb, None, kernel, whole)
 
 
 def test_gemv_rejects(lib):
@@ -97,6 +97,10 @@ def test_gemv_rejects(lib):
     assert gemv(lib, kernel=5) == _lib.EDTYPE
     assert gemv(lib, kernel=7) == _lib.EDTYPE
     assert gemv(lib, kernel=-1) == _lib.EDTYPE
+    # the whole matrix has at least the call's rows, and fewer than 2^31
+    assert gemv(lib, kernel=0, whole=63) == _lib.ESHAPE
+    assert gemv(lib, kernel=0, whole=-1) == _lib.ESHAPE
+    assert gemv(lib, kernel=1, whole=1 << 31) == _lib.ESHAPE
 
 
 def test_gemv_bits_rejects(lib):
@@ -213,11 +217,10 @@ def test_workspace_sizes(lib):
     assert lib.qmm_workspace_bytes(_lib.OP_GEMM, 512, 5120, 17408) == 512 * 17408 * 2 + 512 * 3 * 272 * 2
     assert lib.qmm_workspace_bytes(_lib.OP_ARGMAX, 1, 248320, 0) == 243 * 8
     # fused head: one record per product workgroup and batch row, in the layout
-    # of qmm_gemv's own choice for the shape: 32 rows per workgroup for the
-    # vocabulary-wide head at B = 1, else one workgroup per CU, in both families
-    # (the matrix cores run B >= 3 over the vocabulary and B >= 3 where x leaves
-    # the vector-ALU kernel's LDS: down at B = 5, not at B = 4; their per-CU
-    # kernels serve any N and K, 9000 x 10240 included)
+    # of qmm_gemv's own choice, the vector-ALU family for every shape: 32 rows
+    # per workgroup for the vocabulary-wide head at B = 1, one workgroup per CU
+    # where x fits in LDS otherwise, 4 rows per 64-lane workgroup where x is
+    # staged in registers (B * 2.125 * K bytes above 152 KiB: down from B = 5)
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 248320, 5120) == 7760 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 5120, 5120) == 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 4, 248320, 5120) == 4 * 256 * 8
@@ -225,11 +228,11 @@ def test_workspace_sizes(lib):
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 3, 34816, 5120) == 3 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 2, 5120, 17408) == 2 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 248320, 5120) == 8 * 256 * 8
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 5120, 17408) == 8 * 256 * 8
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 3, 300, 73728) == 3 * 150 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 4, 5120, 17408) == 4 * 256 * 8
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 5, 5120, 17408) == 5 * 256 * 8
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 9000, 10240) == 8 * 250 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 5, 5120, 17408) == 5 * 1280 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 5120, 17408) == 8 * 1280 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 3, 300, 73728) == 3 * 75 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 9000, 10240) == 8 * 2250 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 9, 248320, 5120) == size_max
     assert lib.qmm_workspace_bytes(7, 1, 1, 64) == size_max
 
@@ -237,3 +240,17 @@ def test_workspace_sizes(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load(str(tmp_path / "libw4g.so"))
+
+
+def test_binding_checks_a_given_workspace(lib):
+    """A caller's workspace is checked like the other tensors before its
+    address can reach a kernel: on the inputs' GPU, contiguous, large enough
+    (a host tensor would otherwise be read as a device address)."""
+    import torch
+    import w4_gemv_greedy_amd as w4g
+    need = w4g.workspace_bytes(_lib.OP_GEMM, 70, 320, 1088)
+    assert need > 0
+    with pytest.raises(ValueError, match="same GPU"):
+        w4g._workspace(_lib.OP_GEMM, 70, 320, 1088, 0, torch.empty(need, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        w4g._workspace(_lib.OP_GEMM, 70, 320, 1088, 0, bytearray(need))

@@ -95,3 +95,48 @@ def test_lm_head_argmax_end_to_end():
             top2 = np.sort(ref[m])[-2:]
             bound = 2e-5 * np.max(np.abs(ref[m]))
             assert top2[1] - top2[0] <= 2 * bound, f"row {m}: id {ids[m]} vs {want[m]} beyond a tie"
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_default_gemv_batch_invariant(name):
+    """The library's own choice of kernel (qmm_gemv, qmm_gemv_argmax) depends on
+    K and the matrix alone, never on the batch: row m of an 8-row call is bit
+    for bit the row computed in a 1-, 3- or 5-row call, and the fused head's
+    logits and ids agree at every batch size (a request served beside others
+    gets the bits it gets alone)."""
+    wq, sc, bi, W = _weights(name)
+    N, K, mid = SHAPES[name]
+    x = synth.activations(8, K, workload=5, matrix=mid, layer=11)
+    X = up_bf16(x)
+    y8 = down(w4g.qmm_gemv(*W, X))
+    for Bn in (1, 3, 5):
+        yb = down(w4g.qmm_gemv(*W, X[:Bn].contiguous()))
+        assert np.array_equal(yb.view(np.uint32), y8[:Bn].view(np.uint32)), f"{name}: B={Bn} differs from B=8"
+    y1 = down(w4g.qmm_gemv(*W, X[7:8].contiguous()))
+    assert np.array_equal(y1[0].view(np.uint32), y8[7].view(np.uint32)), f"{name}: row 7 alone differs"
+    rows = _sample_rows(N, 11)[:96]
+    assert_close(y8[:, rows], oracle.qmm_rows(wq, sc, bi, x, rows), f"{name} B=8 default")
+    if name == "lm_head":
+        ids8, lg8 = w4g.qmm_gemv_argmax(*W, X)
+        assert np.array_equal(down(lg8).view(np.uint32), y8.view(np.uint32))
+        ids8 = ids_down(ids8)
+        assert np.array_equal(ids8, oracle.argmax(y8))
+        for Bn in (1, 3):
+            ids_b, lg_b = w4g.qmm_gemv_argmax(*W, X[:Bn].contiguous())
+            assert np.array_equal(down(lg_b).view(np.uint32), y8[:Bn].view(np.uint32))
+            assert np.array_equal(ids_down(ids_b), ids8[:Bn])
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_default_gemv_row_slice_with_whole(B):
+    """A call over a row slice that names its whole matrix (whole = 248,320)
+    gives the whole head's rows bit for bit: an 8-way shard of the vocabulary
+    (31,040 rows: another layout and rows per CU) and an unaligned slice."""
+    wq, sc, bi, W = _weights("lm_head")
+    N, K, mid = SHAPES["lm_head"]
+    x = synth.activations(B, K, workload=5, matrix=mid, layer=20 + B)
+    X = up_bf16(x)
+    y = down(w4g.qmm_gemv(*W, X))
+    for lo, hi in ((3 * 31040, 4 * 31040), (100003, 105123)):
+        ys = down(w4g.qmm_gemv(W[0][lo:hi], W[1][lo:hi], W[2][lo:hi], X, whole=N))
+        assert np.array_equal(ys.view(np.uint32), y[:, lo:hi].view(np.uint32)), f"rows [{lo}, {hi}) at B={B}"

@@ -82,12 +82,22 @@ def workspace_bytes(op, rows, n, k):
 
 
 def _workspace(op, rows, n, k, device, workspace):
+    """The workspace for op: a new one when none is given, else the caller's,
+    checked like every other tensor argument (on the inputs' GPU, contiguous,
+    large enough) before its address reaches a kernel."""
     need = workspace_bytes(op, rows, n, k)
     if need == 0:
         return None, 0
     torch = _torch()
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    d = workspace.get_device()
+    if d < 0 or d != (device if isinstance(device, int) else device.index):
+        raise ValueError("workspace must be on the same GPU as the inputs")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     if workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace needs {need} bytes")
     return workspace, need
@@ -113,19 +123,22 @@ def _call_qmm(fn, op, wq, scales, biases, x, y, workspace, extra=(), y_dtypes=No
     return y
 
 
-def qmm_gemv(wq, scales, biases, x, y=None, workspace=None, kernel=GEMV_AUTO, bits=4):
+def qmm_gemv(wq, scales, biases, x, y=None, workspace=None, kernel=GEMV_AUTO, bits=4, whole=None):
     """Decode product for 1 <= B <= 8 rows of x; returns y [B][N] fp32.
 
-    kernel: GEMV_AUTO (the library's choice), GEMV_VALU, GEMV_MFMA,
-    GEMV_VALU_REGS (the register-staged variant of the vector-ALU family) or
-    GEMV_MFMA_STEP (the step-staged variant of the matrix-core family).
+    kernel: GEMV_AUTO (the library's choice, a function of K and `whole` only,
+    never of B), GEMV_VALU, GEMV_MFMA, GEMV_VALU_REGS (the register-staged
+    variant of the vector-ALU family) or GEMV_MFMA_STEP (the step-staged
+    variant of the matrix-core family).
+    whole: the row count of the whole matrix when wq holds a row slice of it
+    (None: N), so that the slice's rows get the whole matrix's bits.
     bits: code width, 4 (the default) or 2 or 8 (wq [N][K*bits/32], low field
     first; the library's choice of kernel only).
     """
     if x.dim() == 2 and not 1 <= x.shape[0] <= MAX_GEMV_BATCH:
         raise ValueError(f"qmm_gemv takes 1..{MAX_GEMV_BATCH} rows")
     if bits != 4:
-        if kernel != GEMV_AUTO:
+        if kernel != GEMV_AUTO or whole is not None:
             raise ValueError("other code widths take the library's kernel choice only")
         torch = _torch()
         N, K = _check_qmm(wq, scales, biases, x, bits)
@@ -139,9 +152,10 @@ def qmm_gemv(wq, scales, biases, x, y=None, workspace=None, kernel=GEMV_AUTO, bi
                                            y.data_ptr(), rows, N, K, int(bits), None, 0, _stream(wq))
         _lib.check("qmm_gemv_bits", status)
         return y
-    if kernel == GEMV_AUTO:
+    if kernel == GEMV_AUTO and whole is None:
         return _call_qmm("qmm_gemv", OP_GEMV, wq, scales, biases, x, y, workspace)
-    return _call_qmm("qmm_gemv_ex", OP_GEMV, wq, scales, biases, x, y, workspace, (int(kernel),))
+    return _call_qmm("qmm_gemv_ex", OP_GEMV, wq, scales, biases, x, y, workspace,
+                     (int(kernel), int(whole or 0)))
 
 
 def qmm_gemm(wq, scales, biases, x, y=None, workspace=None, out_dtype=None):

@@ -11,7 +11,7 @@ F32, BF16 = 0, 1
 OP_GEMV, OP_GEMM, OP_ARGMAX, OP_GEMV_ARGMAX, OP_ARGMAX_TOP2 = 0, 1, 2, 3, 4
 SENTINEL = 0xFFFFFFFF
 MAX_GEMV_BATCH = 8
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_VALU_REGS, GEMV_MFMA_STEP = 0, 1, 2, 3, 4
 
@@ -39,7 +39,7 @@ def load(path=None):
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.qmm_gemv.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.qmm_gemv.restype = I
-    lib.qmm_gemv_ex.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P, I]
+    lib.qmm_gemv_ex.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P, I, I64]
     lib.qmm_gemv_ex.restype = I
     lib.qmm_gemv_bits.argtypes = [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]
     lib.qmm_gemv_bits.restype = I

@@ -102,7 +102,7 @@ size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k) {
 
 int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                 const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
-                size_t workspace_bytes, void* stream, int kernel) {
+                size_t workspace_bytes, void* stream, int kernel, int64_t whole) {
   if (kernel != W4G_GEMV_AUTO && kernel != W4G_GEMV_VALU && kernel != W4G_GEMV_MFMA &&
       kernel != W4G_GEMV_VALU_REGS && kernel != W4G_GEMV_MFMA_STEP)
     return W4G_EDTYPE;
@@ -110,7 +110,9 @@ int qmm_gemv_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* bias
     return (!wq || !scales || !biases || !x || !y) ? W4G_EINVAL_PTR : W4G_ESHAPE;
   const int rc = check_qmm(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, 0);
   if (rc) return rc;
-  if (kernel == W4G_GEMV_AUTO) kernel = w4g::gemv_auto_family((int)B, N, K);
+  if (whole == 0) whole = N;
+  if (whole < N || whole >= kMaxDim) return W4G_ESHAPE;
+  if (kernel == W4G_GEMV_AUTO) kernel = w4g::gemv_auto_family(whole, K);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (kernel == W4G_GEMV_MFMA || kernel == W4G_GEMV_MFMA_STEP)
     return from_hip(w4g::launch_gemv_mfma(wq, scales, biases, x, y, (int)B, N, K,
@@ -125,7 +127,7 @@ int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
   if (bits != 2 && bits != 4 && bits != 8) return W4G_EDTYPE;
   if (bits == 4)
     return qmm_gemv_ex(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, stream,
-                       W4G_GEMV_AUTO);
+                       W4G_GEMV_AUTO, 0);
   if (B < 1 || B > W4G_MAX_GEMV_BATCH)
     return (!wq || !scales || !biases || !x || !y) ? W4G_EINVAL_PTR : W4G_ESHAPE;
   const int rc = check_qmm(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, 0, 4, bits);
@@ -139,7 +141,7 @@ int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
              const uint16_t* x, float* y, int64_t B, int64_t N, int64_t K, void* workspace,
              size_t workspace_bytes, void* stream) {
   return qmm_gemv_ex(wq, scales, biases, x, y, B, N, K, workspace, workspace_bytes, stream,
-                     W4G_GEMV_AUTO);
+                     W4G_GEMV_AUTO, 0);
 }
 
 int qmm_gemm_ex(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,

@@ -750,7 +750,7 @@ hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_
 }
 
 int64_t gemv_argmax_records(int B, int64_t N, int64_t K) {
-  if (gemv_auto_family(B, N, K) == 2) return gemv_mfma_argmax_records(B, N, K);
+  if (gemv_auto_family(N, K) == 2) return gemv_mfma_argmax_records(B, N, K);
   if (use_regs(B, K, false)) {
     const int R = regs_rows(B);
     return (N + 2 * R - 1) / (2 * R);
@@ -764,25 +764,22 @@ int64_t gemv_argmax_records(int B, int64_t N, int64_t K) {
 hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                               const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                               hipStream_t stream) {
-  if (gemv_auto_family(B, N, K) == 2)
+  if (gemv_auto_family(N, K) == 2)
     return launch_gemv_mfma_argmax(wq, scales, biases, x, y, rec, B, N, K, stream);
   return dispatch<true>(wq, scales, biases, x, y, rec, B, N, K, false, stream);
 }
 
-// Measured with the per-CU layouts of both families (graph-timed, B = 1..8,
-// vector ALUs against matrix cores, us): the vector ALUs are faster at small B;
-// the matrix cores from B = 4 where a CU holds more than 40 rows (gate-up at
-// B = 4: 33.5 against 30.9, at B = 8: 50.2 against 32.2; lm_head at B = 4:
-// 208 against 179), and already at B = 3 where it holds more than 256
-// (lm_head: 183 against 176; gate-up, 136 rows: 29.6 against 29.9), from B = 7
-// for the layer widths (o_proj at B = 6: 10.6 against 11.0, at B = 8: 12.8
-// against 11.5), and where x is staged in registers from B = 3 (down, K =
-// 17408, leaves the vector-ALU kernel's LDS from B = 5: 25.5 against 55.1 at
-// B = 5, 26.6 against 75 at B = 8; at B = 3 and 4 it stays in LDS, 20.0 and
-// 23.5 against 24.9 and 25.1).
-int gemv_auto_family(int B, int64_t N, int64_t K) {
-  if (use_regs(B, K, false)) return B <= 2 ? 1 : 2;
-  if (B >= 7 || (B >= 4 && per_cu_rows(N) > 40) || (B == 3 && per_cu_rows(N) > 256)) return 2;
+// The family qmm_gemv runs: a function of the matrix width K and of the row
+// count of the whole matrix only, never of the batch size or of the rows one
+// call covers, so a row keeps its bits at every batch size and in every row
+// slice (the pages key the K reduction on the whole matrix and ask that a
+// request served beside others get the bits it gets alone).  Every (K, whole)
+// takes the vector-ALU family: it is the faster one at B = 1 for every shape
+// here (o_proj, gate-up, down and the vocabulary head), and the matrix-core
+// family, faster from B = 3..7 depending on the shape, gives other bits.
+int gemv_auto_family(int64_t whole, int64_t K) {
+  (void)whole;
+  (void)K;
   return 1;
 }
 

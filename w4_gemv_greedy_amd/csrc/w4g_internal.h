@@ -31,9 +31,9 @@ hipError_t launch_gemv_bits(const uint32_t* wq, const uint16_t* scales, const ui
                             const uint16_t* x, float* y, int B, int64_t N, int64_t K, int bits,
                             hipStream_t stream);
 bool gemv_bits_fits(int B, int64_t K);
-// Kernel family qmm_gemv runs for a shape (1 = vector ALU, 2 = matrix cores);
-// a function of (B, N, K) only.
-int gemv_auto_family(int B, int64_t N, int64_t K);
+// Kernel family qmm_gemv runs (1 = vector ALU, 2 = matrix cores): a function
+// of the whole matrix's row count and of K only, never of the batch size.
+int gemv_auto_family(int64_t whole, int64_t K);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                          uint32_t* ids, void* workspace, hipStream_t stream);
