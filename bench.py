@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--skip-extras", action="store_true",
                    help="only the headline sweep (used for profiler runs)")
     p.add_argument("--skip-cpu", action="store_true", help="skip the oracle CPU baseline")
-    p.add_argument("--probe", choices=["gate_up", "copy"],
+    p.add_argument("--probe", choices=PROBES,
                    help="run only one kernel a few times (for hardware-counter runs) and exit")
     return p.parse_args()
 
@@ -86,8 +86,16 @@ def counted_traffic():
         return None
 
 
+PROBES = ["copy"] + [f"{p}_b{b}_{f}" for p in ("o_proj", "gate_up", "down", "lm_head")
+                      for b in (1, 8) for f in ("auto", "mfma")] + \
+         ["lm_head_argmax_b1", "gemm_o_proj", "gemm_gate_up", "gemm_down"]
+
+
 def probe(kind):
-    """A short, fixed workload for hardware-counter collection."""
+    """A short, fixed workload for hardware-counter collection: a plain 1 GiB
+    device copy (the calibration), one decode product (`<product>_b<B>_<family>`,
+    four launches over distinct copies of the matrix, three rounds), the fused
+    lm_head + argmax at B=1, or a 512-row prompt product (`gemm_<product>`)."""
     import torch
     import w4_gemv_greedy_amd as w4g
     from w4_gemv_greedy_amd import synth
@@ -100,12 +108,39 @@ def probe(kind):
             b.copy_(a)
         torch.cuda.synchronize()
         return
-    mats = [Mat(2 * INTER, HIDDEN, 5, synth.GATE_UP, l, dev) for l in range(4)]
-    x = make_x(1, HIDDEN, 5, synth.GATE_UP, 0, dev)
-    y = torch.empty((1, 2 * INTER), dtype=torch.float32, device=dev)
+    shapes = {"o_proj": (HIDDEN, HIDDEN, synth.O_PROJ), "gate_up": (2 * INTER, HIDDEN, synth.GATE_UP),
+              "down": (HIDDEN, INTER, synth.DOWN), "lm_head": (VOCAB, HIDDEN, synth.LM_HEAD)}
+    if kind.startswith("gemm_"):
+        N, K, mid = shapes[kind[5:]]
+        mats = [Mat(N, K, 4, mid, l, dev) for l in range(2)]
+        x = make_x(512, K, 4, mid, 0, dev)
+        y = torch.empty((512, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(w4g.workspace_bytes(w4g.OP_GEMM, 512, N, K), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            for m in mats:
+                w4g.qmm_gemm(m.wq, m.sc, m.bi, x, y, ws)
+        torch.cuda.synchronize()
+        return
+    if kind == "lm_head_argmax_b1":
+        N, K, mid = shapes["lm_head"]
+        m = Mat(N, K, 5, mid, 0, dev)
+        x = make_x(1, K, 5, mid, 0, dev)
+        ids = torch.empty(1, dtype=torch.int32, device=dev)
+        ws = torch.empty(w4g.workspace_bytes(w4g.OP_GEMV_ARGMAX, 1, N, K), dtype=torch.uint8, device=dev)
+        for _ in range(6):
+            w4g.qmm_gemv_argmax(m.wq, m.sc, m.bi, x, None, ids, ws, want_logits=False)
+        torch.cuda.synchronize()
+        return
+    name, b, fam = kind.rsplit("_", 2)
+    N, K, mid = shapes[name]
+    B = int(b[1:])
+    kernel = w4g.GEMV_AUTO if fam == "auto" else w4g.GEMV_MFMA
+    mats = [Mat(N, K, 5, mid, l, dev) for l in range(1 if name == "lm_head" else 4)]
+    x = make_x(B, K, 5, mid, 0, dev)
+    y = torch.empty((B, N), dtype=torch.float32, device=dev)
     for _ in range(3):
         for m in mats:
-            w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y)
+            w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y, kernel=kernel)
     torch.cuda.synchronize()
 
 
@@ -133,41 +168,103 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle (plain C, OpenMP over output rows) on the host cores, bounded sample.
+def host_info():
+    """nproc and the CPU model of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
 
-    Runs whole batch-1 products of one layer (o_proj, gate-up, down) and the
-    lm_head plus the argmax, in that order, repeating until the time budget is
-    spent; the rate is their algorithmic bytes over the oracle's time.
+
+def cpu_baseline(budget_s=8.0):
+    """The oracle (plain C, OpenMP over output elements, fp64 sums) on the host cores.
+
+    All cores: whole batch-1 products of one layer (o_proj, gate-up, down) and
+    the lm_head plus the argmax, repeated until `budget_s` is spent; the rate is
+    their algorithmic bytes over the oracle's time, and the decode step of 16
+    layers plus the head follows from the per-call times (ms per token at B=1).
+    One core: a seeded sample of output rows of the same products (1/32 of each
+    matrix), scaled to whole calls.  Per config: ms per call at B = 1, 4, 8 and
+    for the 512-row prompt, from a row (or column) sample at all cores, scaled.
+    Every product's work is proportional to its output count, so a row sample
+    scales exactly up to the sample's own timing noise.
     """
     import oracle
     from w4_gemv_greedy_amd import synth
     oracle.load()
     threads = oracle.threads()
-    mats = []
+    mats = {}
     for name, N, K, mid in (("o_proj", HIDDEN, HIDDEN, synth.O_PROJ),
                             ("gate_up", 2 * INTER, HIDDEN, synth.GATE_UP),
                             ("down", HIDDEN, INTER, synth.DOWN),
                             ("lm_head", VOCAB, HIDDEN, synth.LM_HEAD)):
         wq, sc, bi = synth.weights(N, K, workload=5, matrix=mid, layer=0)
-        x = synth.activations(1, K, workload=5, matrix=mid, layer=0)
-        mats.append((name, N, K, wq, sc, bi, x))
-    done_bytes, spent, counts = 0, 0.0, {}
+        x = synth.activations(8, K, workload=5, matrix=mid, layer=0)
+        mats[name] = (N, K, wq, sc, bi, x)
+
+    # all cores, whole batch-1 calls
+    done_bytes, spent, counts, per_call = 0, 0.0, {}, {}
     while spent < budget_s:
-        for name, N, K, wq, sc, bi, x in mats:
+        for name, (N, K, wq, sc, bi, x) in mats.items():
             t0 = time.perf_counter()
-            y = oracle.qmm(wq, sc, bi, x)
+            y = oracle.qmm(wq, sc, bi, x[:1], threads=threads)
             if name == "lm_head":
                 oracle.argmax(y)
                 done_bytes += 4 * VOCAB
-            spent += time.perf_counter() - t0
+            dt = time.perf_counter() - t0
+            spent += dt
+            per_call.setdefault(name, []).append(dt)
             done_bytes += gemv_bytes(N, K, 1)
             counts[name] = counts.get(name, 0) + 1
+    ms = {k: 1e3 * float(np.median(v)) for k, v in per_call.items()}
+    step_ms = LAYERS * (ms["o_proj"] + ms["gate_up"] + ms["down"]) + ms["lm_head"]
+
+    def sampled(name, B, frac, thr, reps=1):
+        N, K, wq, sc, bi, x = mats[name]
+        rows = np.unique(np.random.default_rng(B).choice(N, max(8, int(N * frac)), replace=False))
+        best = None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.qmm_rows(wq, sc, bi, x[:B], rows, threads=thr)
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        return 1e3 * best * N / rows.size
+
+    # one core, a 1/32 row sample of each batch-1 product
+    one = {name: sampled(name, 1, 1 / 32, 1) for name in mats}
+    one_step_ms = LAYERS * (one["o_proj"] + one["gate_up"] + one["down"]) + one["lm_head"]
+    # per config, all cores (row samples; the 512-row prompt on 64 output columns)
+    cfg = {"1_o_proj_b1": round(ms["o_proj"], 3)}
+    for name in ("gate_up", "down"):
+        cfg[f"2_{name}_b1"] = round(ms[name], 3)
+        for B in (4, 8):
+            cfg[f"2_{name}_b{B}"] = round(sampled(name, B, 1 / 16, threads), 3)
+    cfg["3_lm_head_argmax_b1"] = round(ms["lm_head"], 3)
+    for name in ("o_proj", "gate_up", "down"):
+        N, K, wq, sc, bi, _ = mats[name]
+        xp = synth.activations(512, K, workload=4, matrix=synth.O_PROJ, layer=0)
+        cols = np.arange(0, N, N // 64)[:64]
+        t0 = time.perf_counter()
+        oracle.qmm_rows(wq, sc, bi, xp, cols, threads=threads)
+        cfg[f"4_prompt_m512_{name}"] = round(1e3 * (time.perf_counter() - t0) * N / cols.size, 1)
+    cfg["5_decode_step_b1_ms_per_token"] = round(step_ms, 2)
     sample = ", ".join(f"{v} x {k}" for k, v in counts.items())
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads,
+    return {"value": round(step_bytes(1) / (step_ms * 1e-3) / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"whole batch-1 products of one layer plus lm_head+argmax ({sample}), "
-                      f"{done_bytes / 1e9:.2f} GB in {spent:.1f} s"}
+            "sample": f"whole batch-1 products of one layer plus lm_head+argmax ({sample}, "
+                      f"{done_bytes / 1e9:.2f} GB in {spent:.1f} s), the decode step's rate from their "
+                      f"median per-call times (16 layers plus the head)",
+            "host": dict(host_info(), oracle_threads=threads),
+            "one_core": {"value": round(step_bytes(1) / (one_step_ms * 1e-3) / 1e9, 4), "unit": "GB/s",
+                         "cores": 1, "ms_per_token_b1": round(one_step_ms, 1),
+                         "ms_per_call_b1": {k: round(v, 2) for k, v in one.items()},
+                         "sample": "1/32 of the output rows of each batch-1 product, scaled to whole calls"},
+            "ms_per_call": cfg}
 
 
 def main():
@@ -342,15 +439,16 @@ def ceilings(torch, layers, dev, timed):
         nb = nbytes // 16 * 16
         bufs = [torch.full((nb,), c, dtype=torch.uint8, device=dev) for c in range(copies)]
         best = None
+        launches = max(16, copies)  # every copy once per replay
         for blocks, threads, u in ((256, 1024, 4), (2048, 256, 4), (4096, 256, 2)):
             def run(blocks=blocks, threads=threads, u=u):
-                for i in range(16):
+                for i in range(launches):
                     st = lib.w4g_ceiling_read(bufs[i % copies].data_ptr(), nb, blocks, threads, u,
                                               sink.data_ptr(), stream())
                     if st != 0:
                         raise RuntimeError(f"w4g_ceiling_read: hip error {st}")
             ms, _ = timed(run, 10, 2, True)
-            us = ms * 1e3 / 16
+            us = ms * 1e3 / launches
             if best is None or us < best[0]:
                 best = (us, f"{blocks}x{threads}, {u} loads in flight")
         out["hbm_read"][name] = {"bytes": nb, "us": round(best[0], 2),
@@ -391,29 +489,30 @@ def ceilings(torch, layers, dev, timed):
     return out
 
 
-def eager_percentiles(torch, w4g, layers, dev, calls=160):
+def eager_percentiles(torch, w4g, copies, dev, calls=160):
     """Per-call times of the batch-1 products as eager launches (HIP events around
-    each call, cycling over the 16 layers' weights): median, p10 and p90 in us."""
+    each call, cycling over distinct copies of each matrix: 40 for o_proj, 16
+    for gate-up and down): median, p10 and p90 in us."""
     res = {}
     from w4_gemv_greedy_amd import synth
     for name, idx, N, K in (("o_proj", 0, HIDDEN, HIDDEN), ("gate_up", 1, 2 * INTER, HIDDEN),
                             ("down", 2, HIDDEN, INTER)):
         x = make_x(1, K, 5, synth.GENERIC, 98, dev)
         y = torch.empty((1, N), dtype=torch.float32, device=dev)
-        for l in range(LAYERS):
-            m = layers[l][idx]
+        mats = copies[idx]
+        for m in mats:
             w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
         torch.cuda.synchronize()
         for i in range(calls):
-            m = layers[i % LAYERS][idx]
+            m = mats[i % len(mats)]
             ev[i][0].record()
             w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y)
             ev[i][1].record()
         torch.cuda.synchronize()
         t = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in ev]))
         res[name] = {"median_us": round(float(np.median(t)), 2), "p10_us": round(float(np.percentile(t, 10)), 2),
-                     "p90_us": round(float(np.percentile(t, 90)), 2), "calls": calls}
+                     "p90_us": round(float(np.percentile(t, 90)), 2), "calls": calls, "copies": len(mats)}
     return res
 
 
@@ -423,7 +522,14 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args, make_step):
     step_e, _, _ = make_step(1)
     ms_e, _ = timed(step_e, 10, 3, False)
     ex["sweep_b1_eager_us"] = round(ms_e * 1e3, 1)
-    ex["b1_eager_per_call"] = eager_percentiles(torch, w4g, layers, dev)
+    # distinct copies of each matrix for the per-product timings, so that no call
+    # finds its matrix in the 256 MB cache: o_proj over 40 copies (590 MB: the
+    # 16 layers' and 24 more), gate-up and down over the 16 layers' (1.6 GB and
+    # 0.8 GB)
+    extra_o = [Mat(HIDDEN, HIDDEN, 5, synth.O_PROJ, 100 + c, dev) for c in range(24)]
+    copies = {0: [lay[0] for lay in layers] + extra_o, 1: [lay[1] for lay in layers],
+              2: [lay[2] for lay in layers]}
+    ex["b1_eager_per_call"] = eager_percentiles(torch, w4g, copies, dev)
     log(f"sweep B=1 eager {ex['sweep_b1_eager_us']} us/step; per call {ex['b1_eager_per_call']}")
     # the 16 gate-up launches of a step alone, back to back in a graph
     xg_in = [make_x(1, HIDDEN, 5, synth.GATE_UP, l, dev) for l in range(LAYERS)]
@@ -481,29 +587,32 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args, make_step):
     log(f"lm_head+argmax {ex['lm_head_argmax_us_per_token']} us/token, argmax alone {ex['argmax_us']} us, "
         f"top two {ex['argmax_top2_us']} us")
 
-    # per-product averages at batch 1, 4, 8 for both kernel families, each cycling
-    # through the 16 layers' weights (2.6 GB, so nothing stays in the 256 MB cache)
-    for fam_name, fam in (("valu", w4g.GEMV_VALU), ("mfma", w4g.GEMV_MFMA)):
+    # per-product averages at batch 1, 4, 8: the library's own choice and both
+    # kernel families, each cycling through the distinct copies above
+    for fam_name, fam in (("auto", w4g.GEMV_AUTO), ("valu", w4g.GEMV_VALU), ("mfma", w4g.GEMV_MFMA)):
         for Bn in (1, 4, 8):
+            if fam_name == "valu" and Bn == 1:
+                continue  # the automatic choice is the vector-ALU kernel at B = 1
             for name, idx, N, K, mid in (("o_proj", 0, HIDDEN, HIDDEN, synth.O_PROJ),
                                          ("gate_up", 1, 2 * INTER, HIDDEN, synth.GATE_UP),
                                          ("down", 2, HIDDEN, INTER, synth.DOWN)):
                 x = make_x(Bn, K, 5, mid, 99, dev)
                 y = torch.empty((Bn, N), dtype=torch.float32, device=dev)
+                mats = copies[idx]
 
-                def run(idx=idx, x=x, y=y, fam=fam):
-                    for l in range(LAYERS):
-                        for j in range(3):
-                            m = layers[l][j]
-                            if j == idx:
-                                w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y, kernel=fam)
+                def run(mats=mats, x=x, y=y, fam=fam):
+                    for m in mats:
+                        w4g.qmm_gemv(m.wq, m.sc, m.bi, x, y, kernel=fam)
                 ms, _ = timed(run, 5, 2, True)
-                us = ms * 1e3 / LAYERS
+                us = ms * 1e3 / len(mats)
                 gbs = gemv_bytes(N, K, Bn) / (us * 1e-6) / 1e9
                 ex[f"gemv_{name}_b{Bn}_{fam_name}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
-                                                      "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+                                                      "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                                                      "copies": len(mats)}
     log("per-product: " + ", ".join(f"{k} {v['us']}us {v['GBps']}GB/s" for k, v in ex.items()
                                     if k.startswith("gemv_")))
+    del extra_o, copies
+    torch.cuda.empty_cache()
 
     # other code widths (B = 1): the 8-bit LM head with the greedy argmax, and the
     # gate-up product at 8 and 2 bits, cycling over enough copies that none is
@@ -574,32 +683,37 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args, make_step):
         ids8 = torch.empty(8, dtype=torch.int32, device=dev)
         ws8 = torch.empty(w4g.workspace_bytes(w4g.OP_ARGMAX, 8, VOCAB, 0), dtype=torch.uint8, device=dev)
 
-        def step8():
+        def step8(fam=w4g.GEMV_AUTO):
             for l in range(LAYERS):
                 o, g, d = layers[l]
-                w4g.qmm_gemv(o.wq, o.sc, o.bi, xs8[l][0], yo)
-                w4g.qmm_gemv(g.wq, g.sc, g.bi, xs8[l][1], yg)
-                w4g.qmm_gemv(d.wq, d.sc, d.bi, xs8[l][2], yo)
-            w4g.qmm_gemv(head.wq, head.sc, head.bi, xh8, lg)
+                w4g.qmm_gemv(o.wq, o.sc, o.bi, xs8[l][0], yo, kernel=fam)
+                w4g.qmm_gemv(g.wq, g.sc, g.bi, xs8[l][1], yg, kernel=fam)
+                w4g.qmm_gemv(d.wq, d.sc, d.bi, xs8[l][2], yo, kernel=fam)
+            w4g.qmm_gemv(head.wq, head.sc, head.bi, xh8, lg, kernel=fam)
             w4g.vocab_argmax(lg, ids8, ws8)
-        ms, _ = timed(step8, 10, 2, True)
-        ex["sweep_b8"] = {"us_per_step": round(ms * 1e3, 1), "us_per_token": round(ms * 1e3 / 8, 2),
-                          "GBps": round(step_bytes(8) / (ms * 1e-3) / 1e9, 1)}
-        log(f"sweep B=8: {ex['sweep_b8']}")
+        # the library's own choice (the vector-ALU family: a row's bits at B = 8
+        # are its bits at B = 1), and the matrix-core family named explicitly
+        for key, fam in (("sweep_b8", w4g.GEMV_AUTO), ("sweep_b8_mfma", w4g.GEMV_MFMA)):
+            ms, _ = timed(lambda fam=fam: step8(fam), 10, 2, True)
+            ex[key] = {"us_per_step": round(ms * 1e3, 1), "us_per_token": round(ms * 1e3 / 8, 2),
+                       "GBps": round(step_bytes(8) / (ms * 1e-3) / 1e9, 1)}
+            log(f"{key}: {ex[key]}")
 
         # the head alone at B = 8: product + two-pass argmax, and fused
         ws8f = torch.empty(w4g.workspace_bytes(w4g.OP_GEMV_ARGMAX, 8, VOCAB, HIDDEN), dtype=torch.uint8,
                            device=dev)
 
-        def head8():
-            w4g.qmm_gemv(head.wq, head.sc, head.bi, xh8, lg)
+        def head8(fam=w4g.GEMV_AUTO):
+            w4g.qmm_gemv(head.wq, head.sc, head.bi, xh8, lg, kernel=fam)
             w4g.vocab_argmax(lg, ids8, ws8)
 
         def head8_fused():
             w4g.qmm_gemv_argmax(head.wq, head.sc, head.bi, xh8, None, ids8, ws8f, want_logits=False)
         ms, _ = timed(head8, 10, 2, True, reps=2)
+        ms_m, _ = timed(lambda: head8(w4g.GEMV_MFMA), 10, 2, True, reps=2)
         ms_f, _ = timed(head8_fused, 10, 2, True, reps=2)
-        ex["lm_head_argmax_b8"] = {"us_per_call": round(ms * 1e3, 1), "fused_ids_only_us_per_call": round(ms_f * 1e3, 1)}
+        ex["lm_head_argmax_b8"] = {"us_per_call": round(ms * 1e3, 1), "mfma_us_per_call": round(ms_m * 1e3, 1),
+                                   "fused_ids_only_us_per_call": round(ms_f * 1e3, 1)}
         log(f"lm_head+argmax B=8: {ex['lm_head_argmax_b8']}")
 
     ex["ceilings"] = ceilings(torch, layers, dev, timed)

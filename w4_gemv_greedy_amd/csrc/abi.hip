@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/w4g.h"
 #include "w4g_internal.h"
 
@@ -50,10 +52,31 @@ int check_qmm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases
 int from_hip(hipError_t e) { return e == hipSuccess ? W4G_OK : W4G_ELAUNCH; }
 
 size_t gemv_argmax_bytes(int64_t B, int64_t N, int64_t K) {
-  return (size_t)B * (size_t)w4g::gemv_argmax_records((int)B, N, K) * sizeof(uint2);
+  return (size_t)B * (size_t)w4g::gemv_argmax_records_max((int)B, N, K) * sizeof(uint2);
 }
 
 }  // namespace
+
+namespace w4g {
+
+// Compute units of the current device, queried once per device and kept (a
+// device attribute, the same every time it is read); 1..kMaxCUs.  Where the
+// query fails the layouts assume kMaxCUs.
+int cu_count() {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cached[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return kMaxCUs;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = kMaxCUs;
+  v = n < kMaxCUs ? n : kMaxCUs;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace w4g
 
 extern "C" {
 
@@ -164,25 +187,30 @@ int qmm_gemm(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
   return qmm_gemm_ex(wq, scales, biases, x, y, M, N, K, workspace, workspace_bytes, stream, W4G_F32);
 }
 
-int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                    const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N, int64_t K,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the fused head's entry points: pointers, sizes, alignment
+// and, with `alias`, that no output overlaps an input or another output (the
+// records' `need` bytes at `workspace`, when one is given, among the outputs).
+int check_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                      const uint16_t* x, const float* logits, const uint32_t* ids, int64_t B, int64_t N,
+                      int64_t K, const void* workspace, size_t need, bool alias = true) {
   if (!wq || !scales || !biases || !x || !ids) return W4G_EINVAL_PTR;
   if (B < 1 || B > W4G_MAX_GEMV_BATCH || N < 1 || N >= kMaxDim || K < 64 || K >= kMaxDim || K % 64)
     return W4G_ESHAPE;
   if (!aligned16(wq) || !aligned16(x) || (logits && !aligned16(logits)) || !aligned2(scales) ||
       !aligned2(biases) || (reinterpret_cast<uintptr_t>(ids) & 3u))
     return W4G_EALIGN;
-  const size_t need = gemv_argmax_bytes(B, N, K);
-  if (!workspace || workspace_bytes < need) return W4G_EWORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return W4G_EALIGN;
+  if (!alias) return W4G_OK;
   const size_t wbytes = (size_t)N * (size_t)(K / 8) * sizeof(uint32_t);
   const size_t gbytes = (size_t)N * (size_t)(K / 64) * sizeof(uint16_t);
   const size_t xbytes = (size_t)B * (size_t)K * sizeof(uint16_t);
   const size_t lbytes = logits ? (size_t)B * (size_t)N * sizeof(float) : 0;
   const size_t ibytes = (size_t)B * sizeof(uint32_t);
   const void* outs[3] = {logits, ids, workspace};
-  const size_t osz[3] = {lbytes, ibytes, need};
+  const size_t osz[3] = {lbytes, ibytes, workspace ? need : 0};
   for (int i = 0; i < 3; ++i) {
     if (overlap(outs[i], osz[i], wq, wbytes) || overlap(outs[i], osz[i], scales, gbytes) ||
         overlap(outs[i], osz[i], biases, gbytes) || overlap(outs[i], osz[i], x, xbytes))
@@ -190,11 +218,33 @@ int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
     for (int j = i + 1; j < 3; ++j)
       if (overlap(outs[i], osz[i], outs[j], osz[j])) return W4G_EALIAS;
   }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint2* rec = reinterpret_cast<uint2*>(workspace);
+  return W4G_OK;
+}
+
+int run_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, const uint16_t* x,
+                    float* logits, uint32_t* ids, int64_t B, int64_t N, int64_t K, uint2* rec,
+                    hipStream_t s) {
   const hipError_t e = w4g::launch_gemv_argmax(wq, scales, biases, x, logits, rec, (int)B, N, K, s);
   if (e != hipSuccess) return W4G_ELAUNCH;
   return from_hip(w4g::launch_argmax_combine(rec, B, w4g::gemv_argmax_records((int)B, N, K), ids, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                    const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N, int64_t K,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, nullptr, 0, false);
+  if (rc) return rc;
+  const size_t need = gemv_argmax_bytes(B, N, K);
+  if (!workspace || workspace_bytes < need) return W4G_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return W4G_EALIGN;
+  rc = check_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, workspace, need);
+  if (rc) return rc;
+  return run_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, reinterpret_cast<uint2*>(workspace),
+                         reinterpret_cast<hipStream_t>(stream));
 }
 
 int vocab_argmax_top2(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,

@@ -477,7 +477,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 // + 1), so waiting for all but the newest stages' loads completes the oldest.
 // Per output the arithmetic and its order are those of gemm_kernel, whatever
 // the tile: every variant gives the same bits.
-constexpr int kCUs = 256;  // compute units of the MI355X
+// (the loop choice below is a matter of speed only: the three loops give the
+// same bits; it is keyed on this device's compute units)
 
 // Buffer load of 16 bytes per lane into LDS at m0 + 16 * lane.
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, __amdgpu_buffer_rsrc_t r, uint32_t soff) {
@@ -709,7 +710,10 @@ int64_t g16_of(int64_t K) { return (((K >> 6) + 15) / 16) * 16; }
 
 // Where the 64 x 64 tiles take over (rows of the slice, 128 x 128 tiles it makes)
 #ifndef W4G_SMALL_RULE
-bool small_tiles(int64_t M, int64_t tiles128) { return tiles128 < kCUs / 2 || (M <= 128 && tiles128 < 2 * kCUs); }
+bool small_tiles(int64_t M, int64_t tiles128) {
+  const int cus = cu_count();
+  return tiles128 < cus / 2 || (M <= 128 && tiles128 < 2 * cus);
+}
 #else
 bool small_tiles(int64_t M, int64_t tiles128) { return W4G_SMALL_RULE; }
 #endif
@@ -750,13 +754,13 @@ hipError_t launch_main(const uint32_t* wq, const uint16_t* scales, const uint16_
         // 64 x 64 tiles: a 4-stage ring (83 KiB, one workgroup per CU) while the
         // tiles fit on the CUs once, else 3 stages (62 KiB) so two share a CU
         const int64_t NT = (Ns + 63) / 64, tiles = ((Ms + 63) / 64) * NT, per = (tiles + 7) / 8;
-        if (tiles <= kCUs)
+        if (tiles <= cu_count())
           hipLaunchKernelGGL((gemm_dma_kernel<1, 1, 2, 2, 4, OUT>), dim3((unsigned)(8 * per)), dim3(256), 0,
                              stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles, per, vec);
         else
           hipLaunchKernelGGL((gemm_dma_kernel<1, 1, 2, 2, 3, OUT>), dim3((unsigned)(8 * per)), dim3(256), 0,
                              stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles, per, vec);
-      } else if (!dma || tiles128 >= 2 * kCUs) {
+      } else if (!dma || tiles128 >= 2 * cu_count()) {
         const int64_t NT = (Ns + kTN - 1) / kTN, per = (tiles128 + 7) / 8;
         hipLaunchKernelGGL(gemm_kernel<OUT>, dim3((unsigned)(8 * per)), dim3(256), 0, stream, w_s, s_s,
                            b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles128, per, vec);

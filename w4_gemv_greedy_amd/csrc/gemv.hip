@@ -31,9 +31,6 @@
 // widths (every CU streams the same bytes, no trailing second round), short
 // workgroups of 8 R rows elsewhere.
 #include "w4g_internal.h"
-#ifdef W4G_TUNING
-#include <stdlib.h>
-#endif
 
 namespace w4g {
 namespace {
@@ -41,7 +38,6 @@ namespace {
 constexpr int kChunk = 1024;
 constexpr int kThreads = 256;
 constexpr int kHalfWaves = kThreads / 32;
-constexpr int kCUs = 256;  // compute units of the MI355X
 // LDS one workgroup may take here: most of the CU's 160 KiB (above 64 KiB the
 // kernel asks for it with hipFuncSetAttribute); one such workgroup per CU still
 // streams faster than the register-staged variant (measured: down at B=4,
@@ -595,13 +591,7 @@ hipError_t launch_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t
 // Groups of R rows per half wave in the short layout: two (32-row workgroups
 // for R = 2; measured on the vocabulary-wide head at B = 1 on three GPUs: as
 // fast as one group or up to 5% faster, and half the fused head's records).
-int short_groups() {
-#ifdef W4G_TUNING
-  const char* k = getenv("W4G_SM");
-  if (k && atoi(k) > 0) return atoi(k);
-#endif
-  return 2;
-}
+int short_groups() { return 2; }
 
 template <int B, int R, int P, bool AM, int BITS = 4>
 hipError_t launch_short(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
@@ -617,7 +607,8 @@ hipError_t launch_short(const uint32_t* wq, const uint16_t* scales, const uint16
 // wave, else 16 half waves striding through the share, R rows per item.
 // (Launch bounds: 640 threads for shares of at most 20 groups of R rows, one
 // group per half wave; else 512 threads, 16 half waves striding.)
-int64_t per_cu_rows(int64_t N) { return (N + kCUs - 1) / kCUs; }
+int64_t per_cu_rows(int64_t N, int cus) { return (N + cus - 1) / cus; }
+int64_t per_cu_rows(int64_t N) { return per_cu_rows(N, cu_count()); }
 
 template <int R, int P, int BITS = 4, int B = 1, bool AM = false>
 hipError_t launch_per_cu(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
@@ -637,7 +628,9 @@ hipError_t launch_per_cu(const uint32_t* wq, const uint16_t* scales, const uint1
 
 // The layer widths (a CU's share below 512 rows) take the per-CU layout at
 // B = 1; the vocabulary-wide head keeps the short workgroups there.
-bool b1_per_cu(int64_t N) { return per_cu_rows(N) < 2 * 16 * 16; }
+// (keyed on the MI355X's CU count whatever the device, so that the workspace
+// bound of the fused head, computed with kMaxCUs, holds on any device)
+bool b1_per_cu(int64_t N) { return per_cu_rows(N, kMaxCUs) < 2 * 16 * 16; }
 
 template <int B, int R, bool AM>
 hipError_t launch_regs(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
@@ -669,24 +662,6 @@ hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
     }
   }
   if (B == 1) {
-#ifdef W4G_TUNING
-    const char* knob = AM ? nullptr : getenv(per_cu_rows(N) >= 2 * 16 * 16 ? "W4G_CUH" : "W4G_CU");
-    if (knob) {
-      switch (atoi(knob)) {
-        case 0: break;  // the short-workgroup layout below
-        case 14: return launch_per_cu<1, 4>(wq, scales, biases, x, y, N, K, stream);
-        case 16: return launch_per_cu<1, 6>(wq, scales, biases, x, y, N, K, stream);
-        case 18: return launch_per_cu<1, 8>(wq, scales, biases, x, y, N, K, stream);
-        case 22: return launch_per_cu<2, 2>(wq, scales, biases, x, y, N, K, stream);
-        case 23: return launch_per_cu<2, 3>(wq, scales, biases, x, y, N, K, stream);
-        case 24: return launch_per_cu<2, 4>(wq, scales, biases, x, y, N, K, stream);
-        default: break;
-      }
-      if (atoi(knob) == 0)
-        return few_rows(N) ? launch_short<1, 1, 4, false>(wq, scales, biases, x, y, rec, N, K, stream)
-                           : launch_short<1, 2, 2, false>(wq, scales, biases, x, y, rec, N, K, stream);
-    }
-#endif
     // measured in the decode sweep
     if (b1_per_cu(N)) return launch_per_cu<1, 4, 4, 1, AM>(wq, scales, biases, x, y, N, K, stream, rec);
     return few_rows(N) ? launch_short<1, 1, 4, AM>(wq, scales, biases, x, y, rec, N, K, stream)
@@ -749,16 +724,28 @@ hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_
   return dispatch<false>(wq, scales, biases, x, y, nullptr, B, N, K, force_regs, stream);
 }
 
-int64_t gemv_argmax_records(int B, int64_t N, int64_t K) {
-  if (gemv_auto_family(N, K) == 2) return gemv_mfma_argmax_records(B, N, K);
+namespace {
+// the workgroups of the layout dispatch() launches on a device with `cus`
+// compute units, one record each
+int64_t valu_records(int B, int64_t N, int64_t K, int cus) {
   if (use_regs(B, K, false)) {
     const int R = regs_rows(B);
     return (N + 2 * R - 1) / (2 * R);
   }
-  // the workgroups of the layout dispatch() launches, one record each
-  const int64_t rpw = (B >= 2 || b1_per_cu(N)) ? per_cu_rows(N)
+  const int64_t rpw = (B >= 2 || b1_per_cu(N)) ? per_cu_rows(N, cus)
                                                : (int64_t)kHalfWaves * (few_rows(N) ? 1 : 2) * short_groups();
   return (N + rpw - 1) / rpw;
+}
+}  // namespace
+
+int64_t gemv_argmax_records(int B, int64_t N, int64_t K) {
+  if (gemv_auto_family(N, K) == 2) return gemv_mfma_argmax_records(B, N, K, cu_count());
+  return valu_records(B, N, K, cu_count());
+}
+
+int64_t gemv_argmax_records_max(int B, int64_t N, int64_t K) {
+  if (gemv_auto_family(N, K) == 2) return gemv_mfma_argmax_records(B, N, K, kMaxCUs);
+  return valu_records(B, N, K, kMaxCUs);
 }
 
 hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,

@@ -688,11 +688,12 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cuk_kernel(
   }
 }
 
-constexpr int kCUs = 256;                  // compute units of the MI355X
 constexpr int kMaxBatch = 8;               // decode batch rows at most
 constexpr size_t kCuMaxLds = 152 * 1024;   // dynamic LDS asked for (of 160 KiB per CU)
 
-int64_t cu_rows(int64_t N) { return (N + kCUs - 1) / kCUs; }
+// rows per workgroup of the one-workgroup-per-CU layout on this device
+int64_t cu_rows(int64_t N, int cus) { return (N + cus - 1) / cus; }
+int64_t cu_rows(int64_t N) { return cu_rows(N, cu_count()); }
 int cu_waves(int64_t K) {
   const int64_t NI = ((K >> 6) + 1) >> 1;
   return NI < kCuMaxWaves ? (int)NI : kCuMaxWaves;
@@ -793,10 +794,10 @@ hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* scales, const ui
   return launch<false>(wq, scales, biases, x, y, nullptr, B, N, K, step, stream);
 }
 
-int64_t gemv_mfma_argmax_records(int B, int64_t N, int64_t K) {
+int64_t gemv_mfma_argmax_records(int B, int64_t N, int64_t K, int cus) {
   (void)B;
   (void)K;
-  return (N + cu_rows(N) - 1) / cu_rows(N);
+  return (N + cu_rows(N, cus) - 1) / cu_rows(N, cus);
 }
 
 hipError_t launch_gemv_mfma_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,

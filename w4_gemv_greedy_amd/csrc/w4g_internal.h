@@ -10,6 +10,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// Workgroups of the one-workgroup-per-CU layouts: the current device's compute
+// unit count (queried once per device), at most kMaxCUs, the MI355X's 256.  A
+// layout only decides which workgroup computes which rows; no result depends on
+// it.  Workspace sizes are computed with kMaxCUs, an upper bound for any device.
+constexpr int kMaxCUs = 256;
+int cu_count();
+
 // Kernel launchers.  Arguments are already validated; each returns the
 // hipError_t of its launch(es).
 hipError_t launch_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
@@ -53,12 +60,14 @@ hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const 
                               const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                               hipStream_t stream);
 int64_t gemv_argmax_records(int B, int64_t N, int64_t K);
+// An upper bound of gemv_argmax_records on any device (for workspace sizes).
+int64_t gemv_argmax_records_max(int B, int64_t N, int64_t K);
 // The matrix-core family's epilogue variant: one record per workgroup (per CU,
 // or per 32 rows where the activations are staged in stages).
 hipError_t launch_gemv_mfma_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                                    const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                                    hipStream_t stream);
-int64_t gemv_mfma_argmax_records(int B, int64_t N, int64_t K);
+int64_t gemv_mfma_argmax_records(int B, int64_t N, int64_t K, int cus);
 
 constexpr int kArgmaxBlock = 1024;  // ids per pass-1 record
 constexpr uint32_t kArgmaxFlag = 0x80000000u;  // non-finite bit of a record's id word
