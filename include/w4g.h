@@ -78,6 +78,7 @@ extern "C" {
 #define W4G_EDTYPE 5      /* unknown logits dtype or op code */
 #define W4G_ELAUNCH 6     /* the HIP runtime refused a launch */
 #define W4G_EALIAS 7      /* an output overlaps an input or the workspace */
+#define W4G_ESCRATCH 8    /* the sizes need more than the library's static scratch */
 
 /* logits dtypes */
 #define W4G_F32 0
@@ -252,6 +253,24 @@ int vocab_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int
 int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                     const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N,
                     int64_t K, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qmm_gemv_argmax for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without a workspace, the same results bit for bit (logits and
+ * ids).  The per-workgroup records live in a static device array of the
+ * library, 1 MiB (131,072 records) on each GPU the library runs on, held until
+ * the process ends; sizes that need more, B * (records per batch row) above
+ * 131,072 (qmm_workspace_bytes(W4G_OP_GEMV_ARGMAX, B, N, K) / 8), return
+ * W4G_ESCRATCH before any launch.  The call allocates and frees nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on different streams, or from several threads) race and may return
+ * wrong ids; order them on one stream.  Nothing in the array needs clearing:
+ * each call writes every record it reads.
+ */
+int qmm_gemv_argmax_noalloc(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                            const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N,
+                            int64_t K, void* stream);
 
 /*
  * Top two of each logit row: the winner and the runner-up of the argmax's own

@@ -51,6 +51,7 @@ def test_constants_match_header(lib):
     for k, v in (("W4G_OK", _lib.OK), ("W4G_EINVAL_PTR", _lib.EINVAL_PTR), ("W4G_ESHAPE", _lib.ESHAPE),
                  ("W4G_EALIGN", _lib.EALIGN), ("W4G_EWORKSPACE", _lib.EWORKSPACE),
                  ("W4G_EDTYPE", _lib.EDTYPE), ("W4G_ELAUNCH", _lib.ELAUNCH), ("W4G_EALIAS", _lib.EALIAS),
+                 ("W4G_ESCRATCH", _lib.ESCRATCH),
                  ("W4G_F32", _lib.F32), ("W4G_BF16", _lib.BF16), ("W4G_OP_GEMV", _lib.OP_GEMV),
                  ("W4G_OP_GEMM", _lib.OP_GEMM), ("W4G_OP_ARGMAX", _lib.OP_ARGMAX),
                  ("W4G_OP_GEMV_ARGMAX", _lib.OP_GEMV_ARGMAX), ("W4G_OP_ARGMAX_TOP2", _lib.OP_ARGMAX_TOP2),
@@ -60,7 +61,7 @@ def test_constants_match_header(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         msg = lib.w4g_status_string(s)
         assert msg and msg != b"unknown status"
     assert lib.w4g_status_string(99) == b"unknown status"
@@ -189,6 +190,31 @@ def test_gemv_argmax_rejects(lib):
     assert call(ids=WQ + 64) == _lib.EALIAS
     assert call(ws=Y) == _lib.EALIAS
     assert call(ids=WS) == _lib.EALIAS
+
+
+def test_gemv_argmax_noalloc_rejects(lib):
+    """The no-allocation head validates like qmm_gemv_argmax, and refuses sizes
+    whose records exceed its 1 MiB static scratch, all before any HIP call."""
+    call = lambda **k: lib.qmm_gemv_argmax_noalloc(k.get("wq", WQ), SC, BI, X, k.get("lg", Y),
+                                                   k.get("ids", IDS), k.get("B", 2), k.get("N", 5000),
+                                                   k.get("K", 1024), None)
+    assert call(wq=None) == _lib.EINVAL_PTR
+    assert call(ids=None) == _lib.EINVAL_PTR
+    assert call(B=0) == _lib.ESHAPE
+    assert call(B=9) == _lib.ESHAPE
+    assert call(K=1000) == _lib.ESHAPE
+    assert call(lg=Y + 4) == _lib.EALIGN
+    assert call(ids=IDS + 2) == _lib.EALIGN
+    assert call(lg=X) == _lib.EALIAS
+    assert call(ids=WQ + 64) == _lib.EALIAS
+    # records beyond 131,072: the B = 1 head in 32-row workgroups above 4.19 M rows,
+    # and x staged in registers (4 rows per workgroup) at B = 8 over 300,000 rows
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 5_000_000, 64) > (1 << 20)
+    assert call(B=1, N=5_000_000, K=64) == _lib.ESCRATCH
+    assert call(B=8, N=300_000, K=17408) == _lib.ESCRATCH
+    # the full vocabulary head fits at every batch size
+    for B in range(1, 9):
+        assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, B, 248320, 5120) <= (1 << 20)
 
 
 def test_top2_rejects(lib):

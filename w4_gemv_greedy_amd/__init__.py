@@ -20,7 +20,8 @@ from ._lib import (BF16, F32, GEMV_AUTO, GEMV_MFMA, GEMV_MFMA_STEP, GEMV_VALU, G
                    OP_ARGMAX, OP_ARGMAX_TOP2, OP_GEMM, OP_GEMV, OP_GEMV_ARGMAX, SENTINEL,
                    W4GError)
 
-__all__ = ["qmm_gemv", "qmm_gemm", "qmm_gemv_argmax", "vocab_argmax", "vocab_argmax_top2",
+__all__ = ["qmm_gemv", "qmm_gemm", "qmm_gemv_argmax", "qmm_gemv_argmax_noalloc", "vocab_argmax",
+           "vocab_argmax_top2",
            "workspace_bytes", "SENTINEL", "W4GError"]
 
 
@@ -208,6 +209,31 @@ def qmm_gemv_argmax(wq, scales, biases, x, logits=None, ids=None, workspace=None
                                  rows, N, K, ws.data_ptr(), nbytes, _stream(wq))
     _lib.check("qmm_gemv_argmax", status)
     return ids, logits
+
+
+def qmm_gemv_argmax_noalloc(wq, scales, biases, x, ids, logits=None):
+    """qmm_gemv_argmax for callers that cannot allocate: the caller passes every
+    output (ids [B] int32/uint32, logits [B][N] fp32 or None to skip them); the
+    library keeps the per-workgroup records in a static device array of its
+    own (1 MiB per GPU), so nothing is allocated at any level.  Calls that
+    overlap on one GPU race (one static array per GPU).  Returns ids."""
+    torch = _torch()
+    N, K = _check_qmm(wq, scales, biases, x)
+    rows = x.shape[0]
+    if not 1 <= rows <= MAX_GEMV_BATCH:
+        raise ValueError(f"qmm_gemv_argmax_noalloc takes 1..{MAX_GEMV_BATCH} rows")
+    _need(ids, "ids", (torch.int32, torch.uint32), 1, wq.device)
+    if ids.shape[0] != rows:
+        raise ValueError("ids must have one entry per row")
+    if logits is not None:
+        _need(logits, "logits", (torch.float32,), 2, wq.device)
+        if tuple(logits.shape) != (rows, N):
+            raise ValueError(f"logits must be [{rows}][{N}]")
+    status = _lib.load().qmm_gemv_argmax_noalloc(
+        wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
+        logits.data_ptr() if logits is not None else None, ids.data_ptr(), rows, N, K, _stream(wq))
+    _lib.check("qmm_gemv_argmax_noalloc", status)
+    return ids
 
 
 def vocab_argmax(logits, ids=None, workspace=None, vocab=None):

@@ -78,6 +78,32 @@ int cu_count() {
 
 }  // namespace w4g
 
+namespace {
+
+// The fused head's records for callers that cannot allocate: a file-scope
+// device array (zero at load, one copy per GPU, kept until the process ends).
+// Host code never passes `scratch` itself to a kernel (on the host the name is
+// a stand-in, not a device address): each device's address is taken once with
+// hipGetSymbolAddress, with that device current, and kept.
+constexpr int64_t kScratchRecords = 131072;  // 1 MiB of (value, id | flag) records
+__device__ __align__(256) uint2 scratch[kScratchRecords];
+
+std::atomic<uintptr_t> g_scratch_ptr[64];
+
+// this device's address of `scratch`, or 0 if it cannot be had
+uint2* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  uintptr_t p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return reinterpret_cast<uint2*>(p);
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  g_scratch_ptr[dev].store(reinterpret_cast<uintptr_t>(q), std::memory_order_release);
+  return reinterpret_cast<uint2*>(q);
+}
+
+}  // namespace
+
 extern "C" {
 
 int w4g_abi_version(void) { return W4G_ABI_VERSION; }
@@ -92,6 +118,7 @@ const char* w4g_status_string(int status) {
     case W4G_EDTYPE: return "unknown dtype or op";
     case W4G_ELAUNCH: return "the HIP runtime refused a launch";
     case W4G_EALIAS: return "an output overlaps an input or the workspace";
+    case W4G_ESCRATCH: return "the sizes need more than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -245,6 +272,17 @@ int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
   if (rc) return rc;
   return run_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, reinterpret_cast<uint2*>(workspace),
                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int qmm_gemv_argmax_noalloc(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                            const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N,
+                            int64_t K, void* stream) {
+  const int rc = check_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, nullptr, 0);
+  if (rc) return rc;
+  if (gemv_argmax_bytes(B, N, K) > (size_t)kScratchRecords * sizeof(uint2)) return W4G_ESCRATCH;
+  uint2* rec = scratch_ptr();
+  if (!rec) return W4G_ELAUNCH;
+  return run_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, rec, reinterpret_cast<hipStream_t>(stream));
 }
 
 int vocab_argmax_top2(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
