@@ -410,9 +410,10 @@ def main():
 
 
 def ceilings(torch, layers, dev, timed):
-    """Measured ceilings: a read-only HBM stream of each product's bytes (graph of
-    16 launches cycling over enough copies to defeat the 256 MB cache; the best of
-    three launch shapes), a matrix-core loop with no memory traffic, and torch's
+    """Measured ceilings: a read-only HBM stream of each product's bytes, with plain
+    and with non-temporal loads (a graph of launches cycling over enough copies to
+    defeat the 256 MB cache; the best of three launch shapes), a matrix-core loop
+    with no memory traffic, and torch's
     bf16 matmul (hipBLASLt) on weights dequantized to bf16 (2 bytes per weight
     against 0.5625), for the 512-row prompt shapes."""
     import ctypes
@@ -422,7 +423,7 @@ def ceilings(torch, layers, dev, timed):
         return None
     lib = ctypes.CDLL(hip_build.CEILING_LIB)
     P, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
-    lib.w4g_ceiling_read.argtypes = [P, SZ, I, I, I, P, P]
+    lib.w4g_ceiling_read.argtypes = [P, SZ, I, I, I, I, P, P]
     lib.w4g_ceiling_read.restype = I
     lib.w4g_ceiling_mfma.argtypes = [I, I, P, P]
     lib.w4g_ceiling_mfma.restype = I
@@ -438,21 +439,23 @@ def ceilings(torch, layers, dev, timed):
                                  ("lm_head", gemv_bytes(VOCAB, HIDDEN, 1), 2)):
         nb = nbytes // 16 * 16
         bufs = [torch.full((nb,), c, dtype=torch.uint8, device=dev) for c in range(copies)]
-        best = None
         launches = max(16, copies)  # every copy once per replay
-        for blocks, threads, u in ((256, 1024, 4), (2048, 256, 4), (4096, 256, 2)):
-            def run(blocks=blocks, threads=threads, u=u):
-                for i in range(launches):
-                    st = lib.w4g_ceiling_read(bufs[i % copies].data_ptr(), nb, blocks, threads, u,
-                                              sink.data_ptr(), stream())
-                    if st != 0:
-                        raise RuntimeError(f"w4g_ceiling_read: hip error {st}")
-            ms, _ = timed(run, 10, 2, True)
-            us = ms * 1e3 / launches
-            if best is None or us < best[0]:
-                best = (us, f"{blocks}x{threads}, {u} loads in flight")
-        out["hbm_read"][name] = {"bytes": nb, "us": round(best[0], 2),
-                                 "GBps": round(nb / (best[0] * 1e-6) / 1e9, 1), "launch": best[1]}
+        entry = {"bytes": nb}
+        for nt, key in ((0, "plain"), (1, "nontemporal")):
+            best = None
+            for blocks, threads, u in ((256, 1024, 4), (2048, 256, 4), (4096, 256, 2)):
+                def run(blocks=blocks, threads=threads, u=u, nt=nt):
+                    for i in range(launches):
+                        st = lib.w4g_ceiling_read(bufs[i % copies].data_ptr(), nb, blocks, threads, u, nt,
+                                                  sink.data_ptr(), stream())
+                        if st != 0:
+                            raise RuntimeError(f"w4g_ceiling_read: hip error {st}")
+                ms, _ = timed(run, 10, 2, True)
+                us = ms * 1e3 / launches
+                if best is None or us < best[0]:
+                    best = (us, f"{blocks}x{threads}, {u} loads in flight")
+            entry[key] = {"us": round(best[0], 2), "GBps": round(nb / (best[0] * 1e-6) / 1e9, 1), "launch": best[1]}
+        out["hbm_read"][name] = entry
         del bufs
     torch.cuda.empty_cache()
 

@@ -3,7 +3,7 @@
 // benchmark only).
 //
 // w4g_ceiling_read: a read-only stream of `bytes` (a multiple of 16) with
-// 16-byte vector loads; workgroup b reads the contiguous slice
+// 16-byte vector loads, plain or non-temporal; workgroup b reads the contiguous slice
 // [b * per, (b + 1) * per), its threads striding through it with U loads in
 // flight each.  Nothing is written unless the XOR of everything read equals a
 // fixed constant (never, for the benchmark's buffers), so the loads cannot be
@@ -22,7 +22,9 @@ typedef float f32x16_c __attribute__((ext_vector_type(16)));
 
 namespace {
 
-template <int U>
+typedef uint32_t u32x4_c __attribute__((ext_vector_type(4)));
+
+template <int U, bool NT>
 __global__ __launch_bounds__(1024) void read_kernel(const uint4* __restrict__ p, int64_t n16, int64_t per16,
                                                     uint32_t* __restrict__ sink) {
   const int64_t beg = (int64_t)blockIdx.x * per16;
@@ -33,7 +35,12 @@ __global__ __launch_bounds__(1024) void read_kernel(const uint4* __restrict__ p,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t j = i + (int64_t)u * blockDim.x;
-      v[u] = j < end ? p[j] : make_uint4(0u, 0u, 0u, 0u);
+      if (NT) {
+        const u32x4_c r = __builtin_nontemporal_load(reinterpret_cast<const u32x4_c*>(p) + (j < end ? j : beg));
+        v[u] = j < end ? make_uint4(r[0], r[1], r[2], r[3]) : make_uint4(0u, 0u, 0u, 0u);
+      } else {
+        v[u] = j < end ? p[j] : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -70,19 +77,23 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict_
 extern "C" {
 
 // Returns a hipError_t value (0 on success); 1 (hipErrorInvalidValue) for a
-// bad size or launch shape.
+// bad size or launch shape.  nontemporal: 0 plain loads, 1 non-temporal loads.
 int w4g_ceiling_read(const void* p, size_t bytes, int blocks, int threads, int loads_in_flight,
-                     uint32_t* sink, void* stream) {
+                     int nontemporal, uint32_t* sink, void* stream) {
   if (!p || !sink || bytes % 16 || blocks < 1 || threads < 64 || threads > 1024 || threads % 64)
     return (int)hipErrorInvalidValue;
   const int64_t n16 = (int64_t)(bytes / 16);
   const int64_t per16 = (n16 + blocks - 1) / blocks;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint4* q = reinterpret_cast<const uint4*>(p);
-  switch (loads_in_flight) {
-    case 2: hipLaunchKernelGGL(read_kernel<2>, dim3(blocks), dim3(threads), 0, s, q, n16, per16, sink); break;
-    case 4: hipLaunchKernelGGL(read_kernel<4>, dim3(blocks), dim3(threads), 0, s, q, n16, per16, sink); break;
-    case 8: hipLaunchKernelGGL(read_kernel<8>, dim3(blocks), dim3(threads), 0, s, q, n16, per16, sink); break;
+  const int sel = loads_in_flight * 2 + (nontemporal ? 1 : 0);
+  switch (sel) {
+#define W4G_READ(U, NT)                                                                                 \
+    case U * 2 + NT:                                                                                    \
+      hipLaunchKernelGGL((read_kernel<U, NT>), dim3(blocks), dim3(threads), 0, s, q, n16, per16, sink); \
+      break;
+    W4G_READ(2, 0) W4G_READ(2, 1) W4G_READ(4, 0) W4G_READ(4, 1) W4G_READ(8, 0) W4G_READ(8, 1)
+#undef W4G_READ
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

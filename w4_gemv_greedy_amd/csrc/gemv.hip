@@ -21,7 +21,7 @@
 //   (i, 15 - i), half mirror (i, 7 - i), and quad swaps (i, i ^ 2), (i, i ^ 1).
 //
 // Memory: a half wave owns whole rows; in each chunk lane l reads one 16-byte
-// code vector at byte 16l, so a wave-wide load covers 512 contiguous bytes of
+// code vector at byte 16l (a non-temporal load: the codes are read once), so a wave-wide load covers 512 contiguous bytes of
 // each of two rows.  A work item is one chunk of R consecutive rows; P items
 // are in flight while one is consumed.  The activations are paired and summed
 // once per workgroup into LDS, laid out so that a half wave's reads are
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) it.w[r][v] = pw[r][vo + v];
+      for (int v = 0; v < VPL; ++v) it.w[r][v] = ld_stream(pw[r] + vo + v);
       it.s[r] = ps[r][go];
       it.b[r] = pb[r][go];
     }
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(64) void gemv_valu_regs_kernel(const uint32_t* __re
       uint32_t sv[R], bv[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        wv[r] = *reinterpret_cast<const uint4*>(wq + rows[r] * K8 + (kb >> 3));
+        wv[r] = ld_stream(reinterpret_cast<const uint4*>(wq + rows[r] * K8 + (kb >> 3)));
         sv[r] = scales[rows[r] * G + (kb >> 6)];
         bv[r] = biases[rows[r] * G + (kb >> 6)];
       }

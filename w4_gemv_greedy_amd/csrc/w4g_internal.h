@@ -69,6 +69,26 @@ hipError_t launch_gemv_mfma_argmax(const uint32_t* wq, const uint16_t* scales, c
                                    hipStream_t stream);
 int64_t gemv_mfma_argmax_records(int B, int64_t N, int64_t K, int cus);
 
+// Loads of the packed codes, the stream that is read exactly once per call:
+// non-temporal, so the lines pass through the caches with the streaming
+// policy.  Measured on MI355X, a read-only stream of 2 GiB moves 7.0-7.1 TB/s
+// with non-temporal 16-byte loads against 6.0-6.3 TB/s with plain ones, and
+// the vector-ALU decode sweep runs 8% faster with them.  (The scale and bias
+// tables keep plain loads: a row's table line is read in pieces, one per
+// 1024-element chunk, and with the streaming policy the vocabulary-wide head
+// ran slower; the matrix-core decode keeps plain loads too: it ran slower
+// with non-temporal ones.)
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 ld_stream(const uint2* p) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v[0], v[1]);
+}
+
 constexpr int kArgmaxBlock = 1024;  // ids per pass-1 record
 constexpr uint32_t kArgmaxFlag = 0x80000000u;  // non-finite bit of a record's id word
 
