@@ -208,10 +208,11 @@ def test_gemv_argmax_noalloc_rejects(lib):
     assert call(lg=X) == _lib.EALIAS
     assert call(ids=WQ + 64) == _lib.EALIAS
     # records beyond 131,072: the B = 1 head in 32-row workgroups above 4.19 M rows,
-    # and x staged in registers (4 rows per workgroup) at B = 8 over 300,000 rows
+    # and x staged in registers (4 rows per workgroup: K = 40,960 holds one row of
+    # x in LDS, not two) at B = 8 over 600,000 rows
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 5_000_000, 64) > (1 << 20)
     assert call(B=1, N=5_000_000, K=64) == _lib.ESCRATCH
-    assert call(B=8, N=300_000, K=17408) == _lib.ESCRATCH
+    assert call(B=8, N=600_000, K=40960) == _lib.ESCRATCH
     # the full vocabulary head fits at every batch size
     for B in range(1, 9):
         assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, B, 248320, 5120) <= (1 << 20)
@@ -245,8 +246,9 @@ def test_workspace_sizes(lib):
     # fused head: one record per product workgroup and batch row, in the layout
     # of qmm_gemv's own choice, the vector-ALU family for every shape: 32 rows
     # per workgroup for the vocabulary-wide head at B = 1, one workgroup per CU
-    # where x fits in LDS otherwise, 4 rows per 64-lane workgroup where x is
-    # staged in registers (B * 2.125 * K bytes above 152 KiB: down from B = 5)
+    # where x fits in LDS, and also where a batch too large for it is cut into
+    # parts that fit (down from B = 5: two parts), 4 rows per 64-lane workgroup
+    # where not even two rows of x fit (x staged in registers)
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 248320, 5120) == 7760 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 5120, 5120) == 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 4, 248320, 5120) == 4 * 256 * 8
@@ -255,10 +257,11 @@ def test_workspace_sizes(lib):
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 2, 5120, 17408) == 2 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 248320, 5120) == 8 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 4, 5120, 17408) == 4 * 256 * 8
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 5, 5120, 17408) == 5 * 1280 * 8
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 5120, 17408) == 8 * 1280 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 5, 5120, 17408) == 5 * 256 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 5120, 17408) == 8 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 3, 300, 73728) == 3 * 75 * 8
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 9000, 10240) == 8 * 2250 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 9000, 10240) == 8 * 250 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 600000, 40960) == 8 * 150000 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 9, 248320, 5120) == size_max
     assert lib.qmm_workspace_bytes(7, 1, 1, 64) == size_max
 

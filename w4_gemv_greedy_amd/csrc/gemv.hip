@@ -385,23 +385,38 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
         }
       }
       if (++cc == C) {
+        // every lane holds every sum; lane bb (< B) takes batch row bb's, so
+        // the stores and the argmax fold of a group are one branch, not one per
+        // (row, batch row)
+        float mine[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
           for (int bb = 0; bb < B; ++bb) {
             const float v = half_wave_sum(acc[r][bb]);
-            if (lane == 0 && crow + r < wg_end && (!AM || y != nullptr)) y[(int64_t)bb * N + crow + r] = v;
-            if constexpr (AM) {
-              if (lane == 0 && crow + r < wg_end) {
-                const uint32_t u = __float_as_uint(v);
-                if (!finite_bits(u))
-                  __hip_atomic_fetch_or(&s_bad, 1u << bb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                else
-                  __hip_atomic_fetch_max(&s_best[bb], cand(u, (uint32_t)(crow + r)), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+            mine[r] = bb == 0 ? v : (lane == bb ? v : mine[r]);
+            acc[r][bb] = 0.0f;
+          }
+        }
+        if (lane < B) {
+          uint64_t best = 0;
+          bool bad = false;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if (crow + r < wg_end) {
+              if (!AM || y != nullptr) y[(int64_t)lane * N + crow + r] = mine[r];
+              if constexpr (AM) {
+                const uint32_t u = __float_as_uint(mine[r]);
+                if (!finite_bits(u)) bad = true;
+                else best = umax64(best, cand(u, (uint32_t)(crow + r)));
               }
             }
-            acc[r][bb] = 0.0f;
+          }
+          if constexpr (AM) {
+            // (a candidate word is never 0: every finite value's key is above 0)
+            if (bad) __hip_atomic_fetch_or(&s_bad, 1u << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (best)
+              __hip_atomic_fetch_max(&s_best[lane], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           }
         }
         cc = 0;
@@ -644,10 +659,64 @@ hipError_t launch_regs(const uint32_t* wq, const uint16_t* scales, const uint16_
 
 // The one dispatch both entry points share: the kernel, R and P are functions
 // of (B, N, K) and force_regs only, and the workgroup count follows from them.
+// The largest batch whose activations fit in the shared-memory variant's LDS
+// (0 if not even one row's do).
+int lds_rows(int64_t K) {
+  int b = 0;
+  while (b < 8 && !use_regs(b + 1, K, false)) ++b;
+  return b;
+}
+
+// The per-CU layout for any batch (1..8): R = 2 over more than 40 rows per CU
+// at B >= 2.  Every batch size takes the same workgroups, so the batch can be
+// cut into parts that write their records side by side.
+template <bool AM>
+hipError_t launch_per_cu_any(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                             const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                             hipStream_t stream) {
+  if (B == 1) return launch_per_cu<1, 4, 4, 1, AM>(wq, scales, biases, x, y, N, K, stream, rec);
+  const bool two = per_cu_rows(N) > 40;  // (R = 2 then always strides: 512 threads)
+  switch (B) {
+#define W4G_PER_CU(BB)                                                                               \
+    case BB:                                                                                         \
+      return two ? launch_per_cu<2, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec)       \
+                 : launch_per_cu<1, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec);
+    W4G_PER_CU(2) W4G_PER_CU(3) W4G_PER_CU(4) W4G_PER_CU(5) W4G_PER_CU(6) W4G_PER_CU(7) W4G_PER_CU(8)
+#undef W4G_PER_CU
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Where the activations of the whole batch do not fit in LDS but those of two
+// rows or more do (down_proj, K = 17,408, from B = 5), the batch is cut into
+// the fewest equal parts that fit, each a launch of the per-CU layout: the
+// weights are read once per part, which measured faster than the
+// register-staged variant (down at B = 8: two parts of 4 rows, about 40 us,
+// against 70 us).  Every row has the bits it has alone, in any part.
+int batch_parts(int B, int64_t K) {
+  const int b = lds_rows(K);
+  return b >= 2 && B > b ? (B + b - 1) / b : 1;
+}
+
+// The one dispatch both entry points share: the kernel, R and P are functions
+// of (B, N, K) and force_regs only, and the workgroup count follows from them.
 template <bool AM>
 hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                     const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                     bool force_regs, hipStream_t stream) {
+  const int parts = force_regs ? 1 : batch_parts(B, K);
+  if (parts > 1) {
+    const int64_t grid = (N + per_cu_rows(N) - 1) / per_cu_rows(N);
+    for (int p = 0, b0 = 0; p < parts; ++p) {
+      const int bp = B / parts + (p < B % parts ? 1 : 0);
+      const hipError_t e = launch_per_cu_any<AM>(wq, scales, biases, x + (int64_t)b0 * K,
+                                                 y ? y + (int64_t)b0 * N : nullptr,
+                                                 rec ? rec + (int64_t)b0 * grid : nullptr, bp, N, K, stream);
+      if (e != hipSuccess) return e;
+      b0 += bp;
+    }
+    return hipSuccess;
+  }
   if (use_regs(B, K, force_regs)) {
     switch (B) {
       case 1: return launch_regs<1, 4, AM>(wq, scales, biases, x, y, rec, N, K, stream);
@@ -670,16 +739,7 @@ hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
   // B >= 2: the per-CU layout too, also for the head (measured: down at B = 4
   // 36 -> 22 us, gate-up at B = 8 90 -> 47 us, lm_head at B = 8 581 -> 322 us),
   // two rows per item when a CU's share exceeds 40 rows
-  const bool two = per_cu_rows(N) > 40;  // (R = 2 then always strides: 512 threads)
-  switch (B) {
-#define W4G_PER_CU(BB)                                                                               \
-    case BB:                                                                                         \
-      return two ? launch_per_cu<2, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec)       \
-                 : launch_per_cu<1, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec);
-    W4G_PER_CU(2) W4G_PER_CU(3) W4G_PER_CU(4) W4G_PER_CU(5) W4G_PER_CU(6) W4G_PER_CU(7) W4G_PER_CU(8)
-#undef W4G_PER_CU
-    default: return hipErrorInvalidValue;
-  }
+  return launch_per_cu_any<AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
 }
 
 // 2- and 8-bit codes: the shared-memory variant only (the caller checks that x
@@ -728,6 +788,7 @@ namespace {
 // the workgroups of the layout dispatch() launches on a device with `cus`
 // compute units, one record each
 int64_t valu_records(int B, int64_t N, int64_t K, int cus) {
+  if (batch_parts(B, K) > 1) return (N + per_cu_rows(N, cus) - 1) / per_cu_rows(N, cus);
   if (use_regs(B, K, false)) {
     const int R = regs_rows(B);
     return (N + 2 * R - 1) / (2 * R);
