@@ -127,8 +127,10 @@ int qmm_gemv(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
  * of step 2) and the B70 page serves an INT8 LM head with bf16 scales
  * (b70-optimization-lab, "Reproduce Qwen3.6 27B AutoRound Bring-Up", current
  * best profile); reading: the same affine group-64 format at those widths.
- * Widths 2 and 8 run on the vector ALUs with x staged in LDS, so they need
- * B * 2.125 * K bytes <= 152 KiB (else W4G_ESHAPE).  Order per row, K only:
+ * Widths 2 and 8 run on the vector ALUs with x staged in LDS, so one row of x
+ * must fit: 2.125 * K bytes <= 152 KiB, K <= 72,704 (else W4G_ESHAPE); a batch
+ * whose rows do not fit together runs in parts that do (each reading the
+ * weights once), with the same bits per row.  Order per row, K only:
  * as qmm_gemv's, with each lane's 32-element segment taken as its code words
  * in order; 2-bit: within a word fields (j, j + 8) form one bf16 pair
  * (128 + q), j ascending; 8-bit: a code is its two nibbles, Dl over the low
@@ -157,9 +159,11 @@ int qmm_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* bi
  * the pages' kernel keeps the K split of the whole width for a rank holding a
  * slice (TensorFold PR #1433, step-1 description: chunks(n, whole)).  Today
  * that choice is the vector-ALU family for every (K, whole).  The vector-ALU
- * family stages x in LDS when B * 2.125 * K bytes fit in 152 KiB and in
- * registers otherwise; W4G_GEMV_VALU_REGS forces the register variant (for
- * checking that both variants give the same bits).
+ * family stages x in LDS when B * 2.125 * K bytes fit in 152 KiB; a batch
+ * whose x does not fit runs in parts of two rows or more that do (the weights
+ * read once per part), and x is staged in registers where not even two rows
+ * fit; W4G_GEMV_VALU_REGS forces the register variant (for checking that all
+ * of these give the same bits).
  * The matrix-core family (W4G_GEMV_MFMA) feeds the codes to the matrix cores
  * as exact bf16 values 128 + q; per 64-group it adds s*P_g and
  * (b - 128 s)*X_g in fp32 (P_g the matrix-core group product from zero, X_g

@@ -118,9 +118,10 @@ def test_gemv_bits_rejects(lib):
     # an 8-bit table is twice a 4-bit one: y just past the 4-bit extent still overlaps it
     assert call(y=WQ + 64 * (128 // 8) * 4) == _lib.EALIAS
     assert call(bits=2, y=WQ + 64 * (128 // 16) * 4 - 16) == _lib.EALIAS
-    # x must fit in LDS at widths other than 4: B * 2.125 * K bytes <= 152 KiB
-    assert call(B=8, K=17408) == _lib.ESHAPE
-    assert call(bits=2, B=5, K=17408) == _lib.ESHAPE
+    # one row of x must fit in LDS at widths other than 4 (2.125 * K bytes <= 152 KiB:
+    # K up to 72 chunks of 1024 less one, 72,704); larger batches run in parts
+    assert call(K=73728) == _lib.ESHAPE
+    assert call(bits=2, B=8, K=73728) == _lib.ESHAPE
 
 
 def test_gemm_rejects(lib):

@@ -24,10 +24,9 @@ SHAPES = [(37, 64), (70, 1088), (129, 2048), (300, 5120), (40, 17408), (9477, 10
 
 @pytest.mark.parametrize("bits", [2, 8])
 @pytest.mark.parametrize("N,K", SHAPES)
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8])
 def test_gemv_bits_matches_oracle(N, K, B, bits):
-    if B * 2.125 * K > 152 * 1024:
-        pytest.skip("x does not fit in LDS at this width (W4G_ESHAPE, tested on the CPU)")
+    # (at K = 17,408 from B = 5 the batch runs in two parts whose x fits in LDS)
     if N * K > 2_000_000 and B > 2:
         pytest.skip("large shape: B = 1 and 2 only")
     wq, sc, bi, x = _case(N, K, B, bits, N + K + B)
@@ -36,9 +35,10 @@ def test_gemv_bits_matches_oracle(N, K, B, bits):
     print(f"w{bits} N={N} K={K} B={B}: normwise {e:.2e}")
 
 
+@pytest.mark.parametrize("K", [5120, 17408])
 @pytest.mark.parametrize("bits", [2, 8])
-def test_gemv_bits_batch_invariance_and_determinism(bits):
-    wq, sc, bi, x = _case(300, 5120, 8, bits, 5)
+def test_gemv_bits_batch_invariance_and_determinism(bits, K):
+    wq, sc, bi, x = _case(300, K, 8, bits, 5)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
     y8 = down(w4g.qmm_gemv(*W, up_bf16(x), bits=bits))
     y8b = down(w4g.qmm_gemv(*W, up_bf16(x), bits=bits))

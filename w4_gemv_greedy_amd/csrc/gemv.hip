@@ -745,11 +745,11 @@ hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
 // 2- and 8-bit codes: the shared-memory variant only (the caller checks that x
 // fits), with the 4-bit layouts (per CU, short workgroups for the B = 1 head).
 template <int BITS>
-hipError_t dispatch_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                         const uint16_t* x, float* y, int B, int64_t N, int64_t K, hipStream_t stream) {
-  if (use_regs(B, K, false)) return hipErrorInvalidValue;
+hipError_t dispatch_bits_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                             const uint16_t* x, float* y, int B, int64_t N, int64_t K, bool per_cu,
+                             hipStream_t stream) {
   if (B == 1) {
-    if (b1_per_cu(N)) return launch_per_cu<1, 4, BITS>(wq, scales, biases, x, y, N, K, stream);
+    if (per_cu || b1_per_cu(N)) return launch_per_cu<1, 4, BITS>(wq, scales, biases, x, y, N, K, stream);
     return launch_short<1, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
   }
   const bool two = per_cu_rows(N) > 40;
@@ -764,9 +764,28 @@ hipError_t dispatch_bits(const uint32_t* wq, const uint16_t* scales, const uint1
   }
 }
 
+// Other widths run the shared-memory variant only: where the batch's
+// activations do not fit in LDS, the batch is cut into parts that do, as for
+// 4-bit codes (the weights are read once per part; down_proj at K = 17,408
+// takes two parts from B = 5).  The caller checks gemv_bits_fits.
+template <int BITS>
+hipError_t dispatch_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                         const uint16_t* x, float* y, int B, int64_t N, int64_t K, hipStream_t stream) {
+  if (lds_rows(K) < 1) return hipErrorInvalidValue;
+  const int parts = B > lds_rows(K) ? (B + lds_rows(K) - 1) / lds_rows(K) : 1;
+  for (int p = 0, b0 = 0; p < parts; ++p) {
+    const int bp = B / parts + (p < B % parts ? 1 : 0);
+    const hipError_t e = dispatch_bits_lds<BITS>(wq, scales, biases, x + (int64_t)b0 * K, y + (int64_t)b0 * N,
+                                                 bp, N, K, parts > 1, stream);
+    if (e != hipSuccess) return e;
+    b0 += bp;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
-bool gemv_bits_fits(int B, int64_t K) { return !use_regs(B, K, false); }
+bool gemv_bits_fits(int B, int64_t K) { return B >= 1 && lds_rows(K) >= 1; }
 
 hipError_t launch_gemv_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                             const uint16_t* x, float* y, int B, int64_t N, int64_t K, int bits,
