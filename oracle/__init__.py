@@ -32,11 +32,15 @@ SENTINEL = 0xFFFFFFFF
 _libs = {}
 
 
-def build(plant=0, out=None, quiet=True):
-    """Compile the oracle (optionally with planted mistake ``plant``) and return the path."""
+def build(plant=0, out=None, quiet=True, sanitize=False):
+    """Compile the oracle (optionally with planted mistake ``plant``, or with
+    AddressSanitizer and UndefinedBehaviorSanitizer for a checking run) and
+    return the path."""
     out = out or (LIB if plant == 0 else os.path.join(HERE, f"liboracle_plant{plant}.so"))
-    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
-           f"-DW4O_PLANT={int(plant)}", SRC, "-o", out + ".tmp", "-lm"]
+    opt = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all"] if sanitize else ["-O2"]
+    cmd = ["gcc"] + opt + ["-std=c99", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                           f"-DW4O_PLANT={int(plant)}", SRC, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True, capture_output=quiet)
     os.replace(out + ".tmp", out)
     return out
