@@ -2,8 +2,9 @@
 
 One step = 16 layer-equivalents of (o_proj 5120x5120, fused gate-up
 5120 -> 34816, down_proj 17408 -> 5120) W4 g64 products back to back on one
-stream, then the 248,320-row lm_head product and the greedy argmax over the
-full vocabulary.  Every product takes its own pre-generated bf16 input (no
+stream, then the 248,320-row lm_head product (logits written) and the greedy
+argmax over the full vocabulary (qmm_gemv_argmax: the argmax's first pass in
+the product's epilogue).  Every product takes its own pre-generated bf16 input (no
 norm or activation between them; the inputs are seeded synthetic data of the
 model's shapes, the weights seeded synthetic codes, scales and biases).  The
 step is captured once in a HIP graph and replayed.
@@ -311,7 +312,8 @@ def main():
                 torch.empty((Bn, HIDDEN), dtype=torch.float32, device=dev),
                 torch.empty((Bn, VOCAB), dtype=torch.float32, device=dev),
                 torch.empty(Bn, dtype=torch.int32, device=dev),
-                torch.empty(w4g.workspace_bytes(w4g.OP_ARGMAX, Bn, VOCAB, 0), dtype=torch.uint8, device=dev))
+                torch.empty(w4g.workspace_bytes(w4g.OP_GEMV_ARGMAX, Bn, VOCAB, HIDDEN), dtype=torch.uint8,
+                            device=dev))
 
     def make_step(Bn):
         xs, xh = inputs(Bn)
@@ -325,8 +327,9 @@ def main():
                 if not skip_gate_up:
                     w4g.qmm_gemv(g.wq, g.sc, g.bi, xg, yg)
                 w4g.qmm_gemv(d.wq, d.sc, d.bi, xd, yd)
-            w4g.qmm_gemv(head.wq, head.sc, head.bi, xh, logits)
-            w4g.vocab_argmax(logits, ids, ws)
+            # the lm_head product (its logits written) and the greedy argmax, the
+            # argmax's first pass fused into the product
+            w4g.qmm_gemv_argmax(head.wq, head.sc, head.bi, xh, logits, ids, ws)
         return step, ids, logits
 
     def timed(fn, steps, warmup, graph, reps=1):
