@@ -300,8 +300,27 @@ def test_gemm_tile_variants_bitwise():
     assert_close(y_reg[:, cols], oracle.qmm_rows(wq, sc, bi, x, cols), "gemm tile variants")
 
 
+@pytest.mark.parametrize("N,K", [(70, 128), (1000, 384), (333, 1152), (5120, 5120)])
+def test_gemm_short_prompt_kernel(N, K):
+    """Prompts of at most 32 rows over a narrow matrix take the short-prompt
+    kernel (groups dealt to eight waves; 16-row tiles up to 16 rows, 32-row
+    tiles up to 32; G = 2, 6, 18, 80 cover one partial round, a ragged last
+    round and whole rounds).  Their rows must be bitwise the rows of a 40-row
+    prompt, which the tiled loops compute, and match the oracle."""
+    wq, sc, bi, x = _case(N, K, 40, N + 7 * K)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    X = up_bf16(x)
+    y40 = down(w4g.qmm_gemm(*W, X))
+    for m in (1, 5, 16, 17, 32):
+        ym = down(w4g.qmm_gemm(*W, X[:m].contiguous()))
+        assert np.array_equal(ym.view(np.uint32), y40[:m].view(np.uint32)), f"M={m} N={N} K={K}"
+    cols = np.unique(np.concatenate([np.arange(min(N, 40)), np.arange(max(0, N - 40), N),
+                                     np.random.default_rng(3).choice(N, min(N, 64), replace=False)]))
+    assert_close(y40[:, cols], oracle.qmm_rows(wq, sc, bi, x, cols), f"short prompt N={N} K={K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 37, 64), (7, 130, 1088), (130, 256, 1024), (33, 70, 17408),
-                                   (500, 1100, 512)])
+                                   (500, 1100, 512), (16, 1000, 384), (32, 70, 1152)])
 def test_gemm_bf16_store(M, N, K):
     """bf16 output: the fp32 result (itself held to the 2e-3 bar elsewhere) rounded
     to nearest-even, bit for bit as torch's CPU conversion of the fp32 output

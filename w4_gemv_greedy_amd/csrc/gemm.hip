@@ -25,14 +25,17 @@
 // Work split: a pre-pass writes x permuted into the element order of the code
 // expansion, and the exact three-part group sums.  A workgroup of four waves
 // owns a tile of Y; its activations, codes and scales go through LDS one or two
-// groups at a time.  Three main loops share that arithmetic: 128 x 128 tiles
+// groups at a time.  Four main loops share that arithmetic: 128 x 128 tiles
 // (each wave 64 x 64, 2 x 2 matrix-core tiles) with the operands staged
 // through registers (two workgroups per CU) when there are tiles enough for
 // that; 128 x 128 tiles loaded straight into an LDS ring (one workgroup per
 // CU) when fewer; and 64 x 64 tiles (each wave one 32 x 32 matrix-core tile)
-// through a ring of LDS loads for short prompts and small grids.  The bias
-// terms and the store follow the main loop; the result is fp32, or bf16
-// rounded to nearest-even from it.
+// through a ring of LDS loads for short prompts and small grids.  Prompts of
+// at most 32 rows over narrow matrices take a fourth loop that deals each
+// tile's groups to eight waves and passes the group products on through LDS
+// (a tile's K chain would otherwise run on one wave).  The bias terms and the
+// store follow the main loop; the result is fp32, or bf16 rounded to
+// nearest-even from it.
 #include <algorithm>
 
 #include "w4g_internal.h"
@@ -477,7 +480,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 // + 1), so waiting for all but the newest stages' loads completes the oldest.
 // Per output the arithmetic and its order are those of gemm_kernel, whatever
 // the tile: every variant gives the same bits.
-// (the loop choice below is a matter of speed only: the three loops give the
+// (the loop choice below is a matter of speed only: the four loops give the
 // same bits; it is keyed on this device's compute units)
 
 // Buffer load of 16 bytes per lane into LDS at m0 + 16 * lane.
@@ -494,6 +497,12 @@ __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, __amdgpu_buffe
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// Workgroup barrier for data exchanged through LDS by the waves themselves (the
+// buffer loads in flight are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
 }
 // ... with N = ahead * L for a run-time ahead in [0, A] (the immediate is fixed
 // per instruction)
@@ -706,7 +715,243 @@ __global__ __launch_bounds__(256) void gemm_dma_kernel(
                                                          vec);
 }
 
+// Short prompts: a workgroup of NW waves owns a tile of MR (16 or 32) rows x 32
+// columns of Y, small enough that the tiles of a few-row prompt cover the CUs.
+// The tile's 64-groups go in rounds of NW: in round j wave w forms P_g of group
+// g = NW j + w on the matrix cores, with the operands and the four
+// instructions of the tiled loops (a 32 x 32 matrix-core tile; with MR = 16 its
+// rows 16..31 are zero), and passes it on through LDS with the group's scales
+// 8 s_g; then every wave runs the fp32 chain T += 8 s_g P_g over the round's
+// groups in ascending order for its share of the tile's outputs (wave r keeps
+// values NV r .. NV (r + 1) - 1, NV = MR / (2 NW), of each lane position's
+// sixteen: only rows below MR).  Each output therefore gets the tiled loops'
+// arithmetic in their order, and the same bits.  A round's codes (32 columns x
+// 32 NW bytes) and activations (MR rows x 128 NW bytes) are loaded whole-line
+// by the waves, D rounds ahead into registers, and staged through LDS into the
+// matrix-core layout; products are formed two rounds before they go out, so
+// the matrix cores' latency stays off a round's path.  After the last round
+// wave 0 gathers the tile and adds the bias terms as the tiled loops do,
+// storing only the tile's own rows.
+template <int MR>
+struct ChainOps {
+  v4u c;             // 16 bytes of the round's codes
+  v4u a[MR / 8];     // 16 bytes each of the round's activations
+  uint16_t s;        // scale of column l32, group NW j + w (bf16)
+};
+
+template <int MR, int NW, int D, typename OUT>
+__global__ __launch_bounds__(64 * NW) void gemm_chain_kernel(
+    const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, const uint16_t* __restrict__ xp,
+    const uint16_t* __restrict__ xs, OUT* __restrict__ y, int64_t M, int64_t N, int64_t K,
+    int64_t ldy, int64_t G16, int64_t MT, int64_t tiles, int64_t per, bool vec) {
+  static_assert(MR == 16 || MR == 32, "tile rows");
+  static_assert(NW == 4 || NW == 8, "waves");
+  constexpr int NV = MR / (2 * NW);                  // chain values per lane
+  constexpr int XI = MR / 8;                         // activation loads per wave and round
+  constexpr int CS = 2 * NW;                         // 16-byte code slots per column and round
+  constexpr int XS = 8 * NW;                         // 16-byte activation slots per row and round
+  constexpr int XP_G = NW * 64 * NV * 4;             // one group's products: [reader][lane][NV]
+  constexpr int XS_G = 64 * 4;                       // one group's scales: [lane]
+  constexpr int XCH = NW * (XP_G + XS_G);            // one round's exchange
+  constexpr int SC = 32 * CS * 16, SX = MR * XS * 16;  // one round's staged codes, activations
+  constexpr int ST = SC + SX;
+  constexpr int ZERO = 2 * XCH + 2 * ST;             // 16 zero bytes (rows 16..31 of a 16-row tile)
+  __shared__ __attribute__((aligned(16))) unsigned char smem[ZERO + 16];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int tile = (b & 7) * (int)per + (b >> 3);
+  if (tile >= (int)tiles) return;
+  // row tiles fastest: the row tiles of one column tile share its codes in L2
+  const int nt = __builtin_amdgcn_readfirstlane(tile / (int)MT);
+  const int mt = __builtin_amdgcn_readfirstlane(tile - nt * (int)MT);
+  const int64_t m0 = (int64_t)mt * MR, n0 = (int64_t)nt * 32;
+  const int G = (int)(K >> 6);
+  const int K8 = (int)(K >> 3);
+  const int R = (G + NW - 1) / NW;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(xp + m0 * K), (short)0, (int)((M - m0) * K * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(wq + n0 * K8), (short)0, (int)((N - n0) * K8 * 4), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(scales + n0 * G), (short)0, (int)((N - n0) * G * 2), kRsrcWord3);
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  if (tid < 4) reinterpret_cast<uint32_t*>(smem + ZERO)[tid] = 0u;
+  // loads: 16-byte piece cp of column cr's round segment (32 NW bytes), and
+  // piece xq_i of row xr_i's (128 NW bytes)
+  const int cr = (64 * wave + lane) / CS, cp = (64 * wave + lane) % CS;
+  const int vc = cr * K8 * 4 + cp * 16;
+  int vx[XI], xw[XI];
+  // LDS slots are swizzled so that both the whole-line writes and the
+  // matrix-core reads are free of bank conflicts: codes [column][CS slots],
+  // slot p ^ (column & (CS - 1)); activations [row][XS slots], slot q ^ (row & 15)
+  const int cw = cr * CS * 16 + ((cp ^ (cr & (CS - 1))) << 4);
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int f = (i * NW + wave) * 64 + lane;
+    const int xr = f / XS, xq = f % XS;
+    vx[i] = xr * (int)K * 2 + xq * 16;
+    xw[i] = SC + xr * XS * 16 + ((xq ^ (xr & 15)) << 4);
+  }
+  const int vs = l32 * G * 2;
+  // matrix-core reads: lane (h, l32) takes codes piece 2w + h of column l32 and
+  // activation chunks 4h + t (t = 0..3) of its group, row l32 (a 16-row tile's
+  // rows 16..31 read the zero slot)
+  const int crd = l32 * CS * 16 + (((2 * wave + h) ^ (l32 & (CS - 1))) << 4);
+  int xrd[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    xrd[t] = (MR == 16 && l32 >= 16) ? ZERO - 2 * XCH : SC + l32 * XS * 16 + (((8 * wave + 4 * h + t) ^ (l32 & 15)) << 4);
+
+  // rounds past the last reload the last one (cached), so every round loads alike
+  auto load = [&](ChainOps<MR>& o, int r) __attribute__((always_inline)) {
+    r = r < R ? r : R - 1;
+    o.c = __builtin_amdgcn_raw_buffer_load_b128(rw, vc, r * (32 * NW), 0);
+#pragma unroll
+    for (int i = 0; i < XI; ++i) o.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, vx[i], r * (128 * NW), 0);
+    o.s = __builtin_amdgcn_raw_buffer_load_b16(rs, vs, (NW * r + wave) * 2, 0);
+  };
+  auto stage = [&](const ChainOps<MR>& o, int par) __attribute__((always_inline)) {
+    unsigned char* base = smem + 2 * XCH + par * ST;
+    *reinterpret_cast<v4u*>(base + cw) = o.c;
+#pragma unroll
+    for (int i = 0; i < XI; ++i) *reinterpret_cast<v4u*>(base + xw[i]) = o.a[i];
+  };
+  const uint32_t msk = 0x00780078u, mg = kMagic2;
+  auto compute_p = [&](int par) __attribute__((always_inline)) -> f32x16_t {
+    const unsigned char* base = smem + 2 * XCH + par * ST;
+    const v4u c = *reinterpret_cast<const v4u*>(base + crd);
+    v4u a[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      a[t] = *reinterpret_cast<const v4u*>((MR == 16 && l32 >= 16 ? smem + 2 * XCH : base) + xrd[t]);
+    f32x16_t p;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = 0.0f;
+    p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[0]), expand_codes(c.x, msk, mg), p, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[1]), expand_codes(c.y, msk, mg), p, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[2]), expand_codes(c.z, msk, mg), p, 0, 0, 0);
+    p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[3]), expand_codes(c.w, msk, mg), p, 0, 0, 0);
+    return p;
+  };
+  // this wave's group product of a round -> reader r's slots, and its scales
+  auto put_p = [&](const f32x16_t& p, float s8, int par) __attribute__((always_inline)) {
+    unsigned char* base = smem + par * XCH + wave * XP_G + lane * NV * 4;
+#pragma unroll
+    for (int r = 0; r < NW; ++r) {
+      if constexpr (NV == 4)
+        *reinterpret_cast<float4*>(base + r * 64 * NV * 4) = make_float4(p[4 * r], p[4 * r + 1], p[4 * r + 2], p[4 * r + 3]);
+      else if constexpr (NV == 2)
+        *reinterpret_cast<float2*>(base + r * 64 * NV * 4) = make_float2(p[2 * r], p[2 * r + 1]);
+      else
+        *reinterpret_cast<float*>(base + r * 64 * NV * 4) = p[r];
+    }
+    *reinterpret_cast<float*>(smem + par * XCH + NW * XP_G + wave * XS_G + lane * 4) = s8;
+  };
+  float tot[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) tot[e] = 0.0f;
+  // the chain over round j's groups, ascending
+  auto chain = [&](int j) __attribute__((always_inline)) {
+    const unsigned char* xr_ = smem + (j & 1) * XCH + (wave * 64 + lane) * NV * 4;
+    const float* xsr = reinterpret_cast<const float*>(smem + (j & 1) * XCH + NW * XP_G) + lane;
+    float pv[NW][NV], s8[NW];
+#pragma unroll
+    for (int gq = 0; gq < NW; ++gq) {
+      const float* f = reinterpret_cast<const float*>(xr_ + gq * XP_G);
+#pragma unroll
+      for (int e = 0; e < NV; ++e) pv[gq][e] = f[e];
+      s8[gq] = xsr[gq * 64];
+    }
+    if (NW * (j + 1) <= G) {
+#pragma unroll
+      for (int gq = 0; gq < NW; ++gq)
+#pragma unroll
+        for (int e = 0; e < NV; ++e) tot[e] = __builtin_fmaf(s8[gq], pv[gq][e], tot[e]);
+    } else {  // the last round of a ragged G
+      const int ng = G - NW * j;
+#pragma unroll
+      for (int gq = 0; gq < NW; ++gq)
+        if (gq < ng)
+#pragma unroll
+          for (int e = 0; e < NV; ++e) tot[e] = __builtin_fmaf(s8[gq], pv[gq][e], tot[e]);
+    }
+  };
+
+  ChainOps<MR> ring[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u) load(ring[u], u);
+  stage(ring[0], 0);
+  float sc = 8.0f * bf16_to_f32(ring[0].s);
+  load(ring[0], D);
+  float sc1 = sc;
+  if (R > 1) {
+    stage(ring[1], 1);
+    sc1 = 8.0f * bf16_to_f32(ring[1].s);
+  }
+  load(ring[1], D + 1);
+  lds_barrier();
+  f32x16_t pc = compute_p(0);
+  f32x16_t pc1 = pc;
+  if (R > 1) pc1 = compute_p(1);
+  // round j: its product goes out with its scales and round j + 2's operands
+  // are staged (ring slot (j + 2) % D, then refilled with round j + 2 + D);
+  // after the barrier round j + 2's product is started and the chain takes
+  // round j's products
+  auto round = [&](int j, ChainOps<MR>& nxt) __attribute__((always_inline)) {
+    put_p(pc, sc, j & 1);
+    float sn = sc1;
+    if (j + 2 < R) {
+      stage(nxt, j & 1);
+      sn = 8.0f * bf16_to_f32(nxt.s);
+    }
+    load(nxt, j + 2 + D);
+    lds_barrier();
+    f32x16_t pn = pc1;
+    if (j + 2 < R) pn = compute_p(j & 1);
+    chain(j);
+    pc = pc1;
+    sc = sc1;
+    pc1 = pn;
+    sc1 = sn;
+  };
+  int j0 = 0;
+  for (; j0 + D <= R; j0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) round(j0 + u, ring[(u + 2) % D]);
+  }
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u)
+    if (j0 + u < R) round(j0 + u, ring[(u + 2) % D]);
+
+  // wave 0 gathers the tile (the exchange area is free after this barrier)
+  lds_barrier();
+  float* gat = reinterpret_cast<float*>(smem) + (wave * 64 + lane) * NV;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) gat[e] = tot[e];
+  lds_barrier();
+  if (wave != 0) return;
+  f32x16_t t16[1][1];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) t16[0][0][v] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < NW; ++r) {
+    const float* src = reinterpret_cast<const float*>(smem) + (r * 64 + lane) * NV;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) t16[0][0][NV * r + e] = src[e];
+  }
+  const int64_t mlim = M < m0 + MR ? M : m0 + MR;
+  bias_and_store_any<1, 1, 6, OUT>(t16, scales, biases, xs, y, mlim, N, G, G16, ldy, m0, n0, l32, h, vec);
+}
+
 int64_t g16_of(int64_t K) { return (((K >> 6) + 15) / 16) * 16; }
+
+// The short-prompt kernel takes prompts of at most 32 rows whose 32-column
+// tiles number at most two per CU (wider matrices keep the tiled loops, which
+// stream them as fast)
+bool chain_tiles(int64_t M, int64_t N) { return M <= 32 && (N + 31) / 32 <= 2 * cu_count(); }
 
 // Where the 64 x 64 tiles take over (rows of the slice, 128 x 128 tiles it makes)
 #ifndef W4G_SMALL_RULE
@@ -750,7 +995,21 @@ hipError_t launch_main(const uint32_t* wq, const uint16_t* scales, const uint16_
       const uint16_t *xp_s = xp + ms * K, *xs_s = xs + ms * 3 * G16;
       OUT* y_s = y + ms * N + ns;
       const int64_t tiles128 = ((Ms + kTM - 1) / kTM) * ((Ns + kTN - 1) / kTN);
-      if (dma && small_tiles(Ms, tiles128)) {
+      if (dma && chain_tiles(Ms, Ns)) {
+        // few rows over a narrow matrix: MR x 32 tiles, each column tile's groups
+        // dealt to eight waves
+        const int64_t NT = (Ns + 31) / 32;
+        if (Ms <= 16) {
+          const int64_t tiles = NT, per = (tiles + 7) / 8;
+          hipLaunchKernelGGL((gemm_chain_kernel<16, 8, 3, OUT>), dim3((unsigned)(8 * per)), dim3(512), 0,
+                             stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, (int64_t)1, tiles, per,
+                             vec);
+        } else {
+          const int64_t MT = (Ms + 31) / 32, tiles = MT * NT, per = (tiles + 7) / 8;
+          hipLaunchKernelGGL((gemm_chain_kernel<32, 8, 3, OUT>), dim3((unsigned)(8 * per)), dim3(512), 0,
+                             stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, MT, tiles, per, vec);
+        }
+      } else if (dma && small_tiles(Ms, tiles128)) {
         // 64 x 64 tiles: a 4-stage ring (83 KiB, one workgroup per CU) while the
         // tiles fit on the CUs once, else 3 stages (62 KiB) so two share a CU
         const int64_t NT = (Ns + 63) / 64, tiles = ((Ms + 63) / 64) * NT, per = (tiles + 7) / 8;
