@@ -61,7 +61,11 @@ __device__ __forceinline__ bf16x8_t expand128(uint32_t w, uint32_t m, uint32_t g
 // waves (W = min(8, NI), NI = ceil(G / 2) items of two consecutive groups
 // (2i, 2i + 1)) split the items of every tile into contiguous ranges: wave w
 // takes items [w NI / W, (w + 1) NI / W) of each tile in ascending order, the
-// tiles one after the other, through a ring of P items in flight.
+// tiles one after the other, through a ring of P items in flight.  Where a CU
+// has two tiles or more, two such sets of W waves run side by side, set s
+// taking tiles s, s + 2, ... (four waves per SIMD instead of two, for latency
+// hiding); a tile's items, their split and the order of its wave sums are the
+// same whichever set runs it.
 //
 // v_mfma_f32_16x16x32_bf16: A = activations (batch row m = lane & 15, rows
 // m >= B zero), B = codes of the tile's 16 rows expanded to 128 + q (row
@@ -102,7 +106,8 @@ __device__ __forceinline__ bf16x8_t expand128(uint32_t w, uint32_t m, uint32_t g
 // not change them.
 
 constexpr int kCuRows = 16;      // rows per tile
-constexpr int kCuMaxWaves = 8;   // waves per workgroup
+constexpr int kCuMaxWaves = 8;   // waves per set (the order's wave split)
+constexpr int kCuSets = 2;       // sets of waves per workgroup (whole-x kernel)
 
 // LDS barrier for data exchanged through LDS only: the loads in flight are not
 // waited for
@@ -120,15 +125,19 @@ struct CuItem {
 };
 
 template <bool EVENG, bool AM, int P>
-__global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
+__global__ __launch_bounds__(64 * kCuMaxWaves * kCuSets) void gemv_mfma_cu_kernel(
     const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases,
     const uint16_t* __restrict__ x, float* __restrict__ y, int B, int64_t N, int64_t K, int64_t rpw,
-    int TB, bool hold, uint2* __restrict__ rec) {
+    int TB, bool hold, uint2* __restrict__ rec, int S) {
   extern __shared__ uint4 s_mem[];
   __shared__ uint64_t s_best[AM ? 8 : 1];
   __shared__ uint32_t s_bad;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int W = (int)(blockDim.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63;
+  // S sets of W waves; set s takes tiles s, s + S, ... (every set splits a
+  // tile's items the same way, so which set runs a tile changes nothing)
+  const int W = (int)(blockDim.x >> 6) / S;
+  const int set = __builtin_amdgcn_readfirstlane((tid >> 6) / W);
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) - set * W);
   const int n16 = lane & 15, q = lane >> 4;
   const int G = (int)(K >> 6), NI = (G + 1) >> 1;
   const int64_t KW = K >> 3;
@@ -139,7 +148,8 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   // this wave's items of every tile: [ist, iend) (contiguous, >= 1 since W <= NI)
   const int ist = (int)((int64_t)wave * NI / W), iend = (int)((int64_t)(wave + 1) * NI / W);
   const int cnt = iend - ist;
-  const int n_items = T * cnt;
+  const int my_tiles = set < T ? (T - set + S - 1) / S : 0;
+  const int n_items = my_tiles * cnt;
 
   const int XS = B > 4 ? 8 : 4;                                      // batch slots per group sum
   uint4* s_x = s_mem;                                                // [G][2][4][B]
@@ -159,7 +169,7 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   // g0 + p / 2.  The consumer moves each lane's 16 bytes to lane
   // (row, quarter p), the matrix-core layout, through the LDS crossbar.
   const int pc = lane & 3;
-  int it_t = 0, it_i = ist;
+  int it_t = set, it_i = ist;
   const uint32_t* cptr;
   const uint16_t *sptr = scales, *bptr = biases;
   auto set_tile = [&]() {
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
     }
     if (++it_i == iend) {
       it_i = ist;
-      ++it_t;
+      it_t += S;
       set_tile();
     }
   };
@@ -199,12 +209,12 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   // B = 8 gate-up 31 against 35 us, lm_head 172 against 188), each lane
   // following its own item through the tiles
   static_assert(!EVENG || P == 4, "one pair load per four items");
-  int qt = 0, qi = ist;  // this lane's item of the next pair load: tile, item within the tile
+  int qt = set, qi = ist;  // this lane's item of the next pair load: tile, item within the tile
   auto q_adv = [&](int k) {
     qi += k;
     while (qi >= iend) {
       qi -= cnt;
-      ++qt;
+      qt += S;
     }
   };
   if constexpr (EVENG) q_adv(pc);
@@ -268,9 +278,8 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   // a batch of tiles is done the wave sums are added, at two barriers
   const uint32_t m = 0x000F000Fu, gm = kMagic128;
   f32x4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
-  int ci = ist, bt = 0, tb0 = 0;
+  int ci = ist, tb0 = 0, ct = set;  // ct: the tile being consumed
   float* const red_base = s_red + (wave * 32 + lane) * 4;
-  float* red_ptr = red_base;
   auto group = [&](int g, uint32_t w0, uint32_t w1, uint32_t sb, uint32_t bb) {
     const int ab = lane_a + g * stride_g;
     const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, s_x[ab]);
@@ -307,6 +316,7 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
   auto reduce_batch = [&]() {
     // add the wave sums of the batch's bt tiles in ascending wave order (rows
     // fastest across threads, so the stores of a batch row are contiguous)
+    const int bt = T - tb0 < TB ? T - tb0 : TB;
     lds_barrier();
     const int nout = bt * kCuRows * B;
     for (int o = tid; o < nout; o += (int)blockDim.x) {
@@ -347,14 +357,14 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
     }
     if (++ci == iend) {  // this wave's share of a tile is done: its partial sums to LDS
       ci = ist;
-      if (lane < 32) *reinterpret_cast<f32x4_t*>(red_ptr) = tot;
-      red_ptr += W * 32 * 4;
+      if (lane < 32) *reinterpret_cast<f32x4_t*>(red_base + (ct - tb0) * W * 32 * 4) = tot;
       tot = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      if (++bt == TB || tb0 + bt == T) {
+      ct += S;
+      // every batch whose tiles of this set are all done is reduced (all sets
+      // take part in every batch's reduction, in batch order)
+      while (tb0 < T && (ct >= tb0 + TB || ct >= T)) {
         reduce_batch();
-        tb0 += bt;
-        bt = 0;
-        red_ptr = red_base;
+        tb0 += TB;
       }
     }
   };
@@ -396,6 +406,12 @@ __global__ __launch_bounds__(64 * kCuMaxWaves) void gemv_mfma_cu_kernel(
 #pragma unroll
   for (int sl = 0; sl < P; ++sl)
     if (j + 2 * P + sl < n_items) consume(ring[sl], sl, sqa, bqa);
+
+  // a set without tiles in the last batches still takes part in their reductions
+  while (tb0 < T) {
+    reduce_batch();
+    tb0 += TB;
+  }
 
   // ---- held results out (the last reduction ended with a barrier), then the record
   if (hold) {
@@ -699,6 +715,9 @@ int cu_waves(int64_t K) {
   return NI < kCuMaxWaves ? (int)NI : kCuMaxWaves;
 }
 int cu_tiles(int64_t N) { return (int)((cu_rows(N) + kCuRows - 1) / kCuRows); }
+// two sets of waves where a CU has two tiles or more (and a batch of
+// reductions holds two), else one
+int cu_sets(int64_t N, int64_t K);
 // LDS of the whole-x kernel: the activations and group sums of Bc batch rows,
 // then the partial sums of a batch of tiles
 size_t cu_lds_fixed(int Bc, int64_t K) {
@@ -723,6 +742,9 @@ int cu_batch_tiles(int Bc, int64_t N, int64_t K) {
   const size_t fixed = cu_lds_fixed(Bc, K) + (cu_hold(Bc, N, K) ? cu_held_bytes(Bc, N) : 0);
   const int64_t t = (int64_t)((kCuMaxLds - fixed) / cu_tile_bytes(K));
   return t < cu_tiles(N) ? (int)t : cu_tiles(N);
+}
+int cu_sets(int64_t N, int64_t K) {
+  return cu_tiles(N) >= 2 && cu_batch_tiles(kMaxBatch, N, K) >= 2 ? kCuSets : 1;
 }
 size_t cu_lds_bytes(int Bc, int64_t N, int64_t K) {
   return cu_lds_fixed(Bc, K) + (cu_hold(Bc, N, K) ? cu_held_bytes(Bc, N) : 0) +
@@ -765,9 +787,10 @@ hipError_t launch_cu_pass(const uint32_t* wq, const uint16_t* scales, const uint
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kCuMaxLds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gemv_mfma_cu_kernel<EVENG, AM, 4>), dim3((unsigned)blocks), dim3(64 * cu_waves(K)), lds,
-                     stream, wq, scales, biases, x, y, B, N, K, rpw, cu_batch_tiles(B, N, K), cu_hold(B, N, K),
-                     rec);
+  const int sets = cu_sets(N, K);
+  hipLaunchKernelGGL((gemv_mfma_cu_kernel<EVENG, AM, 4>), dim3((unsigned)blocks), dim3(64 * cu_waves(K) * sets),
+                     lds, stream, wq, scales, biases, x, y, B, N, K, rpw, cu_batch_tiles(B, N, K), cu_hold(B, N, K),
+                     rec, sets);
   return hipGetLastError();
 }
 
