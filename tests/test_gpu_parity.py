@@ -212,13 +212,16 @@ def test_gemv_mfma_large_k(N, K, B):
 
 
 @pytest.mark.parametrize("B,N,K", [(8, 5120, 5120), (3, 300, 1024), (1, 33, 128), (5, 1000, 8256),
-                                   (8, 6001, 4096), (2, 70000, 2048), (4, 37, 8320), (8, 40000, 8192)])
+                                   (8, 6001, 4096), (2, 70000, 2048), (4, 37, 8320), (8, 40000, 8192),
+                                   (8, 40000, 8064)])
 def test_gemv_mfma_step_variant_bitwise(B, N, K):
     """The step-staged per-CU matrix-core kernel, forced where the whole-x one
     runs, gives the same bits: one order whichever of the two K selects (an odd
     group count, a ragged last workgroup, several tile pairs per CU; at
     40000 x 8192 the whole-x kernel's results do not fit in its LDS beside the
-    activations and are stored batch by batch)."""
+    activations and are stored batch by batch; at 40000 x 8064 in batches of
+    five tiles, so the whole-x kernel's two sets of waves, on alternate tiles,
+    meet batches that start on either set)."""
     wq, sc, bi, x = _case(N, K, B, 31 + B)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x))
     a = down(w4g.qmm_gemv(*W, kernel=w4g.GEMV_MFMA))
