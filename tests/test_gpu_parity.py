@@ -151,6 +151,39 @@ def test_gemv_valu_variants_bitwise(N, K, B):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("bits", [4, 2, 8])
+@pytest.mark.parametrize("N,K", [(5120, 17408), (6001, 12352), (700, 9280)])
+def test_gemv_valu_step_staged(N, K, bits):
+    """Batches whose paired activations exceed LDS where a CU's share is at most
+    24 rows (down_proj from B = 5) run the step-staged vector-ALU kernel, the
+    activations staged a chunk at a time by waves of their own: every batch row
+    bitwise equal to the same row alone (B = 1 keeps x whole in LDS), over full
+    shares (20 and 24 rows per CU), a short share, a ragged last chunk (12352 =
+    12 chunks + 64) and all three code widths; sampled rows close to the oracle;
+    for 4-bit codes the fused argmax epilogue too (logits bitwise those of
+    qmm_gemv, ids those of the two-pass argmax)."""
+    wq, sc, bi = synth.weights(N, K, workload=90 + bits, bits=bits)
+    x = synth.activations(8, K, workload=90 + bits)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y8 = down(w4g.qmm_gemv(*W, up_bf16(x), bits=bits))
+    for B in (5, 6, 7):
+        yb = down(w4g.qmm_gemv(*W, up_bf16(x[:B]), bits=bits))
+        assert np.array_equal(yb.view(np.uint32), y8[:B].view(np.uint32)), f"B={B} differs from B=8"
+    for m in range(8):
+        y1 = down(w4g.qmm_gemv(*W, up_bf16(x[m:m + 1]), bits=bits))
+        assert np.array_equal(y1[0].view(np.uint32), y8[m].view(np.uint32)), f"row {m} differs at B=1"
+    rng = np.random.default_rng(N + K + bits)
+    rows = np.unique(np.r_[0:24, N - 24:N, rng.choice(N, 40, replace=False)])
+    ref = oracle.qmm(wq[rows], sc[rows], bi[rows], x, bits=bits)
+    assert_close(y8[:, rows], ref, f"step-staged w{bits} N={N} K={K}")
+    if bits == 4:
+        ids, logits = w4g.qmm_gemv_argmax(*W, up_bf16(x))
+        assert np.array_equal(down(logits).view(np.uint32), y8.view(np.uint32)), "fused logits differ"
+        two_pass = ids_down(w4g.vocab_argmax(up_f32(y8)))
+        assert np.array_equal(ids_down(ids), two_pass)
+        assert np.array_equal(ids_down(ids), oracle.argmax(y8))
+
+
 @pytest.mark.parametrize("N,K", [(9477, 1024), (8193, 3072), (5120, 2048), (300, 17408)])
 def test_gemv_per_cu_layout(N, K):
     """B = 1 with one workgroup per CU (an equal share of rows each, half waves

@@ -462,6 +462,270 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
   }
 }
 
+// Workgroup barrier for data exchanged through LDS only (the loads in flight
+// are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// Step-staged variant for batches whose paired activations exceed LDS, where
+// a CU's share is at most 24 rows: the workgroup's first waves compute (R rows
+// per half wave, every half wave taking its rows' chunks in ascending order,
+// all in step), the last ceil(B / 2) waves only stage the activations of the
+// batch, one chunk at a time, into two LDS buffers (chunk c + 1 is stored
+// while chunk c is used; one barrier per chunk).  Two kinds of waves keep the
+// staging registers apart from the compute registers.  Per row the arithmetic
+// and its order are gemv_valu_kernel's (the same chunk loop into one
+// accumulator per batch row, the same lane tree; a lane past the end of a
+// short last chunk reads lane 0 of chunk 0, kept in LDS for the purpose, and
+// adds exact zeros), so the bits are the same, and the weights are read once
+// for the whole batch.  P: items of codes in flight per half wave; PS: chunks
+// of activations in flight per staging lane.
+// AM: the argmax epilogue as in gemv_valu_kernel.
+template <int B, int R, int P, int PS, bool RAGGED, bool AM, int BITS = 4>
+__global__ __launch_bounds__(512) void gemv_valu_step_kernel(const uint32_t* __restrict__ wq,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const uint16_t* __restrict__ biases,
+                                                             const uint16_t* __restrict__ x,
+                                                             float* __restrict__ y, int64_t N,
+                                                             int64_t K, int64_t rpw, int ncw,
+                                                             uint2* __restrict__ rec) {
+  extern __shared__ uint4 s_mem[];
+  typedef typename CodeVec<BITS>::V V;
+  constexpr int VPL = CodeVec<BITS>::VPL;
+  const int64_t KW = K * BITS / 32, G = K >> 6;
+  const int C = (int)((K + kChunk - 1) / kChunk);
+  // two chunk buffers, then (RAGGED) a copy of chunk 0 for the lanes past the
+  // end of the short last chunk: [3][B][4][32] pairs, then [3][B][32] sums
+  constexpr int NBUF = RAGGED ? 3 : 2;
+  uint4* s_xp = s_mem;
+  float* s_xh = reinterpret_cast<float*>(s_mem + NBUF * B * 128);
+  __shared__ uint64_t s_best[AM ? B : 1];
+  __shared__ uint32_t s_bad;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 31;
+  const int64_t wg_begin = (int64_t)blockIdx.x * rpw;
+  const int64_t wg_end = N - wg_begin < rpw ? N : wg_begin + rpw;
+  if (AM && tid == 0) {
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) s_best[bb] = 0;
+    s_bad = 0;
+  }
+
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) >= ncw) {
+    // staging lane: segment `lane` of batch row sbb (an odd batch's last half
+    // wave repeats row B - 1: the same values to the same places).  A segment
+    // past the end of a short last chunk loads the chunk's first segment; its
+    // slots are never read.
+    const int st = tid - 64 * ncw;
+    const int sbb = (st >> 5) < B ? (st >> 5) : B - 1;
+    auto load_chunk = [&](int c, uint4 (&raw)[4]) {
+      if (c > C - 1) c = C - 1;
+      int64_t e = (int64_t)c * kChunk + (int64_t)lane * 32;
+      if (e >= K) e = (int64_t)c * kChunk;
+      const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)sbb * K + e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = src[i];
+    };
+    auto put_chunk = [&](int c, const uint4 (&raw)[4]) {
+      const int buf = c & 1;
+      float h = 0.0f;
+      uint4 pr[4];
+      if constexpr (BITS == 2) {
+        pair_x2(raw[0], raw[1], pr[0], pr[1]);
+        pair_x2(raw[2], raw[3], pr[2], pr[3]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 q = BITS == 4 ? pair_x(raw[i]) : BITS == 8 ? pair_x8(raw[i]) : pr[i];
+        s_xp[(buf * B + sbb) * 128 + i * 32 + lane] = q;
+        if (RAGGED && c == 0) s_xp[(2 * B + sbb) * 128 + i * 32 + lane] = q;
+        h = dot2(q.x, kOnes, h);
+        h = dot2(q.y, kOnes, h);
+        h = dot2(q.z, kOnes, h);
+        h = dot2(q.w, kOnes, h);
+      }
+      s_xh[(buf * B + sbb) * 32 + lane] = h;
+      if (RAGGED && c == 0) s_xh[(2 * B + sbb) * 32 + lane] = h;
+    };
+    // chunk k in raw[k % PS]; chunk 0 stored before the first barrier, chunk
+    // c + 1 after barrier c, then chunk c + 1 + PS loaded in its place
+    // (the loads stay unconditional, past the last chunk rereading it, so that
+    // each store waits for its own chunk only)
+    uint4 raw[PS][4];
+#pragma unroll
+    for (int k = 0; k < PS; ++k) load_chunk(k, raw[k]);
+    put_chunk(0, raw[0]);
+    load_chunk(PS, raw[0]);
+    int c = 0;
+    for (; c + PS < C; c += PS) {
+#pragma unroll
+      for (int k = 0; k < PS; ++k) {
+        lds_barrier();
+        put_chunk(c + k + 1, raw[(k + 1) % PS]);
+        load_chunk(c + k + 1 + PS, raw[(k + 1) % PS]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PS; ++k) {
+      if (c + k < C) {
+        lds_barrier();
+        if (c + k + 1 < C) put_chunk(c + k + 1, raw[(k + 1) % PS]);
+      }
+    }
+    if constexpr (AM) __syncthreads();
+    return;
+  }
+
+  const int hwi = tid >> 5;
+  const int64_t row0 = wg_begin + (int64_t)hwi * R;  // this half wave's rows (past the share: valid rows, not stored)
+  const int last_lanes = (int)((K - (int64_t)(C - 1) * kChunk) >> 5);
+  const uint32_t m = kNibbles, g = kMagic128;
+
+  const V* pw[R];
+  const uint16_t* ps[R];
+  const uint16_t* pb[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t lrow = row0 + r < wg_end ? row0 + r : wg_end - 1;
+    pw[r] = reinterpret_cast<const V*>(wq + lrow * KW) + VPL * lane;
+    ps[r] = scales + lrow * G + (lane >> 1);
+    pb[r] = biases + lrow * G + (lane >> 1);
+  }
+  int pc = 0;  // chunk of the next item to load (past the last: the last again, never consumed)
+  auto issue = [&](Item<R, BITS>& it) {
+    const int c = pc < C ? pc : C - 1;
+    int vo = c * 32 * VPL, go = c * 16;
+    if (RAGGED && c == C - 1 && lane >= last_lanes) {
+      vo = -VPL * lane;
+      go = -(lane >> 1);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) it.w[r][v] = ld_stream(pw[r] + vo + v);
+      it.s[r] = ps[r][go];
+      it.b[r] = pb[r][go];
+    }
+    ++pc;
+  };
+  Item<R, BITS> ring[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) issue(ring[k]);
+
+  float acc[R][B];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) acc[r][bb] = 0.0f;
+  // item c: chunk c of this half wave's rows
+  auto consume = [&](const Item<R, BITS>& it, int c) {
+    // all half waves are done with chunk c - 1 and chunk c is staged (nothing
+    // of this item is moved above the barrier, where it would wait for loads
+    // issued after the ones the previous item needs)
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    bool active = true;
+    if (RAGGED && c == C - 1 && lane >= last_lanes) active = false;
+    float sc[R], cb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      sc[r] = bf16_to_f32(it.s[r]);
+      cb[r] = __builtin_fmaf(BITS == 8 ? -2176.0f : -128.0f, sc[r], bf16_to_f32(it.b[r]));
+      if (RAGGED && !active) sc[r] = cb[r] = 0.0f;
+    }
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) {
+      // (a lane past the end of a short last chunk: lane 0 of the chunk-0 copy)
+      const int xb = (!RAGGED || active) ? ((c & 1) * B + bb) : (2 * B + bb);
+      const int xl = (!RAGGED || active) ? lane : 0;
+      const uint4* xv = s_xp + xb * 128 + xl;
+      const uint4 x0 = xv[0], x1 = xv[32], x2 = xv[64], x3 = xv[96];
+      const float xh = s_xh[xb * 32 + xl];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float d = 0.0f;
+        if constexpr (BITS == 4) {
+          d = dot_word(it.w[r][0].x, x0, d, m, g);
+          d = dot_word(it.w[r][0].y, x1, d, m, g);
+          d = dot_word(it.w[r][0].z, x2, d, m, g);
+          d = dot_word(it.w[r][0].w, x3, d, m, g);
+        } else if constexpr (BITS == 2) {
+          d = dot_word2(it.w[r][0].x, x0, x1, d, g);
+          d = dot_word2(it.w[r][0].y, x2, x3, d, g);
+        } else {
+          float dl = 0.0f, dh = 0.0f;
+          dot_word8(it.w[r][0].x, x0.x, x0.y, dl, dh, m, g);
+          dot_word8(it.w[r][0].y, x0.z, x0.w, dl, dh, m, g);
+          dot_word8(it.w[r][0].z, x1.x, x1.y, dl, dh, m, g);
+          dot_word8(it.w[r][0].w, x1.z, x1.w, dl, dh, m, g);
+          dot_word8(it.w[r][1].x, x2.x, x2.y, dl, dh, m, g);
+          dot_word8(it.w[r][1].y, x2.z, x2.w, dl, dh, m, g);
+          dot_word8(it.w[r][1].z, x3.x, x3.y, dl, dh, m, g);
+          dot_word8(it.w[r][1].w, x3.z, x3.w, dl, dh, m, g);
+          d = __builtin_fmaf(16.0f, dh, dl);
+        }
+        acc[r][bb] = __builtin_fmaf(sc[r], d, acc[r][bb]);
+        acc[r][bb] = __builtin_fmaf(cb[r], xh, acc[r][bb]);
+      }
+    }
+  };
+  // every half wave has exactly C items; the loads stay unconditional (past
+  // the last chunk they reread it and are never consumed)
+  int c = 0;
+  for (; c + 2 * P - 1 < C; c += P) {
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      consume(ring[k], c + k);
+      issue(ring[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    if (c + k < C) consume(ring[k], c + k);
+    if (c + k + P < C) issue(ring[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < P; ++k)
+    if (c + P + k < C) consume(ring[k], c + P + k);
+
+  // the rows' sums (every lane holds them); lane bb stores batch row bb's
+  float mine[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) {
+      const float v = half_wave_sum(acc[r][bb]);
+      mine[r] = bb == 0 ? v : (lane == bb ? v : mine[r]);
+    }
+  }
+  if (lane < B) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row0 + r;
+      if (row < wg_end) {
+        if (!AM || y != nullptr) y[(int64_t)lane * N + row] = mine[r];
+        if constexpr (AM) {
+          const uint32_t u = __float_as_uint(mine[r]);
+          if (!finite_bits(u))
+            __hip_atomic_fetch_or(&s_bad, 1u << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          else
+            __hip_atomic_fetch_max(&s_best[lane], cand(u, (uint32_t)row), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    }
+  }
+  if constexpr (AM) {
+    __syncthreads();
+    if (tid < B)
+      rec[(int64_t)tid * gridDim.x + blockIdx.x] =
+          make_record(s_best[tid], ((s_bad >> tid) & 1u) != 0, (uint32_t)wg_begin);
+  }
+}
+
 // Register-staged variant of the same arithmetic, for shapes whose paired
 // activations do not fit in LDS (B * 2.125 * K bytes above the limit): each
 // 64-lane workgroup owns 2R rows, a half wave R of them, and reads the x pairs
@@ -698,12 +962,59 @@ int batch_parts(int B, int64_t K) {
   return b >= 2 && B > b ? (B + b - 1) / b : 1;
 }
 
+// Where the batch's activations do not fit in LDS and a CU's share is at most
+// 24 rows (decided with the MI355X's CU count, so that the records of the
+// fused head stay within the bound computed the same way), the step-staged
+// kernel reads the weights once for the whole batch (down at B = 8: 40 us in
+// two parts before).  Four computing waves of 2 x 3 rows: one per SIMD.
+constexpr int kStepR = 3;
+constexpr int64_t kStepRows = 8 * kStepR;
+bool use_step(int B, int64_t N, int64_t K) {
+  return (batch_parts(B, K) > 1 || use_regs(B, K, false)) && per_cu_rows(N, kMaxCUs) <= kStepRows;
+}
+int64_t step_rows(int64_t N, int cus) {
+  const int64_t r = per_cu_rows(N, cus);
+  return r < kStepRows ? r : kStepRows;
+}
+size_t step_lds_bytes(int B, bool ragged) {
+  const size_t nbuf = ragged ? 3 : 2;
+  return nbuf * (size_t)B * (128 * 16 + 32 * 4);
+}
+
+template <bool AM, int BITS = 4>
+hipError_t launch_step(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                       const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                       hipStream_t stream) {
+  const int64_t rpw = step_rows(N, cu_count());
+  const int64_t blocks = (N + rpw - 1) / rpw;
+  const int ncw = (int)((rpw + 2 * kStepR - 1) / (2 * kStepR));  // computing waves
+  const int threads = 64 * (ncw + (B + 1) / 2);                  // then the staging waves
+  const bool ragged = (K % kChunk) != 0;
+  const size_t lds = step_lds_bytes(B, ragged);
+  switch (B) {
+#define W4G_STEP(BB)                                                                                        \
+    case BB:                                                                                                \
+      if (ragged)                                                                                           \
+        hipLaunchKernelGGL((gemv_valu_step_kernel<BB, kStepR, 2, 3, true, AM, BITS>), dim3((unsigned)blocks), \
+                           dim3(threads), lds, stream, wq, scales, biases, x, y, N, K, rpw, ncw, rec);      \
+      else                                                                                                  \
+        hipLaunchKernelGGL((gemv_valu_step_kernel<BB, kStepR, 2, 3, false, AM, BITS>), dim3((unsigned)blocks), \
+                           dim3(threads), lds, stream, wq, scales, biases, x, y, N, K, rpw, ncw, rec);      \
+      return hipGetLastError();
+    W4G_STEP(1) W4G_STEP(2) W4G_STEP(3) W4G_STEP(4) W4G_STEP(5) W4G_STEP(6) W4G_STEP(7) W4G_STEP(8)
+#undef W4G_STEP
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // The one dispatch both entry points share: the kernel, R and P are functions
 // of (B, N, K) and force_regs only, and the workgroup count follows from them.
 template <bool AM>
 hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                     const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                     bool force_regs, hipStream_t stream) {
+  if (!force_regs && use_step(B, N, K))
+    return launch_step<AM>(wq, scales, biases, x, y, rec, B, N, K, stream);
   const int parts = force_regs ? 1 : batch_parts(B, K);
   if (parts > 1) {
     const int64_t grid = (N + per_cu_rows(N) - 1) / per_cu_rows(N);
@@ -771,6 +1082,7 @@ hipError_t dispatch_bits_lds(const uint32_t* wq, const uint16_t* scales, const u
 template <int BITS>
 hipError_t dispatch_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                          const uint16_t* x, float* y, int B, int64_t N, int64_t K, hipStream_t stream) {
+  if (use_step(B, N, K)) return launch_step<false, BITS>(wq, scales, biases, x, y, nullptr, B, N, K, stream);
   if (lds_rows(K) < 1) return hipErrorInvalidValue;
   const int parts = B > lds_rows(K) ? (B + lds_rows(K) - 1) / lds_rows(K) : 1;
   for (int p = 0, b0 = 0; p < parts; ++p) {
@@ -807,6 +1119,7 @@ namespace {
 // the workgroups of the layout dispatch() launches on a device with `cus`
 // compute units, one record each
 int64_t valu_records(int B, int64_t N, int64_t K, int cus) {
+  if (use_step(B, N, K)) return (N + step_rows(N, cus) - 1) / step_rows(N, cus);
   if (batch_parts(B, K) > 1) return (N + per_cu_rows(N, cus) - 1) / per_cu_rows(N, cus);
   if (use_regs(B, K, false)) {
     const int R = regs_rows(B);
