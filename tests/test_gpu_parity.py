@@ -188,8 +188,9 @@ def test_gemv_valu_step_staged(N, K, bits):
 def test_gemv_per_cu_layout(N, K):
     """B = 1 with one workgroup per CU (an equal share of rows each, half waves
     striding through it; ragged shares and a last workgroup with an odd row
-    count) against the oracle, and bitwise equal to the same rows computed by
-    the layout of B = 2 and by the register-staged variant."""
+    count; at 300 x 17408 the step-staged kernel, x staged a chunk at a time)
+    against the oracle, and bitwise equal to the same rows computed by the
+    layout of B = 2 and by the register-staged variant."""
     wq, sc, bi, x = _case(N, K, 2, N % 97)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
     y1 = down(w4g.qmm_gemv(*W, up_bf16(x[:1]), kernel=1))

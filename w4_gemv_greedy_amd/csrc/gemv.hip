@@ -469,8 +469,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Step-staged variant for batches whose paired activations exceed LDS, where
-// a CU's share is at most 24 rows: the workgroup's first waves compute (R rows
+// Step-staged variant for batches whose paired activations exceed LDS, and for
+// one row of long activations, where a CU's share is at most 24 rows: the
+// workgroup's first waves compute (R rows
 // per half wave, every half wave taking its rows' chunks in ascending order,
 // all in step), the last ceil(B / 2) waves only stage the activations of the
 // batch, one chunk at a time, into two LDS buffers (chunk c + 1 is stored
@@ -480,11 +481,12 @@ __device__ __forceinline__ void lds_barrier() {
 // accumulator per batch row, the same lane tree; a lane past the end of a
 // short last chunk reads lane 0 of chunk 0, kept in LDS for the purpose, and
 // adds exact zeros), so the bits are the same, and the weights are read once
-// for the whole batch.  P: items of codes in flight per half wave; PS: chunks
-// of activations in flight per staging lane.
+// for the whole batch; the codes stream from the first chunk on instead of
+// after all of x is staged.  P: items of codes in flight per half wave; PS:
+// chunks of activations in flight per staging lane.
 // AM: the argmax epilogue as in gemv_valu_kernel.
 template <int B, int R, int P, int PS, bool RAGGED, bool AM, int BITS = 4>
-__global__ __launch_bounds__(512) void gemv_valu_step_kernel(const uint32_t* __restrict__ wq,
+__global__ __launch_bounds__(B == 1 ? 1024 : 512) void gemv_valu_step_kernel(const uint32_t* __restrict__ wq,
                                                              const uint16_t* __restrict__ scales,
                                                              const uint16_t* __restrict__ biases,
                                                              const uint16_t* __restrict__ x,
@@ -966,11 +968,16 @@ int batch_parts(int B, int64_t K) {
 // 24 rows (decided with the MI355X's CU count, so that the records of the
 // fused head stay within the bound computed the same way), the step-staged
 // kernel reads the weights once for the whole batch (down at B = 8: 40 us in
-// two parts before).  Four computing waves of 2 x 3 rows: one per SIMD.
-constexpr int kStepR = 3;
-constexpr int64_t kStepRows = 8 * kStepR;
+// two parts before), with four computing waves of 2 x 3 rows (one per SIMD).
+// At B = 1 it takes shares of at most 20 rows whose x spans 8 chunks or more,
+// one row per half wave, so that the codes stream while x is staged (down at
+// B = 1: 11.8 -> 10.4 us; o_proj, 5 chunks, gains nothing).
+constexpr int64_t kStepRows = 24;
+constexpr int step_r(int B) { return B == 1 ? 1 : 3; }
 bool use_step(int B, int64_t N, int64_t K) {
-  return (batch_parts(B, K) > 1 || use_regs(B, K, false)) && per_cu_rows(N, kMaxCUs) <= kStepRows;
+  const int64_t r = per_cu_rows(N, kMaxCUs);
+  if (B == 1 && r <= 20 && K >= 8 * kChunk) return true;
+  return (batch_parts(B, K) > 1 || use_regs(B, K, false)) && r <= kStepRows;
 }
 int64_t step_rows(int64_t N, int cus) {
   const int64_t r = per_cu_rows(N, cus);
@@ -987,18 +994,20 @@ hipError_t launch_step(const uint32_t* wq, const uint16_t* scales, const uint16_
                        hipStream_t stream) {
   const int64_t rpw = step_rows(N, cu_count());
   const int64_t blocks = (N + rpw - 1) / rpw;
-  const int ncw = (int)((rpw + 2 * kStepR - 1) / (2 * kStepR));  // computing waves
-  const int threads = 64 * (ncw + (B + 1) / 2);                  // then the staging waves
+  const int ncw = (int)((rpw + 2 * step_r(B) - 1) / (2 * step_r(B)));  // computing waves
+  const int threads = 64 * (ncw + (B + 1) / 2);                        // then the staging waves
   const bool ragged = (K % kChunk) != 0;
   const size_t lds = step_lds_bytes(B, ragged);
   switch (B) {
 #define W4G_STEP(BB)                                                                                        \
     case BB:                                                                                                \
       if (ragged)                                                                                           \
-        hipLaunchKernelGGL((gemv_valu_step_kernel<BB, kStepR, 2, 3, true, AM, BITS>), dim3((unsigned)blocks), \
+        hipLaunchKernelGGL((gemv_valu_step_kernel<BB, step_r(BB), 2, BB == 1 ? 5 : 3, true, AM, BITS>),       \
+                           dim3((unsigned)blocks),                                                          \
                            dim3(threads), lds, stream, wq, scales, biases, x, y, N, K, rpw, ncw, rec);      \
       else                                                                                                  \
-        hipLaunchKernelGGL((gemv_valu_step_kernel<BB, kStepR, 2, 3, false, AM, BITS>), dim3((unsigned)blocks), \
+        hipLaunchKernelGGL((gemv_valu_step_kernel<BB, step_r(BB), 2, BB == 1 ? 5 : 3, false, AM, BITS>),      \
+                           dim3((unsigned)blocks),                                                          \
                            dim3(threads), lds, stream, wq, scales, biases, x, y, N, K, rpw, ncw, rec);      \
       return hipGetLastError();
     W4G_STEP(1) W4G_STEP(2) W4G_STEP(3) W4G_STEP(4) W4G_STEP(5) W4G_STEP(6) W4G_STEP(7) W4G_STEP(8)
