@@ -320,17 +320,20 @@ def test_gemm_kernels_agree_bitwise(M, N, K):
 
 
 def test_gemm_tile_variants_bitwise():
-    """The three main loops (register-staged 128 x 128 tiles from 512 tiles up,
-    LDS-load 128 x 128 from 256, LDS-load 64 x 64 below) follow one order: the
-    rows they share are bitwise equal, and sampled columns match the oracle."""
+    """The main loops (register-staged 128 x 128 tiles from 512 tiles up,
+    LDS-load 128 x 128 from 256, LDS-load 64 x 128 from 128, LDS-load 64 x 64
+    below) follow one order: the rows they share are bitwise equal, and sampled
+    columns match the oracle."""
     N, K = 8155, 256                      # 64 column tiles of 128, the last ragged
     wq, sc, bi, x = _case(N, K, 1000, 77)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
     X = up_bf16(x)
     y_reg = down(w4g.qmm_gemm(*W, X))                         # 8 x 64 = 512 tiles
     y_lds = down(w4g.qmm_gemm(*W, X[:500].contiguous()))      # 4 x 64 = 256 tiles
+    y_half = down(w4g.qmm_gemm(*W, X[:300].contiguous()))     # 3 x 64 = 192: 64 x 128 tiles
     y_small = down(w4g.qmm_gemm(*W, X[:100].contiguous()))    # 64 x 64 tiles
     assert np.array_equal(y_lds.view(np.uint32), y_reg[:500].view(np.uint32))
+    assert np.array_equal(y_half.view(np.uint32), y_reg[:300].view(np.uint32))
     assert np.array_equal(y_small.view(np.uint32), y_reg[:100].view(np.uint32))
     cols = np.unique(np.concatenate([np.arange(40), np.arange(N - 40, N),
                                      np.random.default_rng(5).choice(N, 60, replace=False)]))

@@ -28,9 +28,10 @@
 // groups at a time.  Four main loops share that arithmetic: 128 x 128 tiles
 // (each wave 64 x 64, 2 x 2 matrix-core tiles) with the operands staged
 // through registers (two workgroups per CU) when there are tiles enough for
-// that; 128 x 128 tiles loaded straight into an LDS ring (one workgroup per
-// CU) when fewer; and 64 x 64 tiles (each wave one 32 x 32 matrix-core tile)
-// through a ring of LDS loads for short prompts and small grids.  Prompts of
+// that; tiles loaded straight into an LDS ring when fewer: 128 x 128 (one
+// workgroup per CU) while they cover the CUs, 64 x 128 (each wave 32 x 64,
+// two workgroups per CU) where they cover half of them, and 64 x 64 (each wave
+// one 32 x 32 matrix-core tile) for short prompts and small grids.  Prompts of
 // at most 32 rows over narrow matrices take a fourth loop that deals each
 // tile's groups to eight waves and passes the group products on through LDS
 // (a tile's K chain would otherwise run on one wave).  The bias terms and the
@@ -978,7 +979,8 @@ namespace {
 //   the register-staged loop with 128 x 128 tiles when there are enough tiles
 //   for two workgroups per CU (or when the LDS-load kernel does not apply),
 //   the LDS-load loop with 128 x 128 tiles while they still cover every CU,
-//   and the LDS-load loop with 64 x 64 tiles (a deeper ring) below that.
+//   with 64 x 128 tiles (two workgroups per CU) where they cover half of them
+//   or more, and with 64 x 64 tiles (a deeper ring) below that.
 template <typename OUT>
 hipError_t launch_main(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                        const uint16_t* xp, const uint16_t* xs, OUT* y, int64_t M, int64_t N,
@@ -1023,6 +1025,13 @@ hipError_t launch_main(const uint32_t* wq, const uint16_t* scales, const uint16_
         const int64_t NT = (Ns + kTN - 1) / kTN, per = (tiles128 + 7) / 8;
         hipLaunchKernelGGL(gemm_kernel<OUT>, dim3((unsigned)(8 * per)), dim3(256), 0, stream, w_s, s_s,
                            b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles128, per, vec);
+      } else if (tiles128 < cu_count()) {
+        // 128 x 128 tiles would leave CUs idle: 64 x 128 tiles, a 3-stage ring
+        // (74 KiB) so two share a CU (o_proj and down at 512 rows, 160 tiles of
+        // 128 x 128: 67 -> 64 and 202 -> 195 us)
+        const int64_t NT = (Ns + 127) / 128, tiles = ((Ms + 63) / 64) * NT, per = (tiles + 7) / 8;
+        hipLaunchKernelGGL((gemm_dma_kernel<1, 2, 2, 2, 3, OUT>), dim3((unsigned)(8 * per)), dim3(256), 0,
+                           stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles, per, vec);
       } else {
         const int64_t NT = (Ns + kTN - 1) / kTN, per = (tiles128 + 7) / 8;
         hipLaunchKernelGGL((gemm_dma_kernel<2, 2, 2, 2, 3, OUT>), dim3((unsigned)(8 * per)), dim3(256), 0,
