@@ -260,7 +260,11 @@ def test_workspace_sizes(lib):
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 4, 5120, 17408) == 4 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 5, 5120, 17408) == 5 * 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 5120, 17408) == 8 * 256 * 8
-    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 3, 300, 73728) == 3 * 75 * 8
+    # x too long for LDS over at most 24 rows per CU: the step-staged kernel, one
+    # record per CU share (2 rows here); also at B = 1 where x spans 8 chunks or more
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 3, 300, 73728) == 3 * 150 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 3000, 17408) == 1 * 250 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 3000, 5120) == 1 * 250 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 9000, 10240) == 8 * 250 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 600000, 40960) == 8 * 150000 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 9, 248320, 5120) == size_max

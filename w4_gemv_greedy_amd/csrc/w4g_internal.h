@@ -62,8 +62,8 @@ hipError_t launch_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const 
 int64_t gemv_argmax_records(int B, int64_t N, int64_t K);
 // An upper bound of gemv_argmax_records on any device (for workspace sizes).
 int64_t gemv_argmax_records_max(int B, int64_t N, int64_t K);
-// The matrix-core family's epilogue variant: one record per workgroup (per CU,
-// or per 32 rows where the activations are staged in stages).
+// The matrix-core family's epilogue variant: one record per workgroup (one
+// workgroup per CU share, whether x is held whole or staged step by step).
 hipError_t launch_gemv_mfma_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                                    const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                                    hipStream_t stream);
