@@ -184,6 +184,27 @@ def test_gemv_valu_step_staged(N, K, bits):
         assert np.array_equal(ids_down(ids), oracle.argmax(y8))
 
 
+@pytest.mark.parametrize("B", [2, 5, 8])
+def test_gemv_wide_share_layout(B):
+    """More than 512 rows per CU (the vocabulary-wide head's layout at B >= 2:
+    four rows per half wave) over a ragged share and a ragged last chunk: every
+    batch row bitwise equal to the row alone, sampled rows against the oracle,
+    and the fused argmax epilogue equal to the two-pass argmax."""
+    N, K = 140001, 1088
+    wq, sc, bi, x = _case(N, K, B, 60 + B)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y = down(w4g.qmm_gemv(*W, up_bf16(x)))
+    for m in (0, B - 1):
+        y1 = down(w4g.qmm_gemv(*W, up_bf16(x[m:m + 1])))
+        assert np.array_equal(y1[0].view(np.uint32), y[m].view(np.uint32)), f"row {m} differs at B=1"
+    rows = np.unique(np.r_[0:600, N - 600:N, np.random.default_rng(B).choice(N, 200, replace=False)])
+    assert_close(y[:, rows], oracle.qmm(wq[rows], sc[rows], bi[rows], x), f"wide share B={B}")
+    ids, logits = w4g.qmm_gemv_argmax(*W, up_bf16(x))
+    assert np.array_equal(down(logits).view(np.uint32), y.view(np.uint32))
+    assert np.array_equal(ids_down(ids), ids_down(w4g.vocab_argmax(up_f32(y))))
+    assert np.array_equal(ids_down(ids), oracle.argmax(y))
+
+
 @pytest.mark.parametrize("N,K", [(9477, 1024), (8193, 3072), (5120, 2048), (300, 17408)])
 def test_gemv_per_cu_layout(N, K):
     """B = 1 with one workgroup per CU (an equal share of rows each, half waves

@@ -896,10 +896,10 @@ hipError_t launch_per_cu(const uint32_t* wq, const uint16_t* scales, const uint1
                          const uint16_t* x, float* y, int64_t N, int64_t K, hipStream_t stream,
                          uint2* rec = nullptr) {
   const int64_t rpw = per_cu_rows(N);
-  // (R = 2 at B >= 2 runs only for shares above 40 rows, so that pairing never
+  // (R >= 2 at B >= 2 runs only for shares above 40 rows, so that it never
   // takes the 640-thread variant, which is not built for it; nor are 8-bit
   // codes at B >= 7, whose registers exceed the 640-thread budget)
-  if constexpr (!(R == 2 && B >= 2) && !(BITS == 8 && B >= 7)) {
+  if constexpr (!(R >= 2 && B >= 2) && !(BITS == 8 && B >= 7)) {
     if (rpw <= 20 * R)
       return launch_lds<B, R, P, AM, 640, BITS>(wq, scales, biases, x, y, rec, N, K, rpw,
                                                 64 * (int)((rpw + 2 * R - 1) / (2 * R)), stream);
@@ -934,19 +934,23 @@ int lds_rows(int64_t K) {
 }
 
 // The per-CU layout for any batch (1..8): R = 2 over more than 40 rows per CU
-// at B >= 2.  Every batch size takes the same workgroups, so the batch can be
-// cut into parts that write their records side by side.
+// at B >= 2, R = 4 over more than 512 (the vocabulary-wide head: each pass of
+// the activations through LDS feeds twice the rows; measured at B = 2..8,
+// 3-11% faster than R = 2).  Every batch size takes the same workgroups, so the
+// batch can be cut into parts that write their records side by side.
 template <bool AM>
 hipError_t launch_per_cu_any(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                              const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
                              hipStream_t stream) {
   if (B == 1) return launch_per_cu<1, 4, 4, 1, AM>(wq, scales, biases, x, y, N, K, stream, rec);
-  const bool two = per_cu_rows(N) > 40;  // (R = 2 then always strides: 512 threads)
+  const int64_t rows = per_cu_rows(N);
+  const bool two = rows > 40, four = rows > 512;  // (R >= 2 then always strides: 512 threads)
   switch (B) {
 #define W4G_PER_CU(BB)                                                                               \
     case BB:                                                                                         \
-      return two ? launch_per_cu<2, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec)       \
-                 : launch_per_cu<1, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec);
+      return four  ? launch_per_cu<4, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec)     \
+             : two ? launch_per_cu<2, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec)     \
+                   : launch_per_cu<1, 2, 4, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec);
     W4G_PER_CU(2) W4G_PER_CU(3) W4G_PER_CU(4) W4G_PER_CU(5) W4G_PER_CU(6) W4G_PER_CU(7) W4G_PER_CU(8)
 #undef W4G_PER_CU
     default: return hipErrorInvalidValue;
