@@ -102,6 +102,64 @@ __device__ __forceinline__ float half_wave_sum(float v) {
   return v;
 }
 
+// The same tree for NB values at once (NB = 2, 4 or 8; batch rows past B
+// enter as zeros), transposed: each step adds the same pairs of lanes as
+// half_wave_sum, in the same operand order, but a lane keeps only half of the
+// values it holds, the half its partner does not keep.  The 16-lane row swap
+// leaves value 2k's pair sums in row 0 and value 2k + 1's in row 1 (one
+// v_permlane16_swap per pair of values); mirror and half mirror then split by
+// lane bits 3 and 2 the same way; the quad swaps add what is left.  So every
+// value's total has the bits half_wave_sum gives it, and lane i of the half
+// wave ends with the total of value half_wave_index<NB>(i): NB - 1 + ... + 1
+// swaps and about 2 NB instructions in all, not 10 NB.
+template <int NB>
+__device__ __forceinline__ int half_wave_index(int lane) {
+  int t = (lane >> 4) & 1;
+  if constexpr (NB >= 4) t |= ((lane >> 3) & 1) << 1;
+  if constexpr (NB >= 8) t |= ((lane >> 2) & 1) << 2;
+  return t;
+}
+// lanes of a half wave that hold value t: the first of each group of 32 / NB
+template <int NB>
+__device__ __forceinline__ bool half_wave_first(int lane) {
+  return (lane & (32 / NB - 1)) == 0;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_keep_add(float lo_keep, float hi_keep, bool hi) {
+  // keep one of two values and add the partner's copy of the same value
+  const float keep = hi ? hi_keep : lo_keep;
+  const float send = hi ? lo_keep : hi_keep;
+  const int o = __builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xF, 0xF, false);
+  return keep + __int_as_float(o);
+}
+template <int NB>
+__device__ __forceinline__ float half_wave_sums(const float (&v)[NB], int lane) {
+  static_assert(NB == 2 || NB == 4 || NB == 8, "2, 4 or 8 values");
+  float a[NB / 2];
+#pragma unroll
+  for (int k = 0; k < NB / 2; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * k]), __float_as_uint(v[2 * k + 1]),
+                                                    false, false);
+    a[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  float t;
+  if constexpr (NB == 2) {
+    t = dpp_add<0x140>(a[0]);
+    t = dpp_add<0x141>(t);
+  } else if constexpr (NB == 4) {
+    t = dpp_keep_add<0x140>(a[0], a[1], (lane & 8) != 0);
+    t = dpp_add<0x141>(t);
+  } else {
+    const float b0 = dpp_keep_add<0x140>(a[0], a[1], (lane & 8) != 0);
+    const float b1 = dpp_keep_add<0x140>(a[2], a[3], (lane & 8) != 0);
+    t = dpp_keep_add<0x141>(b0, b1, (lane & 4) != 0);
+  }
+  t = dpp_add<0x4E>(t);
+  t = dpp_add<0xB1>(t);
+  return t;
+}
+constexpr int sums_width(int B) { return B <= 2 ? 2 : B <= 4 ? 4 : 8; }
+
 // Other code widths (2 and 8 bits: 32/bits codes per uint32, low field first).
 // 2-bit: word t of a lane's 32 elements covers elements 16t .. 16t + 15; field j
 // and field j + 8 go to one bf16 pair (128 + q[j], 128 + q[j + 8]) with one
@@ -385,26 +443,40 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
         }
       }
       if (++cc == C) {
-        // every lane holds every sum; lane bb (< B) takes batch row bb's, so
-        // the stores and the argmax fold of a group are one branch, not one per
-        // (row, batch row)
+        // B = 1: every lane holds the sum and lane 0 stores it; B >= 2: the
+        // transposed tree leaves batch row bq's sum in lanes of its own, and
+        // the first of them stores it, so the stores and the argmax fold of a
+        // group are one branch, not one per (row, batch row)
         float mine[R];
+        int bq = 0;
+        bool st = lane == 0;
+        if constexpr (B == 1) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+          for (int r = 0; r < R; ++r) {
+            mine[r] = half_wave_sum(acc[r][0]);
+            acc[r][0] = 0.0f;
+          }
+        } else {
+          constexpr int NB = sums_width(B);
+          bq = half_wave_index<NB>(lane);
+          st = half_wave_first<NB>(lane) && bq < B;
 #pragma unroll
-          for (int bb = 0; bb < B; ++bb) {
-            const float v = half_wave_sum(acc[r][bb]);
-            mine[r] = bb == 0 ? v : (lane == bb ? v : mine[r]);
-            acc[r][bb] = 0.0f;
+          for (int r = 0; r < R; ++r) {
+            float v[NB];
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) v[bb] = bb < B ? acc[r][bb < B ? bb : 0] : 0.0f;
+            mine[r] = half_wave_sums<NB>(v, lane);
+#pragma unroll
+            for (int bb = 0; bb < B; ++bb) acc[r][bb] = 0.0f;
           }
         }
-        if (lane < B) {
+        if (st) {
           uint64_t best = 0;
           bool bad = false;
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             if (crow + r < wg_end) {
-              if (!AM || y != nullptr) y[(int64_t)lane * N + crow + r] = mine[r];
+              if (!AM || y != nullptr) y[(int64_t)bq * N + crow + r] = mine[r];
               if constexpr (AM) {
                 const uint32_t u = __float_as_uint(mine[r]);
                 if (!finite_bits(u)) bad = true;
@@ -414,9 +486,9 @@ __global__ __launch_bounds__(MAXT) void gemv_valu_kernel(const uint32_t* __restr
           }
           if constexpr (AM) {
             // (a candidate word is never 0: every finite value's key is above 0)
-            if (bad) __hip_atomic_fetch_or(&s_bad, 1u << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (bad) __hip_atomic_fetch_or(&s_bad, 1u << bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (best)
-              __hip_atomic_fetch_max(&s_best[lane], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              __hip_atomic_fetch_max(&s_best[bq], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           }
         }
         cc = 0;
@@ -693,28 +765,38 @@ __global__ __launch_bounds__(B == 1 ? 1024 : 512) void gemv_valu_step_kernel(con
   for (int k = 0; k < P; ++k)
     if (c + P + k < C) consume(ring[k], c + P + k);
 
-  // the rows' sums (every lane holds them); lane bb stores batch row bb's
+  // the rows' sums: B = 1, every lane holds them and lane 0 stores; B >= 2,
+  // the transposed tree leaves batch row bq's in lanes of its own
   float mine[R];
+  int bq = 0;
+  bool st = lane == 0;
+  if constexpr (B == 1) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < R; ++r) mine[r] = half_wave_sum(acc[r][0]);
+  } else {
+    constexpr int NB = sums_width(B);
+    bq = half_wave_index<NB>(lane);
+    st = half_wave_first<NB>(lane) && bq < B;
 #pragma unroll
-    for (int bb = 0; bb < B; ++bb) {
-      const float v = half_wave_sum(acc[r][bb]);
-      mine[r] = bb == 0 ? v : (lane == bb ? v : mine[r]);
+    for (int r = 0; r < R; ++r) {
+      float v[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) v[bb] = bb < B ? acc[r][bb < B ? bb : 0] : 0.0f;
+      mine[r] = half_wave_sums<NB>(v, lane);
     }
   }
-  if (lane < B) {
+  if (st) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t row = row0 + r;
       if (row < wg_end) {
-        if (!AM || y != nullptr) y[(int64_t)lane * N + row] = mine[r];
+        if (!AM || y != nullptr) y[(int64_t)bq * N + row] = mine[r];
         if constexpr (AM) {
           const uint32_t u = __float_as_uint(mine[r]);
           if (!finite_bits(u))
-            __hip_atomic_fetch_or(&s_bad, 1u << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_or(&s_bad, 1u << bq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           else
-            __hip_atomic_fetch_max(&s_best[lane], cand(u, (uint32_t)row), __ATOMIC_RELAXED,
+            __hip_atomic_fetch_max(&s_best[bq], cand(u, (uint32_t)row), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
         }
       }
