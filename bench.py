@@ -462,6 +462,44 @@ def ceilings(torch, layers, dev, timed):
         del bufs
     torch.cuda.empty_cache()
 
+    # the codes of each layer matrix read in the shape of one wave load of a decode
+    # kernel (non-temporal 16-byte loads): which load layouts can stream at HBM rate
+    lib.w4g_ceiling_read_rows.argtypes = [P, ctypes.c_int64, ctypes.c_int64, I, I, I, I, P, P]
+    lib.w4g_ceiling_read_rows.restype = I
+    pats = ((0, "half_wave_512B_per_row", 2, 512), (1, "mfma16_in_place_64B_per_row", 16, 64),
+            (2, "mfma16_adjacent_lanes_64B_per_row", 16, 64), (3, "mfma32_in_place_32B_per_row", 32, 32))
+    out["code_load_layouts"] = {}
+    for name, rows, K, copies in (("o_proj", HIDDEN, HIDDEN, 40), ("gate_up", 2 * INTER, HIDDEN, 6),
+                                  ("down", HIDDEN, INTER, 12)):
+        rb = K // 2
+        bufs = [torch.full((rows * rb,), c, dtype=torch.uint8, device=dev) for c in range(copies)]
+        launches = max(16, copies)
+        entry = {"bytes": rows * rb}
+        for pat, key, tr, per in pats:
+            tiles = -(-rows // tr)
+            # whole rows per unit where there are enough tiles, else the most slices
+            # per row that keep the units at 4096 or fewer; one workgroup per CU,
+            # one unit per wave up to 4096 units, else 8 waves striding through them
+            cands = [k for k in range(1, rb // per + 1) if rb % (k * per) == 0 and tiles * k <= 4096]
+            sl = cands[-1] if cands else 1
+            units = tiles * sl
+            blocks = 256
+            threads = 64 * max(1, min(16, -(-units // blocks))) if units <= 4096 else 512
+
+            def run(pat=pat, sl=sl, blocks=blocks, threads=threads):
+                for i in range(launches):
+                    st = lib.w4g_ceiling_read_rows(bufs[i % copies].data_ptr(), rows, rb, pat, sl, blocks, threads,
+                                                   sink.data_ptr(), stream())
+                    if st != 0:
+                        raise RuntimeError(f"w4g_ceiling_read_rows: hip error {st}")
+            ms, _ = timed(run, 10, 2, True)
+            us = ms * 1e3 / launches
+            entry[key] = {"us": round(us, 2), "GBps": round(rows * rb / (us * 1e-6) / 1e9, 1), "slices": sl,
+                          "launch": f"{blocks}x{threads}"}
+        out["code_load_layouts"][name] = entry
+        del bufs
+    torch.cuda.empty_cache()
+
     blocks, iters = 1024, 400
     flop = blocks * 4 * iters * 8 * 32768
 

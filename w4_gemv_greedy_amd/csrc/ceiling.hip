@@ -9,6 +9,17 @@
 // fixed constant (never, for the benchmark's buffers), so the loads cannot be
 // dropped.
 //
+// w4g_ceiling_read_rows: a read-only stream of a row-major [rows][row_bytes]
+// matrix in the shape of one wave load instruction of a decode kernel, with
+// non-temporal 16-byte loads: pattern 0, a half wave per row (32 lanes read a
+// row's 512 contiguous bytes: the vector-ALU decode); pattern 1, 16 rows x 64
+// bytes with lane l on row l % 16, bytes 16 (l / 16) (a 16 x 16 x 32
+// matrix-core operand loaded in place); pattern 2, the same 16 x 64 bytes with
+// four adjacent lanes per row; pattern 3, 32 rows x 32 bytes with lane l on
+// row l % 32 (a 32 x 32 x 16 operand in place).  Work units are (tile of rows,
+// slice of the row) spread over all waves of the grid, up to 8 loads in flight
+// per lane.
+//
 // w4g_ceiling_mfma: every wave issues `iters` rounds of eight independent
 // v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 each, 32,768 FLOP), with no memory
 // traffic, and stores only if a result equals a fixed constant.
@@ -44,6 +55,61 @@ __global__ __launch_bounds__(1024) void read_kernel(const uint4* __restrict__ p,
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+template <int PAT>
+struct RowPattern {
+  static constexpr int rows = PAT == 0 ? 2 : PAT == 3 ? 32 : 16;     // rows per wave load
+  static constexpr int bytes = PAT == 0 ? 512 : PAT == 3 ? 32 : 64;  // bytes per row per wave load
+};
+
+template <int PAT, int U>
+__global__ __launch_bounds__(1024) void read_rows_kernel(const uint8_t* __restrict__ p, int64_t rows,
+                                                        int64_t row_bytes, int ks, uint32_t* __restrict__ sink) {
+  typedef RowPattern<PAT> RP;
+  const int lane = threadIdx.x & 63;
+  int r, off;
+  if (PAT == 0) {
+    r = lane >> 5;
+    off = 16 * (lane & 31);
+  } else if (PAT == 1) {
+    r = lane & 15;
+    off = 16 * (lane >> 4);
+  } else if (PAT == 2) {
+    r = lane >> 2;
+    off = 16 * (lane & 3);
+  } else {
+    r = lane & 31;
+    off = 16 * (lane >> 5);
+  }
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t tiles = (rows + RP::rows - 1) / RP::rows;
+  const int64_t seg = row_bytes / ks;       // a multiple of RP::bytes (checked by the host)
+  const int steps = (int)(seg / RP::bytes);
+  uint32_t acc = 0;
+  for (int64_t u = wave; u < tiles * ks; u += waves) {
+    const int64_t t = u / ks, k = u - t * ks;
+    int64_t row = t * RP::rows + r;
+    row = row < rows ? row : rows - 1;  // a partial last tile rereads the last row
+    const uint8_t* base = p + row * row_bytes + k * seg + off;
+    for (int s0 = 0; s0 < steps; s0 += U) {
+      uint4 v[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if (s0 + j < steps) {
+          const u32x4_c q =
+              __builtin_nontemporal_load(reinterpret_cast<const u32x4_c*>(base + (int64_t)(s0 + j) * RP::bytes));
+          v[j] = make_uint4(q[0], q[1], q[2], q[3]);
+        } else {
+          v[j] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
@@ -95,6 +161,30 @@ int w4g_ceiling_read(const void* p, size_t bytes, int blocks, int threads, int l
     W4G_READ(2, 0) W4G_READ(2, 1) W4G_READ(4, 0) W4G_READ(4, 1) W4G_READ(8, 0) W4G_READ(8, 1)
 #undef W4G_READ
     default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+// Returns a hipError_t value; 1 (hipErrorInvalidValue) for a bad pattern, size
+// or launch shape.  `slices` cuts each row into that many equal slices (so that
+// there are enough work units for every wave); row_bytes must be a multiple of
+// slices times the pattern's bytes per row per load (512, 64, 64, 32).
+int w4g_ceiling_read_rows(const void* p, int64_t rows, int64_t row_bytes, int pattern, int slices, int blocks,
+                          int threads, uint32_t* sink, void* stream) {
+  static const int per_load[4] = {512, 64, 64, 32};
+  if (!p || !sink || rows < 1 || row_bytes < 1 || pattern < 0 || pattern > 3 || slices < 1 || blocks < 1 ||
+      threads < 64 || threads > 1024 || threads % 64 || row_bytes % ((int64_t)slices * per_load[pattern]))
+    return (int)hipErrorInvalidValue;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* q = reinterpret_cast<const uint8_t*>(p);
+  switch (pattern) {
+#define W4G_ROWS(PAT)                                                                                        \
+    case PAT:                                                                                                \
+      hipLaunchKernelGGL((read_rows_kernel<PAT, 8>), dim3(blocks), dim3(threads), 0, s, q, rows, row_bytes,  \
+                         slices, sink);                                                                      \
+      break;
+    W4G_ROWS(0) W4G_ROWS(1) W4G_ROWS(2) W4G_ROWS(3)
+#undef W4G_ROWS
   }
   return (int)hipGetLastError();
 }
