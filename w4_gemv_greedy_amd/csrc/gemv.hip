@@ -1050,19 +1050,24 @@ int batch_parts(int B, int64_t K) {
   return b >= 2 && B > b ? (B + b - 1) / b : 1;
 }
 
-// Where the batch's activations do not fit in LDS and a CU's share is at most
-// 24 rows (decided with the MI355X's CU count, so that the records of the
-// fused head stay within the bound computed the same way), the step-staged
-// kernel reads the weights once for the whole batch (down at B = 8: 40 us in
-// two parts before), with four computing waves of 2 x 3 rows (one per SIMD).
-// At B = 1 it takes shares of at most 20 rows whose x spans 8 chunks or more,
-// one row per half wave, so that the codes stream while x is staged (down at
-// B = 1: 11.8 -> 10.4 us; o_proj, 5 chunks, gains nothing).
+// Where a CU's share is at most 24 rows (decided with the MI355X's CU count,
+// so that the records of the fused head stay within the bound computed the
+// same way) the step-staged kernel serves every batch of three rows or more:
+// it reads the weights once for the whole batch where the batch's activations
+// do not fit in LDS (down at B = 8: 40 us in two parts before), and where they
+// do, staging them a chunk at a time while the codes stream beats staging them
+// whole first (o_proj at B = 3 / 8: 8.1 -> 7.7 / 11.9 -> 11.5 us, down at
+// B = 3 / 4: 17.5 -> 16.0 / 19.8 -> 18.7 us; B = 2 gains nothing certain).
+// Four computing waves of 2 x 3 rows (one per SIMD).  At B = 1 it takes shares
+// of at most 20 rows whose x spans 8 chunks or more, one row per half wave, so
+// that the codes stream while x is staged (down at B = 1: 11.8 -> 10.4 us;
+// o_proj, 5 chunks, gains nothing).
 constexpr int64_t kStepRows = 24;
 constexpr int step_r(int B) { return B == 1 ? 1 : 3; }
 bool use_step(int B, int64_t N, int64_t K) {
   const int64_t r = per_cu_rows(N, kMaxCUs);
   if (B == 1 && r <= 20 && K >= 8 * kChunk) return true;
+  if (B >= 3 && r <= kStepRows) return true;
   return (batch_parts(B, K) > 1 || use_regs(B, K, false)) && r <= kStepRows;
 }
 int64_t step_rows(int64_t N, int cus) {
