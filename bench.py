@@ -669,7 +669,15 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args, make_step):
     ms, _ = timed(head8_step, 10, 2, True, reps=4)
     ex["w8_lm_head_argmax_us_per_token"] = round(ms * 1e3, 2)
     ex["w8_lm_head_argmax_GBps"] = round((1.0625 * VOCAB * HIDDEN + 2 * HIDDEN + 8 * VOCAB) / (ms * 1e-3) / 1e9, 1)
-    del head8
+    # the same head with the argmax's first pass fused into the product (ids only)
+    ws8 = torch.empty(w4g.workspace_bytes(w4g.OP_GEMV_BITS_ARGMAX, 1, VOCAB, HIDDEN), dtype=torch.uint8,
+                      device=dev)
+
+    def head8_fused():
+        w4g.qmm_gemv_argmax(head8.wq, head8.sc, head8.bi, xh, ids=ids, workspace=ws8, want_logits=False, bits=8)
+    ms, _ = timed(head8_fused, 10, 2, True, reps=4)
+    ex["w8_lm_head_argmax_fused_ids_only_us_per_token"] = round(ms * 1e3, 2)
+    del head8, ws8
     xg1 = make_x(1, HIDDEN, 5, synth.GATE_UP, 0, dev)
     yg1 = torch.empty((1, 2 * INTER), dtype=torch.float32, device=dev)
     for bits, copies in ((8, 4), (2, 6)):
@@ -684,7 +692,8 @@ def secondary(torch, w4g, synth, layers, head, dev, timed, args, make_step):
         ex[f"w{bits}_gate_up_b1"] = {"us": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
         del mats
     log(f"other widths: w8 lm_head+argmax {ex['w8_lm_head_argmax_us_per_token']} us/token "
-        f"({ex['w8_lm_head_argmax_GBps']} GB/s), w8 gate_up {ex['w8_gate_up_b1']}, w2 gate_up {ex['w2_gate_up_b1']}")
+        f"({ex['w8_lm_head_argmax_GBps']} GB/s; fused, ids only "
+        f"{ex['w8_lm_head_argmax_fused_ids_only_us_per_token']}), w8 gate_up {ex['w8_gate_up_b1']}, w2 gate_up {ex['w2_gate_up_b1']}")
     torch.cuda.empty_cache()
 
     # prompt products: the 512-row pass, the 128-row round and short prompts of 64

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define W4G_ABI_VERSION 2
+#define W4G_ABI_VERSION 3
 #define W4G_SENTINEL 0xFFFFFFFFu
 #define W4G_MAX_GEMV_BATCH 8
 
@@ -90,6 +90,7 @@ extern "C" {
 #define W4G_OP_ARGMAX 2
 #define W4G_OP_GEMV_ARGMAX 3
 #define W4G_OP_ARGMAX_TOP2 4
+#define W4G_OP_GEMV_BITS_ARGMAX 5
 
 /*
  * Decode product, 1 <= B <= 8 activation rows.
@@ -259,6 +260,28 @@ int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
                     int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qmm_gemv_argmax at another code width: the greedy head over a 2- or 8-bit
+ * affine group-64 matrix (the W8 LM head the B70 page serves, "Reproduce
+ * Qwen3.6 27B AutoRound Bring-Up": a runtime INT8 target LM head; other widths
+ * take their own kernel variant, TensorFold PR #1433, owner's review of step
+ * 2), with the argmax's first pass fused into the product's epilogue as in
+ * qmm_gemv_argmax.
+ *   wq, scales, biases, x, B, N, K, bits: as qmm_gemv_bits (bits 2, 4 or 8,
+ *   else W4G_EDTYPE; 4 is qmm_gemv_argmax); N < 2^31.
+ *   logits [B][N] fp32, or NULL: when given, exactly the bits qmm_gemv_bits
+ *   writes for the same (B, N, K, bits).
+ *   ids [B] uint32: as qmm_gemv_argmax, always equal to vocab_argmax over
+ *   those logits.
+ *   workspace: at least qmm_workspace_bytes(W4G_OP_GEMV_BITS_ARGMAX, B, N, K)
+ *   bytes (the same for 2 and 8 bits), 8-byte aligned.
+ * W4G_ESHAPE where qmm_gemv_bits refuses the shape (one row of x must fit in
+ * LDS: K <= 72,704).
+ */
+int qmm_gemv_bits_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                         const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N, int64_t K,
+                         int bits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * qmm_gemv_argmax for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * arguments without a workspace, the same results bit for bit (logits and
@@ -303,6 +326,7 @@ int vocab_argmax_top2(const void* logits, int dtype, int64_t rows, int64_t vocab
  *   op W4G_OP_ARGMAX: rows = rows, n = vocab, k ignored.
  *   op W4G_OP_GEMV_ARGMAX: rows = B, n = N, k = K.
  *   op W4G_OP_ARGMAX_TOP2: rows = rows, n = vocab (>= 2), k ignored.
+ *   op W4G_OP_GEMV_BITS_ARGMAX: rows = B, n = N, k = K (2- and 8-bit codes).
  * Returns (size_t)-1 for an unknown op or sizes out of range.
  */
 size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k);

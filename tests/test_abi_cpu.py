@@ -55,6 +55,7 @@ def test_constants_match_header(lib):
                  ("W4G_F32", _lib.F32), ("W4G_BF16", _lib.BF16), ("W4G_OP_GEMV", _lib.OP_GEMV),
                  ("W4G_OP_GEMM", _lib.OP_GEMM), ("W4G_OP_ARGMAX", _lib.OP_ARGMAX),
                  ("W4G_OP_GEMV_ARGMAX", _lib.OP_GEMV_ARGMAX), ("W4G_OP_ARGMAX_TOP2", _lib.OP_ARGMAX_TOP2),
+                 ("W4G_OP_GEMV_BITS_ARGMAX", _lib.OP_GEMV_BITS_ARGMAX),
                  ("W4G_GEMV_AUTO", _lib.GEMV_AUTO), ("W4G_GEMV_VALU", _lib.GEMV_VALU),
                  ("W4G_GEMV_MFMA", _lib.GEMV_MFMA), ("W4G_GEMV_VALU_REGS", _lib.GEMV_VALU_REGS)):
         assert val(k) == v, k
@@ -193,6 +194,36 @@ def test_gemv_argmax_rejects(lib):
     assert call(ids=WS) == _lib.EALIAS
 
 
+def test_gemv_bits_argmax_rejects(lib):
+    """The fused head at 2 and 8 bits validates like qmm_gemv_argmax, with the
+    code table sized by the width, and refuses widths other than 2, 4, 8 and K
+    whose one row of x does not fit in LDS, all before any HIP call."""
+    need = lib.qmm_workspace_bytes(_lib.OP_GEMV_BITS_ARGMAX, 2, 5000, 1024)
+    assert need > 0 and need % 16 == 0
+    call = lambda **k: lib.qmm_gemv_bits_argmax(k.get("wq", WQ), SC, BI, X, k.get("lg", Y),
+                                                k.get("ids", IDS), k.get("B", 2), k.get("N", 5000),
+                                                k.get("K", 1024), k.get("bits", 8), k.get("ws", WS),
+                                                k.get("wsb", need), None)
+    for bits in (0, 1, 3, 16):
+        assert call(bits=bits) == _lib.EDTYPE
+    assert call(wq=None) == _lib.EINVAL_PTR
+    assert call(ids=None) == _lib.EINVAL_PTR
+    assert call(B=0) == _lib.ESHAPE
+    assert call(B=9) == _lib.ESHAPE
+    assert call(K=1000) == _lib.ESHAPE
+    assert call(K=80000) == _lib.ESHAPE  # one row of x (80,000 activations) exceeds LDS
+    assert call(lg=Y + 4) == _lib.EALIGN
+    assert call(ids=IDS + 2) == _lib.EALIGN
+    assert call(ws=WS + 4) == _lib.EALIGN
+    assert call(ws=None) == _lib.EWORKSPACE
+    assert call(wsb=need - 8) == _lib.EWORKSPACE
+    assert call(lg=X) == _lib.EALIAS
+    assert call(ws=Y) == _lib.EALIAS
+    # the code table of 5000 rows x 1024 codes: 5,120,000 bytes at 8 bits, 1,280,000 at 2
+    assert call(ids=WQ + 5_000_000) == _lib.EALIAS
+    assert call(bits=2, ids=WQ + 1_279_996) == _lib.EALIAS
+
+
 def test_gemv_argmax_noalloc_rejects(lib):
     """The no-allocation head validates like qmm_gemv_argmax, and refuses sizes
     whose records exceed its 1 MiB static scratch, all before any HIP call."""
@@ -247,9 +278,10 @@ def test_workspace_sizes(lib):
     # fused head: one record per product workgroup and batch row, in the layout
     # of qmm_gemv's own choice, the vector-ALU family for every shape: 32 rows
     # per workgroup for the vocabulary-wide head at B = 1, one workgroup per CU
-    # where x fits in LDS, and also where a batch too large for it is cut into
-    # parts that fit (down from B = 5: two parts), 4 rows per 64-lane workgroup
-    # where not even two rows of x fit (x staged in registers)
+    # where x fits in LDS, also where a batch too large for it is cut into parts
+    # that fit, one per CU share of at most 24 rows for the step-staged kernel
+    # (o_proj and down from B = 3), 4 rows per 64-lane workgroup where not even
+    # two rows of x fit (x staged in registers)
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 248320, 5120) == 7760 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 1, 5120, 5120) == 256 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 4, 248320, 5120) == 4 * 256 * 8
@@ -268,6 +300,17 @@ def test_workspace_sizes(lib):
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 9000, 10240) == 8 * 250 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 8, 600000, 40960) == 8 * 150000 * 8
     assert lib.qmm_workspace_bytes(_lib.OP_GEMV_ARGMAX, 9, 248320, 5120) == size_max
+    # the fused head at 2 and 8 bits: the same layouts (32-row workgroups for the
+    # vocabulary-wide head at B = 1, one workgroup per CU share elsewhere, the
+    # step-staged kernel over at most 24 rows per CU from B = 3 or where x does
+    # not fit); K whose one row of x exceeds LDS is out of range
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_BITS_ARGMAX, 1, 248320, 5120) == 7760 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_BITS_ARGMAX, 8, 248320, 5120) == 8 * 256 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_BITS_ARGMAX, 1, 5120, 5120) == 256 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_BITS_ARGMAX, 8, 5120, 17408) == 8 * 256 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_BITS_ARGMAX, 3, 300, 5120) == 3 * 150 * 8
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_BITS_ARGMAX, 1, 5120, 80000) == size_max
+    assert lib.qmm_workspace_bytes(_lib.OP_GEMV_BITS_ARGMAX, 9, 5120, 5120) == size_max
     assert lib.qmm_workspace_bytes(7, 1, 1, 64) == size_max
 
 

@@ -72,3 +72,68 @@ def test_w8_lm_head_full_size():
     ids = ids_down(w4g.vocab_argmax(logits_t))
     assert ids[0] == oracle.argmax(logits)[0]
     print(f"w8 lm_head: normwise {e:.2e} over {rows.size} rows, id {ids[0]}")
+
+
+def _bits_head(wq, sc, bi, x, bits, want_logits=True):
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    X = up_bf16(x)
+    ids, logits = w4g.qmm_gemv_argmax(*W, X, want_logits=want_logits, bits=bits)
+    ref_logits = w4g.qmm_gemv(*W, X, bits=bits)
+    two_pass = w4g.vocab_argmax(ref_logits)
+    return (ids_down(ids), down(logits) if logits is not None else None, down(ref_logits),
+            ids_down(two_pass))
+
+
+# shapes over every layout the 2- and 8-bit products take: one workgroup per CU
+# share (x whole in LDS), the step-staged kernel (at most 24 rows per CU from
+# B = 3, and where x does not fit), the batch in parts (K = 40,960 holds one row
+# of x in LDS over more than 24 rows per CU), and 32-row workgroups for the
+# vocabulary-wide head at B = 1
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("N,K", [(37, 64), (1000, 1024), (5000, 5120), (3000, 17408), (6400, 40960),
+                                 (140000, 1024)])
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_bits_fused_head_matches_two_pass(N, K, B, bits):
+    """The fused head at 2 and 8 bits: logits bitwise those of qmm_gemv_bits,
+    ids bitwise those of the two-pass argmax over them and of the oracle's
+    argmax of them."""
+    wq, sc, bi, x = _case(N, K, B, bits, N % 89 + B)
+    ids, logits, ref_logits, two_pass = _bits_head(wq, sc, bi, x, bits)
+    assert np.array_equal(logits.view(np.uint32), ref_logits.view(np.uint32)), "logits differ"
+    assert np.array_equal(ids, two_pass), (ids, two_pass)
+    assert np.array_equal(ids, oracle.argmax(ref_logits)), "ids differ from the oracle's argmax"
+    if K <= 1024:
+        assert_close(logits, oracle.qmm(wq, sc, bi, x, bits=bits), f"w{bits} head N={N} K={K} B={B}")
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+def test_bits_fused_head_planted_rows(bits):
+    """Non-finite and tied rows through the fused head: an activation row holding
+    +Inf makes its logits non-finite and its id the sentinel; a row of x that is
+    all zeros makes every logit of that row zero, a tie the lowest id wins."""
+    N, K, B = 5000, 1024, 3
+    wq, sc, bi, x = _case(N, K, B, bits, 17)
+    x = x.copy()
+    x[1, 100] = 0x7F80      # +Inf (bf16 bits)
+    x[2, :] = 0              # all +0.0: every logit of row 2 is exactly zero
+    ids, logits, ref_logits, two_pass = _bits_head(wq, sc, bi, x, bits)
+    assert np.array_equal(logits.view(np.uint32), ref_logits.view(np.uint32))
+    assert ids[1] == 0xFFFFFFFF and ids[2] == 0
+    assert np.array_equal(ids, two_pass)
+    assert np.array_equal(ids, oracle.argmax(ref_logits))
+
+
+def test_w8_lm_head_fused_full_size():
+    """The fused W8 LM head at full size, B = 1 and 8: logits bitwise those of
+    qmm_gemv_bits, ids those of the two-pass argmax and the oracle's."""
+    N, K = synth.VOCAB, synth.HIDDEN
+    wq, sc, bi = synth.weights(N, K, workload=6, matrix=synth.LM_HEAD, bits=8)
+    x = synth.activations(8, K, workload=6, matrix=synth.LM_HEAD)
+    for B in (1, 8):
+        ids, logits, ref_logits, two_pass = _bits_head(wq, sc, bi, x[:B], 8)
+        assert np.array_equal(logits.view(np.uint32), ref_logits.view(np.uint32)), f"B={B}"
+        assert np.array_equal(ids, two_pass), (B, ids, two_pass)
+        assert np.array_equal(ids, oracle.argmax(ref_logits)), f"B={B}"
+        ids_only, none, _, _ = _bits_head(wq, sc, bi, x[:B], 8, want_logits=False)
+        assert none is None and np.array_equal(ids_only, ids)
+        print(f"w8 fused head B={B}: ids {ids.tolist()}")

@@ -17,7 +17,7 @@ import ctypes
 from . import _lib
 from ._lib import (BF16, F32, GEMV_AUTO, GEMV_MFMA, GEMV_MFMA_STEP, GEMV_VALU, GEMV_VALU_REGS,  # noqa: F401
                    MAX_GEMV_BATCH,
-                   OP_ARGMAX, OP_ARGMAX_TOP2, OP_GEMM, OP_GEMV, OP_GEMV_ARGMAX, SENTINEL,
+                   OP_ARGMAX, OP_ARGMAX_TOP2, OP_GEMM, OP_GEMV, OP_GEMV_ARGMAX, OP_GEMV_BITS_ARGMAX, SENTINEL,
                    W4GError)
 
 __all__ = ["qmm_gemv", "qmm_gemm", "qmm_gemv_argmax", "qmm_gemv_argmax_noalloc", "vocab_argmax",
@@ -176,10 +176,11 @@ def qmm_gemm(wq, scales, biases, x, y=None, workspace=None, out_dtype=None):
                      y_dtypes=(torch.bfloat16,))
 
 
-def qmm_gemv_argmax(wq, scales, biases, x, logits=None, ids=None, workspace=None, want_logits=True):
+def qmm_gemv_argmax(wq, scales, biases, x, logits=None, ids=None, workspace=None, want_logits=True, bits=4):
     """Decode product and greedy argmax per batch row, the argmax's first pass
     fused into the product; returns (ids, logits).  The logits are bitwise
-    those of qmm_gemv (the same kernel family).
+    those of qmm_gemv (the same kernel family; with bits 2 or 8, those of
+    qmm_gemv(..., bits=bits)).
 
     ids: int32 tensor [B] holding uint32 bits (0xFFFFFFFF = a non-finite logit
     in the row).  logits: [B][N] fp32, allocated when not given and
@@ -187,7 +188,7 @@ def qmm_gemv_argmax(wq, scales, biases, x, logits=None, ids=None, workspace=None
     logits are never written and None is returned in their place.
     """
     torch = _torch()
-    N, K = _check_qmm(wq, scales, biases, x)
+    N, K = _check_qmm(wq, scales, biases, x, bits)
     rows = x.shape[0]
     if not 1 <= rows <= MAX_GEMV_BATCH:
         raise ValueError(f"qmm_gemv_argmax takes 1..{MAX_GEMV_BATCH} rows")
@@ -202,8 +203,15 @@ def qmm_gemv_argmax(wq, scales, biases, x, logits=None, ids=None, workspace=None
     _need(ids, "ids", (torch.int32, torch.uint32), 1, wq.device)
     if ids.shape[0] != rows:
         raise ValueError("ids must have one entry per row")
-    ws, nbytes = _workspace(OP_GEMV_ARGMAX, rows, N, K, wq.device, workspace)
     lib = _lib.load()
+    if bits != 4:
+        ws, nbytes = _workspace(OP_GEMV_BITS_ARGMAX, rows, N, K, wq.device, workspace)
+        status = lib.qmm_gemv_bits_argmax(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
+                                          logits.data_ptr() if logits is not None else None, ids.data_ptr(),
+                                          rows, N, K, int(bits), ws.data_ptr(), nbytes, _stream(wq))
+        _lib.check("qmm_gemv_bits_argmax", status)
+        return ids, logits
+    ws, nbytes = _workspace(OP_GEMV_ARGMAX, rows, N, K, wq.device, workspace)
     status = lib.qmm_gemv_argmax(wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), x.data_ptr(),
                                  logits.data_ptr() if logits is not None else None, ids.data_ptr(),
                                  rows, N, K, ws.data_ptr(), nbytes, _stream(wq))

@@ -8,14 +8,14 @@ LIB_PATH = os.path.join(HERE, "libw4g.so")
 # status codes and constants, as in include/w4g.h
 OK, EINVAL_PTR, ESHAPE, EALIGN, EWORKSPACE, EDTYPE, ELAUNCH, EALIAS, ESCRATCH = range(9)
 F32, BF16 = 0, 1
-OP_GEMV, OP_GEMM, OP_ARGMAX, OP_GEMV_ARGMAX, OP_ARGMAX_TOP2 = 0, 1, 2, 3, 4
+OP_GEMV, OP_GEMM, OP_ARGMAX, OP_GEMV_ARGMAX, OP_ARGMAX_TOP2, OP_GEMV_BITS_ARGMAX = 0, 1, 2, 3, 4, 5
 SENTINEL = 0xFFFFFFFF
 MAX_GEMV_BATCH = 8
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 GEMV_AUTO, GEMV_VALU, GEMV_MFMA, GEMV_VALU_REGS, GEMV_MFMA_STEP = 0, 1, 2, 3, 4
 
-EXPORTS = ["qmm_gemv", "qmm_gemv_ex", "qmm_gemv_bits", "qmm_gemm", "qmm_gemm_ex", "qmm_gemv_argmax", "qmm_gemv_argmax_noalloc", "vocab_argmax",
+EXPORTS = ["qmm_gemv", "qmm_gemv_ex", "qmm_gemv_bits", "qmm_gemm", "qmm_gemm_ex", "qmm_gemv_argmax", "qmm_gemv_bits_argmax", "qmm_gemv_argmax_noalloc", "vocab_argmax",
            "vocab_argmax_top2", "qmm_workspace_bytes", "w4g_status_string", "w4g_abi_version"]
 
 _lib = None
@@ -49,6 +49,8 @@ def load(path=None):
     lib.qmm_gemm_ex.restype = I
     lib.qmm_gemv_argmax.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.qmm_gemv_argmax.restype = I
+    lib.qmm_gemv_bits_argmax.argtypes = [P, P, P, P, P, P, I64, I64, I64, I, P, SZ, P]
+    lib.qmm_gemv_bits_argmax.restype = I
     lib.qmm_gemv_argmax_noalloc.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
     lib.qmm_gemv_argmax_noalloc.restype = I
     lib.vocab_argmax_top2.argtypes = [P, I, I64, I64, I64, P, P, P, SZ, P]

@@ -54,6 +54,9 @@ int from_hip(hipError_t e) { return e == hipSuccess ? W4G_OK : W4G_ELAUNCH; }
 size_t gemv_argmax_bytes(int64_t B, int64_t N, int64_t K) {
   return (size_t)B * (size_t)w4g::gemv_argmax_records_max((int)B, N, K) * sizeof(uint2);
 }
+size_t gemv_bits_argmax_bytes(int64_t B, int64_t N, int64_t K) {
+  return (size_t)B * (size_t)w4g::gemv_bits_argmax_records_max((int)B, N, K) * sizeof(uint2);
+}
 
 }  // namespace
 
@@ -145,6 +148,11 @@ size_t qmm_workspace_bytes(int op, int64_t rows, int64_t n, int64_t k) {
           k >= kMaxDim || k % 64)
         return (size_t)-1;
       return gemv_argmax_bytes(rows, n, k);
+    case W4G_OP_GEMV_BITS_ARGMAX:
+      if (rows < 1 || rows > W4G_MAX_GEMV_BATCH || n < 1 || n >= kMaxDim || k < 64 ||
+          k >= kMaxDim || k % 64 || !w4g::gemv_bits_fits((int)rows, k))
+        return (size_t)-1;
+      return gemv_bits_argmax_bytes(rows, n, k);
     default:
       return (size_t)-1;
   }
@@ -223,7 +231,7 @@ namespace {
 // records' `need` bytes at `workspace`, when one is given, among the outputs).
 int check_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                       const uint16_t* x, const float* logits, const uint32_t* ids, int64_t B, int64_t N,
-                      int64_t K, const void* workspace, size_t need, bool alias = true) {
+                      int64_t K, const void* workspace, size_t need, bool alias = true, int bits = 4) {
   if (!wq || !scales || !biases || !x || !ids) return W4G_EINVAL_PTR;
   if (B < 1 || B > W4G_MAX_GEMV_BATCH || N < 1 || N >= kMaxDim || K < 64 || K >= kMaxDim || K % 64)
     return W4G_ESHAPE;
@@ -231,7 +239,7 @@ int check_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t
       !aligned2(biases) || (reinterpret_cast<uintptr_t>(ids) & 3u))
     return W4G_EALIGN;
   if (!alias) return W4G_OK;
-  const size_t wbytes = (size_t)N * (size_t)(K / 8) * sizeof(uint32_t);
+  const size_t wbytes = (size_t)N * (size_t)(K * bits / 32) * sizeof(uint32_t);
   const size_t gbytes = (size_t)N * (size_t)(K / 64) * sizeof(uint16_t);
   const size_t xbytes = (size_t)B * (size_t)K * sizeof(uint16_t);
   const size_t lbytes = logits ? (size_t)B * (size_t)N * sizeof(float) : 0;
@@ -272,6 +280,27 @@ int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
   if (rc) return rc;
   return run_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, reinterpret_cast<uint2*>(workspace),
                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int qmm_gemv_bits_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                         const uint16_t* x, float* logits, uint32_t* ids, int64_t B, int64_t N, int64_t K,
+                         int bits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (bits != 2 && bits != 4 && bits != 8) return W4G_EDTYPE;
+  if (bits == 4)
+    return qmm_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, workspace, workspace_bytes, stream);
+  int rc = check_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, nullptr, 0, false, bits);
+  if (rc) return rc;
+  if (!w4g::gemv_bits_fits((int)B, K)) return W4G_ESHAPE;
+  const size_t need = gemv_bits_argmax_bytes(B, N, K);
+  if (!workspace || workspace_bytes < need) return W4G_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u) return W4G_EALIGN;
+  rc = check_gemv_argmax(wq, scales, biases, x, logits, ids, B, N, K, workspace, need, true, bits);
+  if (rc) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint2* rec = reinterpret_cast<uint2*>(workspace);
+  const hipError_t e = w4g::launch_gemv_bits_argmax(wq, scales, biases, x, logits, rec, (int)B, N, K, bits, s);
+  if (e != hipSuccess) return W4G_ELAUNCH;
+  return from_hip(w4g::launch_argmax_combine(rec, B, w4g::gemv_bits_argmax_records((int)B, N, K), ids, s));
 }
 
 int qmm_gemv_argmax_noalloc(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,

@@ -1155,20 +1155,22 @@ hipError_t dispatch(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
 
 // 2- and 8-bit codes: the shared-memory variant only (the caller checks that x
 // fits), with the 4-bit layouts (per CU, short workgroups for the B = 1 head).
-template <int BITS>
+// AM: the argmax's pass 1 as the epilogue, one record per workgroup and batch
+// row at rec (as for 4-bit codes).
+template <int BITS, bool AM = false>
 hipError_t dispatch_bits_lds(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                             const uint16_t* x, float* y, int B, int64_t N, int64_t K, bool per_cu,
+                             const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K, bool per_cu,
                              hipStream_t stream) {
   if (B == 1) {
-    if (per_cu || b1_per_cu(N)) return launch_per_cu<1, 4, BITS>(wq, scales, biases, x, y, N, K, stream);
-    return launch_short<1, 2, 2, false, BITS>(wq, scales, biases, x, y, nullptr, N, K, stream);
+    if (per_cu || b1_per_cu(N)) return launch_per_cu<1, 4, BITS, 1, AM>(wq, scales, biases, x, y, N, K, stream, rec);
+    return launch_short<1, 2, 2, AM, BITS>(wq, scales, biases, x, y, rec, N, K, stream);
   }
   const bool two = per_cu_rows(N) > 40;
   switch (B) {
-#define W4G_PER_CU(BB)                                                                            \
-    case BB:                                                                                      \
-      return two ? launch_per_cu<2, 2, BITS, BB>(wq, scales, biases, x, y, N, K, stream)          \
-                 : launch_per_cu<1, 2, BITS, BB>(wq, scales, biases, x, y, N, K, stream);
+#define W4G_PER_CU(BB)                                                                                  \
+    case BB:                                                                                            \
+      return two ? launch_per_cu<2, 2, BITS, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec)       \
+                 : launch_per_cu<1, 2, BITS, BB, AM>(wq, scales, biases, x, y, N, K, stream, rec);
     W4G_PER_CU(2) W4G_PER_CU(3) W4G_PER_CU(4) W4G_PER_CU(5) W4G_PER_CU(6) W4G_PER_CU(7) W4G_PER_CU(8)
 #undef W4G_PER_CU
     default: return hipErrorInvalidValue;
@@ -1177,22 +1179,41 @@ hipError_t dispatch_bits_lds(const uint32_t* wq, const uint16_t* scales, const u
 
 // Other widths run the shared-memory variant only: where the batch's
 // activations do not fit in LDS, the batch is cut into parts that do, as for
-// 4-bit codes (the weights are read once per part; down_proj at K = 17,408
-// takes two parts from B = 5).  The caller checks gemv_bits_fits.
-template <int BITS>
+// 4-bit codes (the weights are read once per part), each part writing its
+// records beside the others'; from B = 3 where a CU's share is at most 24 rows,
+// and where the batch's activations exceed LDS (down_proj at K = 17,408 from
+// B = 5), the step-staged kernel reads the weights once for the whole batch.
+// The caller checks gemv_bits_fits.
+template <int BITS, bool AM = false>
 hipError_t dispatch_bits(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
-                         const uint16_t* x, float* y, int B, int64_t N, int64_t K, hipStream_t stream) {
-  if (use_step(B, N, K)) return launch_step<false, BITS>(wq, scales, biases, x, y, nullptr, B, N, K, stream);
+                         const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                         hipStream_t stream) {
+  if (use_step(B, N, K)) return launch_step<AM, BITS>(wq, scales, biases, x, y, rec, B, N, K, stream);
   if (lds_rows(K) < 1) return hipErrorInvalidValue;
   const int parts = B > lds_rows(K) ? (B + lds_rows(K) - 1) / lds_rows(K) : 1;
+  const int64_t grid = (N + per_cu_rows(N) - 1) / per_cu_rows(N);  // per-CU workgroups, when in parts
   for (int p = 0, b0 = 0; p < parts; ++p) {
     const int bp = B / parts + (p < B % parts ? 1 : 0);
-    const hipError_t e = dispatch_bits_lds<BITS>(wq, scales, biases, x + (int64_t)b0 * K, y + (int64_t)b0 * N,
-                                                 bp, N, K, parts > 1, stream);
+    const hipError_t e = dispatch_bits_lds<BITS, AM>(wq, scales, biases, x + (int64_t)b0 * K,
+                                                     y ? y + (int64_t)b0 * N : nullptr,
+                                                     rec ? rec + (int64_t)b0 * grid : nullptr, bp, N, K,
+                                                     parts > 1, stream);
     if (e != hipSuccess) return e;
     b0 += bp;
   }
   return hipSuccess;
+}
+
+// the workgroups of the layout dispatch_bits launches on a device with `cus`
+// compute units, one record each
+int64_t bits_records(int B, int64_t N, int64_t K, int cus) {
+  if (use_step(B, N, K)) return (N + step_rows(N, cus) - 1) / step_rows(N, cus);
+  const int parts = lds_rows(K) >= 1 && B > lds_rows(K) ? (B + lds_rows(K) - 1) / lds_rows(K) : 1;
+  if (B == 1 && parts == 1 && !b1_per_cu(N)) {
+    const int64_t rpw = (int64_t)kHalfWaves * 2 * short_groups();
+    return (N + rpw - 1) / rpw;
+  }
+  return (N + per_cu_rows(N, cus) - 1) / per_cu_rows(N, cus);
 }
 
 }  // namespace
@@ -1203,9 +1224,22 @@ hipError_t launch_gemv_bits(const uint32_t* wq, const uint16_t* scales, const ui
                             const uint16_t* x, float* y, int B, int64_t N, int64_t K, int bits,
                             hipStream_t stream) {
   switch (bits) {
-    case 2: return dispatch_bits<2>(wq, scales, biases, x, y, B, N, K, stream);
-    case 8: return dispatch_bits<8>(wq, scales, biases, x, y, B, N, K, stream);
+    case 2: return dispatch_bits<2>(wq, scales, biases, x, y, nullptr, B, N, K, stream);
+    case 8: return dispatch_bits<8>(wq, scales, biases, x, y, nullptr, B, N, K, stream);
     default: return launch_gemv(wq, scales, biases, x, y, B, N, K, false, stream);
+  }
+}
+
+int64_t gemv_bits_argmax_records(int B, int64_t N, int64_t K) { return bits_records(B, N, K, cu_count()); }
+int64_t gemv_bits_argmax_records_max(int B, int64_t N, int64_t K) { return bits_records(B, N, K, kMaxCUs); }
+
+hipError_t launch_gemv_bits_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                                   const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                                   int bits, hipStream_t stream) {
+  switch (bits) {
+    case 2: return dispatch_bits<2, true>(wq, scales, biases, x, y, rec, B, N, K, stream);
+    case 8: return dispatch_bits<8, true>(wq, scales, biases, x, y, rec, B, N, K, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

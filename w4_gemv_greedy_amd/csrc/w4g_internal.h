@@ -38,6 +38,14 @@ hipError_t launch_gemv_bits(const uint32_t* wq, const uint16_t* scales, const ui
                             const uint16_t* x, float* y, int B, int64_t N, int64_t K, int bits,
                             hipStream_t stream);
 bool gemv_bits_fits(int B, int64_t K);
+// The fused head at 2 or 8 bits: launch_gemv_bits's kernels with the argmax's
+// pass 1 as their epilogue (one record per workgroup and batch row), so the
+// logits are launch_gemv_bits's bit for bit; y may be null.
+hipError_t launch_gemv_bits_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                                   const uint16_t* x, float* y, uint2* rec, int B, int64_t N, int64_t K,
+                                   int bits, hipStream_t stream);
+int64_t gemv_bits_argmax_records(int B, int64_t N, int64_t K);
+int64_t gemv_bits_argmax_records_max(int B, int64_t N, int64_t K);
 // Kernel family qmm_gemv runs (1 = vector ALU, 2 = matrix cores): a function
 // of the whole matrix's row count and of K only, never of the batch size.
 int gemv_auto_family(int64_t whole, int64_t K);
