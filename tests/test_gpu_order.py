@@ -1,0 +1,48 @@
+"""The vector-ALU decode order, checked bit for bit against a model of it
+(valu_order.py: the documented chunks, lane segments, pair order, fused
+multiply-adds and lane tree, every step rounded once to fp32) on inputs where
+each dot2 adds terms of one sign (codes 0..15 expand to 128 + q > 0, and the
+activations are taken non-negative), so that the model of the dot2's rounding
+holds.  Rows come from the per-CU kernel (B = 1 and, with the transposed lane
+tree, B = 8) and from the step-staged kernel (x spanning nine chunks), and are
+compared at B = 1 and B = 8."""
+import numpy as np
+import pytest
+
+import valu_order
+from gpu_util import down, up_bf16, up_u32
+from w4_gemv_greedy_amd import synth
+
+pytestmark = pytest.mark.gpu
+w4g = pytest.importorskip("w4_gemv_greedy_amd")
+
+
+def _positive(x, narrow):
+    x = np.asarray(x, dtype=np.uint16) & np.uint16(0x7FFF)  # |x|
+    if narrow:  # every activation in [1, 2): products within one binade of each other
+        x = (x & np.uint16(0x007F)) | np.uint16(0x3F80)
+    return x
+
+
+@pytest.mark.parametrize("N,K,rows,narrow", [
+    (24, 1024, [0, 7, 23], True),
+    (24, 1024, [0, 7, 23], False),
+    (6400, 2048, [0, 1, 24, 3333, 6399], False),   # 25 rows per CU: the per-CU kernel at B = 8 too
+    (12, 9216, [0, 11], False),                     # nine chunks: the step-staged kernel
+])
+def test_valu_order_bitwise(N, K, rows, narrow):
+    wq, sc, bi = synth.weights(N, K, workload=91)
+    x = _positive(synth.activations(8, K, workload=91), narrow)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y8 = down(w4g.qmm_gemv(*W, up_bf16(x), kernel=w4g.GEMV_VALU)).view(np.uint32)
+    y1 = down(w4g.qmm_gemv(*W, up_bf16(x[:1]), kernel=w4g.GEMV_VALU)).view(np.uint32)
+    bad = []
+    for n in rows:
+        for b in (0, 5):
+            want = valu_order.f32_bits(valu_order.row(wq[n], sc[n], bi[n], x[b]))
+            got = int(y8[b, n])
+            if got != want:
+                bad.append((n, b, hex(got), hex(want)))
+        if int(y1[0, n]) != int(y8[0, n]):
+            bad.append((n, "B=1 vs B=8", hex(int(y1[0, n])), hex(int(y8[0, n]))))
+    assert not bad, bad

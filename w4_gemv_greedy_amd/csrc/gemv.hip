@@ -110,8 +110,8 @@ __device__ __forceinline__ float half_wave_sum(float v) {
 // v_permlane16_swap per pair of values); mirror and half mirror then split by
 // lane bits 3 and 2 the same way; the quad swaps add what is left.  So every
 // value's total has the bits half_wave_sum gives it, and lane i of the half
-// wave ends with the total of value half_wave_index<NB>(i): NB - 1 + ... + 1
-// swaps and about 2 NB instructions in all, not 10 NB.
+// wave ends with the total of value half_wave_index<NB>(i): NB / 2 row swaps
+// and about 2 NB instructions in all, against 10 NB for NB separate trees.
 template <int NB>
 __device__ __forceinline__ int half_wave_index(int lane) {
   int t = (lane >> 4) & 1;
