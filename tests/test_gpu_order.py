@@ -46,3 +46,21 @@ def test_valu_order_bitwise(N, K, rows, narrow):
         if int(y1[0, n]) != int(y8[0, n]):
             bad.append((n, "B=1 vs B=8", hex(int(y1[0, n])), hex(int(y8[0, n]))))
     assert not bad, bad
+
+
+def test_valu_order_signed_activations():
+    """With signed activations a dot2 can cancel, where the instruction rounds
+    more coarsely than the model; most rows still equal the model bit for bit
+    and the others stay within fp32 accuracy of it (seeded, so deterministic:
+    500 of 512 rows equal here)."""
+    N, K = 64, 1024
+    wq, sc, bi = synth.weights(N, K, workload=92)
+    x = synth.activations(8, K, workload=92)
+    y = down(w4g.qmm_gemv(up_u32(wq), up_bf16(sc), up_bf16(bi), up_bf16(x)))
+    want = np.array([[float(valu_order.row(wq[n], sc[n], bi[n], x[b])) for n in range(N)] for b in range(8)],
+                    dtype=np.float32)
+    equal = int(np.sum(y.view(np.uint32) == want.view(np.uint32)))
+    print(f"signed activations: {equal} of {y.size} rows equal the model bit for bit")
+    assert equal >= 0.9 * y.size
+    err = np.max(np.abs(y.astype(np.float64) - want), axis=1) / np.max(np.abs(want.astype(np.float64)), axis=1)
+    assert np.all(err <= 2e-6), err
