@@ -64,3 +64,25 @@ def test_valu_order_signed_activations():
     assert equal >= 0.9 * y.size
     err = np.max(np.abs(y.astype(np.float64) - want), axis=1) / np.max(np.abs(want.astype(np.float64)), axis=1)
     assert np.all(err <= 2e-6), err
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("N,K,rows", [(24, 1024, [0, 7, 23]), (6400, 2048, [0, 3333, 6399]), (12, 9216, [0, 11])])
+def test_valu_order_other_widths_bitwise(bits, N, K, rows):
+    """The 2- and 8-bit orders (the same kernels with the lane's segment held in
+    BITS-bit fields) against the model bit for bit, non-negative activations,
+    B = 1 and 8."""
+    wq, sc, bi = synth.weights(N, K, workload=93, bits=bits)
+    x = _positive(synth.activations(8, K, workload=93), False)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    y8 = down(w4g.qmm_gemv(*W, up_bf16(x), bits=bits)).view(np.uint32)
+    y1 = down(w4g.qmm_gemv(*W, up_bf16(x[:1]), bits=bits)).view(np.uint32)
+    bad = []
+    for n in rows:
+        for b in (0, 5):
+            want = valu_order.f32_bits(valu_order.row(wq[n], sc[n], bi[n], x[b], bits=bits))
+            if int(y8[b, n]) != want:
+                bad.append((n, b, hex(int(y8[b, n])), hex(want)))
+        if int(y1[0, n]) != int(y8[0, n]):
+            bad.append((n, "B=1 vs B=8"))
+    assert not bad, bad
