@@ -21,9 +21,12 @@ def test_graph_replays_match_eager():
     wq, sc, bi = synth.weights(N, K, workload=70)
     hq, hs, hb = synth.weights(V, K, workload=71)
     dq, ds, db = synth.weights(Nd, Kd, workload=74)
+    V8 = 20000  # the fused head at 8 bits (short workgroups, then the combine)
+    eq, es, eb = synth.weights(V8, K, workload=78, bits=8)
     W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
     H = (up_u32(hq), up_bf16(hs), up_bf16(hb))
     D = (up_u32(dq), up_bf16(ds), up_bf16(db))
+    E = (up_u32(eq), up_bf16(es), up_bf16(eb))
     x1 = up_bf16(synth.activations(1, K, workload=70))
     x8 = up_bf16(synth.activations(8, K, workload=72))
     xm = up_bf16(synth.activations(96, K, workload=73))
@@ -42,8 +45,16 @@ def test_graph_replays_match_eager():
     wsg = torch.empty(w4g.workspace_bytes(w4g.OP_GEMM, 96, N, K), dtype=torch.uint8, device=dev)
     wss = torch.empty(w4g.workspace_bytes(w4g.OP_GEMM, 16, N, K), dtype=torch.uint8, device=dev)
     wsa = torch.empty(w4g.workspace_bytes(w4g.OP_ARGMAX, 1, V, 0), dtype=torch.uint8, device=dev)
-    outs = (y1, y8, ym, ys, yd1, yd8, lg)
-    names = ("gemv b1", "gemv b8", "gemm", "gemm 16 rows", "down b1", "down b8", "lm_head")
+    # the fused heads: 4-bit over the V rows at B = 8, 8-bit over V8 rows at B = 1
+    lgf = torch.empty((8, V), dtype=torch.float32, device=dev)
+    idsf = torch.empty(8, dtype=torch.int32, device=dev)
+    wsf = torch.empty(w4g.workspace_bytes(w4g.OP_GEMV_ARGMAX, 8, V, K), dtype=torch.uint8, device=dev)
+    lg8 = torch.empty((1, V8), dtype=torch.float32, device=dev)
+    ids8 = torch.empty(1, dtype=torch.int32, device=dev)
+    ws8 = torch.empty(w4g.workspace_bytes(w4g.OP_GEMV_BITS_ARGMAX, 1, V8, K), dtype=torch.uint8, device=dev)
+    outs = (y1, y8, ym, ys, yd1, yd8, lg, lgf, lg8)
+    names = ("gemv b1", "gemv b8", "gemm", "gemm 16 rows", "down b1", "down b8", "lm_head", "fused head b8",
+             "w8 fused head")
 
     def work():
         w4g.qmm_gemv(*W, x1, y1)
@@ -54,9 +65,12 @@ def test_graph_replays_match_eager():
         w4g.qmm_gemv(*D, xd8, yd8)
         w4g.qmm_gemv(*H, x1, lg)
         w4g.vocab_argmax(lg, ids, wsa)
+        w4g.qmm_gemv_argmax(*H, x8, logits=lgf, ids=idsf, workspace=wsf)
+        w4g.qmm_gemv_argmax(*E, x1, logits=lg8, ids=ids8, workspace=ws8, bits=8)
 
     work()
-    ref = [down(t).copy() for t in outs] + [ids_down(ids).copy()]
+    id_outs = (ids, idsf, ids8)
+    ref = [down(t).copy() for t in outs] + [ids_down(t).copy() for t in id_outs]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -68,11 +82,12 @@ def test_graph_replays_match_eager():
     for rep in range(4):
         for t in outs:
             t.fill_(float("nan"))
-        ids.fill_(-2)
+        for t in id_outs:
+            t.fill_(-2)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [down(t) for t in outs] + [ids_down(ids)]
-        for a, b, name in zip(got, ref, names + ("ids",)):
+        got = [down(t) for t in outs] + [ids_down(t) for t in id_outs]
+        for a, b, name in zip(got, ref, names + ("ids", "fused ids b8", "w8 fused ids")):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"replay {rep}: {name}"
         _ = torch.ones(1000, device=dev).sum().item()  # eager work between replays
