@@ -261,11 +261,11 @@ int qmm_gemv_argmax(const uint32_t* wq, const uint16_t* scales, const uint16_t* 
 
 /*
  * qmm_gemv_argmax at another code width: the greedy head over a 2- or 8-bit
- * affine group-64 matrix (the W8 LM head the B70 page serves, "Reproduce
- * Qwen3.6 27B AutoRound Bring-Up": a runtime INT8 target LM head; other widths
- * take their own kernel variant, TensorFold PR #1433, owner's review of step
- * 2), with the argmax's first pass fused into the product's epilogue as in
- * qmm_gemv_argmax.
+ * affine group-64 matrix (the B70 page, "Reproduce Qwen3.6 27B AutoRound
+ * Bring-Up", serves its target model's vocabulary projection with 8-bit
+ * integer weights; other widths take their own kernel variant, TensorFold PR
+ * #1433, owner's review of step 2), with the argmax's first pass fused into
+ * the product's epilogue as in qmm_gemv_argmax.
  *   wq, scales, biases, x, B, N, K, bits: as qmm_gemv_bits (bits 2, 4 or 8,
  *   else W4G_EDTYPE; 4 is qmm_gemv_argmax); N < 2^31.
  *   logits [B][N] fp32, or NULL: when given, exactly the bits qmm_gemv_bits
