@@ -304,8 +304,9 @@ int qmm_gemv_argmax_noalloc(const uint32_t* wq, const uint16_t* scales, const ui
  * ordering (value descending, lowest id first among equal values, -0.0 equal
  * to +0.0) and the gap between them, so that a greedy pick that differs
  * between two computations of the logits can be told apart from a near tie.
- * (Reading: the pages' session merges "the top two" across blocks for its
- * tie test, TensorFold PR #1433, step-1 description; no format is given.)
+ * (Reading: the pages' session keeps the two best candidates of each block
+ * and merges them for its tie test, TensorFold PR #1433, step-1 description;
+ * no format is given.)
  *   logits, dtype, rows, ld: as vocab_argmax; 2 <= vocab < 2^31.
  *   ids2 [rows][2] uint32: winner, runner-up (ids2[r][0] equals vocab_argmax's
  *   id); both W4G_SENTINEL if the row holds NaN or +-Inf.
