@@ -42,8 +42,8 @@
  *    and pair_pick turns the flag into the id sentinel; step-2 description:
  *    the session reads the maxInt(u32) sentinel as a failure, never as a
  *    logit).  Otherwise the largest value wins and an exact tie goes to the
- *    lowest id (the same step-1 description lists an argmax and a pick that
- *    "tie to the higher id" among the controls that must fail).  Comparison is
+ *    lowest id (the same step-1 description lists, among the controls that
+ *    must fail, an argmax and a pick that resolve a tie to the larger id).  Comparison is
  *    IEEE float comparison, so -0.0 and +0.0 tie and denormals compare
  *    exactly.  bf16 logits are widened to fp32 exactly first.
  *
