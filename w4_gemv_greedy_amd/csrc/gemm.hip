@@ -955,14 +955,10 @@ int64_t g16_of(int64_t K) { return (((K >> 6) + 15) / 16) * 16; }
 bool chain_tiles(int64_t M, int64_t N) { return M <= 32 && (N + 31) / 32 <= 2 * cu_count(); }
 
 // Where the 64 x 64 tiles take over (rows of the slice, 128 x 128 tiles it makes)
-#ifndef W4G_SMALL_RULE
 bool small_tiles(int64_t M, int64_t tiles128) {
   const int cus = cu_count();
   return tiles128 < cus / 2 || (M <= 128 && tiles128 < 2 * cus);
 }
-#else
-bool small_tiles(int64_t M, int64_t tiles128) { return W4G_SMALL_RULE; }
-#endif
 
 
 }  // namespace
