@@ -757,8 +757,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_chain_kernel(
   constexpr int XCH = NW * (XP_G + XS_G);            // one round's exchange
   constexpr int SC = 32 * CS * 16, SX = MR * XS * 16;  // one round's staged codes, activations
   constexpr int ST = SC + SX;
-  constexpr int ZERO = 2 * XCH + 2 * ST;             // 16 zero bytes (rows 16..31 of a 16-row tile)
-  __shared__ __attribute__((aligned(16))) unsigned char smem[ZERO + 16];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * XCH + 2 * ST];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int tile = (b & 7) * (int)per + (b >> 3);
@@ -779,7 +778,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_chain_kernel(
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-  if (tid < 4) reinterpret_cast<uint32_t*>(smem + ZERO)[tid] = 0u;
   // loads: 16-byte piece cp of column cr's round segment (32 NW bytes), and
   // piece xq_i of row xr_i's (128 NW bytes)
   const int cr = (64 * wave + lane) / CS, cp = (64 * wave + lane) % CS;
@@ -799,12 +797,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_chain_kernel(
   const int vs = l32 * G * 2;
   // matrix-core reads: lane (h, l32) takes codes piece 2w + h of column l32 and
   // activation chunks 4h + t (t = 0..3) of its group, row l32 (a 16-row tile's
-  // rows 16..31 read the zero slot)
+  // rows 16..31 are zeros held in registers; their lanes read nothing)
   const int crd = l32 * CS * 16 + (((2 * wave + h) ^ (l32 & (CS - 1))) << 4);
   int xrd[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    xrd[t] = (MR == 16 && l32 >= 16) ? ZERO - 2 * XCH : SC + l32 * XS * 16 + (((8 * wave + 4 * h + t) ^ (l32 & 15)) << 4);
+    xrd[t] = SC + (l32 & (MR - 1)) * XS * 16 + (((8 * wave + 4 * h + t) ^ (l32 & 15)) << 4);
 
   // rounds past the last reload the last one (cached), so every round loads alike
   auto load = [&](ChainOps<MR>& o, int r) __attribute__((always_inline)) {
@@ -825,9 +823,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_chain_kernel(
     const unsigned char* base = smem + 2 * XCH + par * ST;
     const v4u c = *reinterpret_cast<const v4u*>(base + crd);
     v4u a[4];
+    if (MR == 16 && l32 >= 16) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      a[t] = *reinterpret_cast<const v4u*>((MR == 16 && l32 >= 16 ? smem + 2 * XCH : base) + xrd[t]);
+      for (int t = 0; t < 4; ++t) a[t] = v4u{0u, 0u, 0u, 0u};
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4u*>(base + xrd[t]);
+    }
     f32x16_t p;
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = 0.0f;
