@@ -361,6 +361,26 @@ def test_gemm_tile_variants_bitwise():
     assert_close(y_reg[:, cols], oracle.qmm_rows(wq, sc, bi, x, cols), "gemm tile variants")
 
 
+def test_gemm_small_grid_variants_bitwise():
+    """Small grids over a wide matrix: past 32 rows, where 64 x 64 tiles would
+    outnumber the CUs, 64 x 128 tiles run (100 rows: 2 x 129); at 20 rows the
+    64 x 64 tiles stay (257 of them, a column tile too many for the short-prompt
+    kernel).  Their rows are bitwise the rows of a 600-row prompt (register-
+    staged 128 x 128 tiles) and sampled columns match the oracle."""
+    N, K = 16390, 256                     # 129 column tiles of 128, the last ragged
+    wq, sc, bi, x = _case(N, K, 600, 91)
+    W = (up_u32(wq), up_bf16(sc), up_bf16(bi))
+    X = up_bf16(x)
+    y_reg = down(w4g.qmm_gemm(*W, X))                         # 5 x 129 = 645 tiles
+    y_mid = down(w4g.qmm_gemm(*W, X[:100].contiguous()))      # 64 x 128 tiles
+    y_few = down(w4g.qmm_gemm(*W, X[:20].contiguous()))       # 64 x 64 tiles
+    assert np.array_equal(y_mid.view(np.uint32), y_reg[:100].view(np.uint32))
+    assert np.array_equal(y_few.view(np.uint32), y_reg[:20].view(np.uint32))
+    cols = np.unique(np.concatenate([np.arange(40), np.arange(N - 40, N),
+                                     np.random.default_rng(6).choice(N, 60, replace=False)]))
+    assert_close(y_mid[:, cols], oracle.qmm_rows(wq, sc, bi, x[:100], cols), "gemm small grid")
+
+
 @pytest.mark.parametrize("N,K", [(70, 128), (1000, 384), (333, 1152), (5120, 5120)])
 def test_gemm_short_prompt_kernel(N, K):
     """Prompts of at most 32 rows over a narrow matrix take the short-prompt

@@ -31,7 +31,8 @@
 // that; tiles loaded straight into an LDS ring when fewer: 128 x 128 (one
 // workgroup per CU) while they cover the CUs, 64 x 128 (each wave 32 x 64,
 // two workgroups per CU) where they cover half of them, and 64 x 64 (each wave
-// one 32 x 32 matrix-core tile) for short prompts and small grids.  Prompts of
+// one 32 x 32 matrix-core tile) for short prompts and small grids (64 x 128
+// again past 32 rows where 64 x 64 tiles would outnumber the CUs).  Prompts of
 // at most 32 rows over narrow matrices take a fourth loop that deals each
 // tile's groups to eight waves and passes the group products on through LDS
 // (a tile's K chain would otherwise run on one wave).  The bias terms and the
@@ -978,7 +979,8 @@ namespace {
 //   for two workgroups per CU (or when the LDS-load kernel does not apply),
 //   the LDS-load loop with 128 x 128 tiles while they still cover every CU,
 //   with 64 x 128 tiles (two workgroups per CU) where they cover half of them
-//   or more, and with 64 x 64 tiles (a deeper ring) below that.
+//   or more, and with 64 x 64 tiles (a deeper ring) below that, except past 32
+//   rows where those would outnumber the CUs (64 x 128 again).
 template <typename OUT>
 hipError_t launch_main(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                        const uint16_t* xp, const uint16_t* xs, OUT* y, int64_t M, int64_t N,
@@ -1011,9 +1013,17 @@ hipError_t launch_main(const uint32_t* wq, const uint16_t* scales, const uint16_
         }
       } else if (dma && small_tiles(Ms, tiles128)) {
         // 64 x 64 tiles: a 4-stage ring (83 KiB, one workgroup per CU) while the
-        // tiles fit on the CUs once, else 3 stages (62 KiB) so two share a CU
+        // tiles fit on the CUs once, else 3 stages (62 KiB) so two share a CU;
+        // past 32 rows, where they outnumber the CUs, 64 x 128 tiles (half as
+        // many, two per CU: gate-up at 128 rows 107 -> 102 us, at 64 rows 72.2 ->
+        // 71.3; at 16 and 32 rows, whose second half-tile of rows is empty,
+        // they were slower)
         const int64_t NT = (Ns + 63) / 64, tiles = ((Ms + 63) / 64) * NT, per = (tiles + 7) / 8;
-        if (tiles <= cu_count())
+        if (tiles > cu_count() && Ms > 32) {
+          const int64_t NT2 = (Ns + 127) / 128, tiles2 = ((Ms + 63) / 64) * NT2, per2 = (tiles2 + 7) / 8;
+          hipLaunchKernelGGL((gemm_dma_kernel<1, 2, 2, 2, 3, OUT>), dim3((unsigned)(8 * per2)), dim3(256), 0,
+                             stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT2, tiles2, per2, vec);
+        } else if (tiles <= cu_count())
           hipLaunchKernelGGL((gemm_dma_kernel<1, 1, 2, 2, 4, OUT>), dim3((unsigned)(8 * per)), dim3(256), 0,
                              stream, w_s, s_s, b_s, xp_s, xs_s, y_s, Ms, Ns, K, N, G16, NT, tiles, per, vec);
         else
